@@ -1,0 +1,221 @@
+/*
+ * kda_oracle.c -- fp64 CPU oracle for the Kimi Delta Attention (KDA) operator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library,
+ * its headers, its Python binding) includes, links or calls this file.  Only
+ * the tests, the smoke check and the CPU-baseline leg of the benchmark use it.
+ * It shares no code, header, table or constant with the GPU path.
+ *
+ * What it computes, and where that comes from:
+ *
+ *  - Gate ("Architecture Deep Dive: Kimi K3...", section 3.2, equation 1;
+ *    "Kimi K3 Deep Dive...", "The Design: Putting a Lower Bound on Log-Decay"
+ *    and its illustrative code): the per-channel log-decay of token t is
+ *        g_t = g_min * sigmoid(theta_t),  g_min = -5,
+ *    so g_t lies in [-5, 0] and the per-step decay factor is exp(g_t).
+ *
+ *  - Chunk-local cumulative log-decay (same page, "The Problem: The
+ *    Diagonal-Block Dilemma"): the decay from position i to j inside a chunk
+ *    is the product of the per-step factors, i.e. exp of the sum of g over
+ *    (i, j].  With 16-token chunks the inclusive prefix sum of g restarted
+ *    at every chunk start is the quantity whose exponent the chunked method
+ *    scales by; it is reported by the gate helper.
+ *
+ *  - The recurrence ("Kimi K3" explainer, "Across the sequence": a gated
+ *    delta-rule linear attention; each token reads a fixed-size state,
+ *    forgets part of it channel-wise and writes into it).  Per head, with
+ *    state S of shape [d_k, d_v] and for every token t in order:
+ *        S   <- Diag(exp(g_t)) S                       (channel-wise forget)
+ *        u_t  = beta_t * (v_t - S^T k_t)                (delta-rule read)
+ *        S   <- S + k_t u_t^T                           (write)
+ *        o_t  = S^T q_t                                 (output read)
+ *    The decode step is this body for one token with S updated in place.
+ *
+ * Plain loops in double precision, no blocking or reordering beyond the
+ * definition.  Threads only split independent (batch, head) sequences.
+ * Column j of S evolves independently of the other columns (every operation
+ * above acts on columns separately), so an optional column list restricts
+ * the computation to those columns of o and S_T; with no list every column
+ * is computed.
+ *
+ * Layouts (row-major, all double):
+ *   q, k  [B, T, H, dk]     v  [B, T, H, dv]      g (or theta) [B, T, H, dk]
+ *   beta  [B, T, H]         S0 [B, H, dk, dv]
+ *   o     [B, T, H, nc]     S_T [B, H, dk, nc]    (nc = ncols, or dv)
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_G_MIN (-5.0)
+#define ORACLE_CHUNK 16
+
+/* sigmoid written from its definition 1 / (1 + e^{-x}). */
+static double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* g = g_min * sigmoid(theta), elementwise over n values. */
+void kda_oracle_gate(long n, const double* theta, double* g) {
+    for (long i = 0; i < n; ++i) g[i] = ORACLE_G_MIN * oracle_sigmoid(theta[i]);
+}
+
+/* Inclusive prefix sum of g along T, restarted at every 16-token chunk start
+ * (positions 0, 16, 32, ...).  g and gcum are [B, T, H, dk]. */
+void kda_oracle_gate_cumsum(int B, int T, int H, int dk, const double* g, double* gcum) {
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int c = 0; c < dk; ++c) {
+                double run = 0.0;
+                for (int t = 0; t < T; ++t) {
+                    size_t idx = (((size_t)b * T + t) * H + h) * dk + c;
+                    if (t % ORACLE_CHUNK == 0) run = 0.0;
+                    run += g[idx];
+                    gcum[idx] = run;
+                }
+            }
+}
+
+typedef struct {
+    int B, T, H, dk, dv, nc;
+    const double *q, *k, *v, *g, *beta, *S0;
+    const int* cols;
+    double *o, *S_T;
+    int tid, nthreads;
+    int status;
+} job_t;
+
+/* One (batch, head) sequence, token by token. */
+static int run_sequence(const job_t* J, int b, int h) {
+    const int T = J->T, H = J->H, dk = J->dk, dv = J->dv, nc = J->nc;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * nc);
+    double* u = (double*)malloc(sizeof(double) * (size_t)nc);
+    if (!S || !u) { free(S); free(u); return 1; }
+
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < nc; ++j) {
+            int col = J->cols ? J->cols[j] : j;
+            S[(size_t)i * nc + j] =
+                J->S0 ? J->S0[(((size_t)b * H + h) * dk + i) * dv + col] : 0.0;
+        }
+
+    for (int t = 0; t < T; ++t) {
+        const size_t row = ((size_t)b * T + t) * H + h;
+        const double* qt = J->q + row * dk;
+        const double* kt = J->k + row * dk;
+        const double* vt = J->v + row * dv;
+        const double* gt = J->g + row * dk;
+        const double bt = J->beta[row];
+
+        /* forget: S <- Diag(exp(g_t)) S  (row i of S is channel i of d_k) */
+        for (int i = 0; i < dk; ++i) {
+            const double a = exp(gt[i]);
+            for (int j = 0; j < nc; ++j) S[(size_t)i * nc + j] *= a;
+        }
+        /* read: u = beta * (v - S^T k) */
+        for (int j = 0; j < nc; ++j) {
+            double r = 0.0;
+            for (int i = 0; i < dk; ++i) r += S[(size_t)i * nc + j] * kt[i];
+            const int col = J->cols ? J->cols[j] : j;
+            u[j] = bt * (vt[col] - r);
+        }
+        /* write: S <- S + k u^T */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < nc; ++j) S[(size_t)i * nc + j] += kt[i] * u[j];
+        /* output: o_t = S^T q */
+        double* ot = J->o + row * nc;
+        for (int j = 0; j < nc; ++j) {
+            double r = 0.0;
+            for (int i = 0; i < dk; ++i) r += S[(size_t)i * nc + j] * qt[i];
+            ot[j] = r;
+        }
+    }
+
+    if (J->S_T)
+        memcpy(J->S_T + ((size_t)b * H + h) * dk * nc, S, sizeof(double) * (size_t)dk * nc);
+    free(S);
+    free(u);
+    return 0;
+}
+
+static void* worker(void* arg) {
+    job_t* J = (job_t*)arg;
+    const int n = J->B * J->H;
+    for (int s = J->tid; s < n; s += J->nthreads)
+        if (run_sequence(J, s / J->H, s % J->H)) J->status = 1;
+    return NULL;
+}
+
+/* Token-by-token recurrence with the log-decay g given directly.
+ * cols: NULL for all d_v columns, else ncols indices into [0, dv).
+ * S0 and S_T may be NULL.  Returns 0 on success, nonzero on bad arguments
+ * or allocation failure. */
+int kda_oracle_recurrence(int B, int T, int H, int dk, int dv,
+                          const double* q, const double* k, const double* v,
+                          const double* g, const double* beta, const double* S0,
+                          const int* cols, int ncols, double* o, double* S_T,
+                          int nthreads) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return 2;
+    if (!q || !k || !v || !g || !beta || !o) return 2;
+    const int nc = cols ? ncols : dv;
+    if (nc <= 0) return 2;
+    if (cols)
+        for (int j = 0; j < nc; ++j)
+            if (cols[j] < 0 || cols[j] >= dv) return 2;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > B * H) nthreads = B * H > 0 ? B * H : 1;
+
+    job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return 1; }
+    for (int i = 0; i < nthreads; ++i) {
+        job_t J = {B, T, H, dk, dv, nc, q, k, v, g, beta, S0, cols, o, S_T, i, nthreads, 0};
+        jobs[i] = J;
+    }
+    for (int i = 1; i < nthreads; ++i) pthread_create(&th[i], NULL, worker, &jobs[i]);
+    worker(&jobs[0]);
+    int status = jobs[0].status;
+    for (int i = 1; i < nthreads; ++i) {
+        pthread_join(th[i], NULL);
+        status |= jobs[i].status;
+    }
+    free(jobs);
+    free(th);
+    return status;
+}
+
+/* Chunked-prefill result: the gate applied to theta, then the recurrence.
+ * (Chunking is an evaluation order; the result is the recurrence's.) */
+int kda_oracle_chunk_fwd(int B, int T, int H, int dk, int dv,
+                         const double* q, const double* k, const double* v,
+                         const double* theta, const double* beta, const double* S0,
+                         const int* cols, int ncols, double* o, double* S_T,
+                         int nthreads) {
+    const size_t n = (size_t)B * T * H * dk;
+    double* g = (double*)malloc(sizeof(double) * (n ? n : 1));
+    if (!g) return 1;
+    kda_oracle_gate((long)n, theta, g);
+    int st = kda_oracle_recurrence(B, T, H, dk, dv, q, k, v, g, beta, S0, cols, ncols,
+                                   o, S_T, nthreads);
+    free(g);
+    return st;
+}
+
+/* One decode step: the recurrence body for a single token per (batch, head),
+ * S [B, H, dk, dv] updated in place, o [B, H, dv]. */
+int kda_oracle_decode_step(int B, int H, int dk, int dv,
+                           const double* q, const double* k, const double* v,
+                           const double* theta, const double* beta, double* S,
+                           double* o, int nthreads) {
+    const size_t n = (size_t)B * H * dk;
+    double* g = (double*)malloc(sizeof(double) * (n ? n : 1));
+    double* S_new = (double*)malloc(sizeof(double) * ((size_t)B * H * dk * dv + 1));
+    if (!g || !S_new) { free(g); free(S_new); return 1; }
+    kda_oracle_gate((long)n, theta, g);
+    /* [B, H, d] with T = 1 is the [B, T, H, d] layout with T = 1. */
+    int st = kda_oracle_recurrence(B, 1, H, dk, dv, q, k, v, g, beta, S, NULL, 0, o, S_new,
+                                   nthreads);
+    if (st == 0) memcpy(S, S_new, sizeof(double) * (size_t)B * H * dk * dv);
+    free(g);
+    free(S_new);
+    return st;
+}
