@@ -1,0 +1,184 @@
+"""Benchmark of the KDA operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one kda_chunk_fwd call (gate, intra-chunk tiles, UT/WY transform and
+inter-chunk scan) over the 64K-token training-shaped prefill: B=1, H=16,
+T=65536, d_k=d_v=128, bf16 q/k/v, fp32 theta ~ N(0, 2), beta, S0 = 0, seeded
+synthetic data already resident in HBM.  The timed region is exactly K steps
+between two device synchronisations, measured with HIP events on the stream the
+kernels run on.  The decode step (B=256, H=16 fp32 state, in place) is timed
+the same way and reported in the "decode" object.  The fp64 oracle is timed on
+the host cores on a bounded sample of the same prefill ("cpu_baseline").
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak
+METRIC = "KDA chunk_fwd tokens/s @H16 d128 T64K; % bf16 MFMA peak; decode GB/s"
+
+
+def prefill_work(B, T, H, dk, dv, es=2, s0=False, chunk=16):
+    """Algorithmic flops and HBM bytes of one chunked prefill.
+    flops per token*head: 6*dk*dv (state products) + 6*C*dk (A_kk, A_qk, W) + 4*C*dv (Ut, A_qk U);
+    bytes per token*head: q, k, v, o in the storage type, theta fp32, beta fp32; plus S_T (and S0)."""
+    th = B * T * H
+    flops = th * (6 * dk * dv + 6 * chunk * dk + 4 * chunk * dv)
+    nbytes = th * (es * (2 * dk + dv) + es * dv + 4 * dk + 4) + B * H * dk * dv * 4 * (2 if s0 else 1)
+    return flops, nbytes
+
+
+def decode_work(B, H, dk, dv, es=2):
+    """Per step: fp32 state read + write, token inputs and output."""
+    nbytes = B * H * (8 * dk * dv + es * (2 * dk + dv) + 4 * dk + 4 + es * dv)
+    flops = B * H * 7 * dk * dv
+    return flops, nbytes
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(x, T_sample, threads):
+    """The oracle as it stands, on the first T_sample tokens of every head."""
+    import oracle
+    sl = {k: (v[:, :T_sample].contiguous().cpu() if v is not None and v.dim() >= 3 else v)
+          for k, v in x.items() if k != "S0"}
+    t0 = time.perf_counter()
+    oracle.chunk_fwd(sl["q"], sl["k"], sl["v"], sl["theta"], sl["beta"], None, nthreads=threads)
+    dt = time.perf_counter() - t0
+    B = x["q"].shape[0]
+    return {"value": B * T_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {T_sample} tokens of all {x['q'].shape[2]} heads of the same prefill "
+                      f"(fp64 token-by-token recurrence, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_64k")
+    ap.add_argument("--segments", type=int, default=0)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the KDA operator "
+              "shards over batch and heads without communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_gated_delta_12_amd as kda
+    from chunked_gated_delta_12_amd import inputs as kin
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kda.load_library()
+    stream = torch.cuda.current_stream(dev)
+
+    w = kin.WORKLOADS[args.workload]
+    x = kin.chunk_inputs(w, device=dev)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    seg = args.segments or kda.kda_chunk_fwd_auto_segments(B, T, H, dk, dv)
+    o = torch.empty((B, T, H, dv), device=dev, dtype=x["q"].dtype)
+    S_T = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    nws = kda.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, seg)
+    ws = torch.empty(max(nws, 16), device=dev, dtype=torch.uint8)
+
+    def step():
+        kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], x["S0"], segments=seg,
+                          o=o, S_T=S_T, workspace=ws, stream=stream)
+
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    ms, wall_ms = time_calls(step, args.steps, args.warmup, stream)
+    es = 2 if w.dtype == "bf16" else 4
+    flops, nbytes = prefill_work(B, T, H, dk, dv, es=es, s0=x["S0"] is not None)
+    achieved_gbs = nbytes / (ms * 1e-3) / 1e9
+    achieved_tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": B * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "dk": dk, "dv": dv,
+                   "theta": f"N({w.theta_mu},{w.theta_sigma})", "segments": seg,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_chunk_fwd (map + combine + out kernels, one call)",
+                     "algorithmic_bytes": nbytes},
+        "mfma": {"achieved": achieved_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": flops},
+    }
+
+    if not args.no_decode:
+        dw = kin.DECODE_WORKLOADS["decode_b256"]
+        S, gen = kin.decode_state(dw, device=dev)
+        nt = 16
+        tok = kin.decode_token(dw, gen, device=dev, steps=nt)
+        od = torch.empty((dw.B, dw.H, dw.dv), device=dev, dtype=torch.bfloat16)
+        it = [0]
+
+        def dstep():
+            i = it[0] % nt
+            it[0] += 1
+            kda.kda_decode_step(tok["q"][i], tok["k"][i], tok["v"][i], tok["theta"][i], tok["beta"][i], S,
+                                o=od, stream=stream)
+
+        dms, _ = time_calls(dstep, args.decode_steps, 3, stream)
+        dfl, dby = decode_work(dw.B, dw.H, dw.dk, dw.dv)
+        gbs = dby / (dms * 1e-3) / 1e9
+        out["decode"] = {"workload": dw.name, "B": dw.B, "H": dw.H, "d": dw.dk, "ms_per_step": dms,
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "tokens_per_s": dw.B / (dms * 1e-3), "algorithmic_bytes": dby,
+                         "steps_timed": args.decode_steps}
+        del S, tok
+
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        Ts = min(args.cpu_tokens, T)
+        out["cpu_baseline"] = cpu_baseline(x, Ts, threads)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

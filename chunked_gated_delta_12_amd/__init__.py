@@ -1,0 +1,205 @@
+"""Python binding of libkda, the KDA operator for MI355X (gfx950).
+
+The functions here carry the C entry points' names and only marshal arguments:
+they check torch tensors (device, dtype, shape, contiguity), allocate outputs
+and workspace with torch (device memory is plumbing), pass raw pointers and
+the current HIP stream to libkda, and raise on a non-OK status.  Every step of
+the operator runs in libkda's HIP kernels; there is no fallback.  If libkda.so
+has not been built, every call raises.
+
+    o, S_T = kda_chunk_fwd(q, k, v, theta, beta, S0=None)
+    o      = kda_decode_step(q, k, v, theta, beta, S)        # S updated in place
+    g, gc  = kda_gate(theta)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+HEADER_PATH = os.path.join(_HERE, "..", "include", "kda.h")
+
+KDA_BF16, KDA_F32 = 0, 1
+KDA_CHUNK = 16
+KDA_G_MIN = -5.0
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it first "
+                           "(python -m chunked_gated_delta_12_amd.build)")
+    lib = ctypes.CDLL(path)
+    c_int, c_size, vp, fp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+    lib.kda_chunk_fwd.argtypes = [c_int] * 7 + [vp] * 3 + [fp] * 3 + [vp, fp, vp, c_size, vp]
+    lib.kda_chunk_fwd.restype = c_int
+    lib.kda_chunk_fwd_workspace_size.argtypes = [c_int] * 6 + [ctypes.POINTER(c_size)]
+    lib.kda_chunk_fwd_workspace_size.restype = c_int
+    lib.kda_chunk_fwd_auto_segments.argtypes = [c_int] * 5
+    lib.kda_chunk_fwd_auto_segments.restype = c_int
+    lib.kda_decode_step.argtypes = [c_int] * 5 + [vp] * 3 + [fp] * 3 + [vp, vp]
+    lib.kda_decode_step.restype = c_int
+    lib.kda_gate.argtypes = [c_int] * 4 + [fp, fp, fp, vp]
+    lib.kda_gate.restype = c_int
+    lib.kda_status_string.argtypes = [c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions include/kda.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def _check(fn, status):
+    if status != 0:
+        lib = load_library()
+        raise KdaError(fn, status, lib.kda_last_error().decode() or lib.kda_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kda_chunk_fwd_auto_segments(B, T, H, dk, dv) -> int:
+    return int(load_library().kda_chunk_fwd_auto_segments(B, T, H, dk, dv))
+
+
+def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments=0) -> int:
+    n = ctypes.c_size_t(0)
+    _check("kda_chunk_fwd_workspace_size",
+           load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments, ctypes.byref(n)))
+    return int(n.value)
+
+
+def kda_chunk_fwd(q, k, v, theta, beta, S0=None, *, segments=0, o=None, S_T=None,
+                  want_state=True, workspace=None, stream=None):
+    """Chunked prefill.  q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32), theta
+    [B,T,H,dk] fp32, beta [B,T,H] fp32, S0 [B,H,dk,dv] fp32 or None.
+    Returns (o, S_T); S_T is None when want_state is False."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(q, "q", dt, (B, T, H, dk), dev)
+    _need(k, "k", dt, (B, T, H, dk), dev)
+    _need(v, "v", dt, (B, T, H, dv), dev)
+    _need(theta, "theta", torch.float32, (B, T, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _need(o, "o", dt, (B, T, H, dv), dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
+    nbytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.kda_chunk_fwd(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
+                           _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
+                           _stream(q, stream))
+    _check("kda_chunk_fwd", st)
+    return o, S_T
+
+
+def kda_decode_step(q, k, v, theta, beta, S, *, o=None, stream=None):
+    """One decode step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), theta [B,H,dk]
+    fp32, beta [B,H] fp32, S [B,H,dk,dv] fp32 (updated in place).  Returns o."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(q, "q", dt, (B, H, dk), dev)
+    _need(k, "k", dt, (B, H, dk), dev)
+    _need(v, "v", dt, (B, H, dv), dev)
+    _need(theta, "theta", torch.float32, (B, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(S, "S", torch.float32, (B, H, dk, dv), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _need(o, "o", dt, (B, H, dv), dev)
+    st = lib.kda_decode_step(code, B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(beta),
+                             _ptr(S), _ptr(o), _stream(q, stream))
+    _check("kda_decode_step", st)
+    return o
+
+
+def kda_gate(theta, *, g=True, g_cum=True, stream=None):
+    """Bounded gate. theta [B,T,H,dk] fp32 -> (g, g_cum) fp32 (either may be skipped
+    by passing False).  Pre-allocated tensors may be passed instead of True."""
+    lib = load_library()
+    B, T, H, dk = theta.shape
+    dev = theta.device
+    _need(theta, "theta", torch.float32, (B, T, H, dk), dev)
+    if g is True:
+        g = torch.empty_like(theta)
+    if g_cum is True:
+        g_cum = torch.empty_like(theta)
+    g = g if isinstance(g, torch.Tensor) else None
+    g_cum = g_cum if isinstance(g_cum, torch.Tensor) else None
+    for name, t in (("g", g), ("g_cum", g_cum)):
+        if t is not None:
+            _need(t, name, torch.float32, (B, T, H, dk), dev)
+    st = lib.kda_gate(B, T, H, dk, _ptr(theta), _ptr(g), _ptr(g_cum), _stream(theta, stream))
+    _check("kda_gate", st)
+    return g, g_cum
+
+
+__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_gate", "kda_chunk_fwd_workspace_size",
+           "kda_chunk_fwd_auto_segments", "load_library", "header_functions", "KdaError",
+           "KDA_BF16", "KDA_F32", "KDA_CHUNK", "KDA_G_MIN"]

@@ -1,0 +1,218 @@
+// kda_api.cpp -- the C ABI of libkda (declared in include/kda.h).
+//
+// Every entry point validates all of its arguments on the host first (sizes,
+// dtype, NULL pointers, 16-byte alignment, overlaps, workspace size) and only
+// then touches HIP, so a rejected call enqueues nothing.  Problems are
+// reported as kda_status codes plus a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return KDA_OK;
+}
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;   // [lo, hi); empty when the pointer is NULL
+};
+
+Range rng(const char* name, const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{name, a, p ? a + bytes : a};
+}
+
+bool overlap(const Range& a, const Range& b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Product of sizes must stay far inside int64 for the kernels' index math.
+bool sizes_fit(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const double x = (double)a * (double)b * (double)c * (double)d;
+    return x < 4.0e18;
+}
+
+int check_common(int dtype, int B, int H, int dk, int dv) {
+    if (dtype != KDA_BF16 && dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (B < 1 || H < 1) return fail(KDA_ERR_SHAPE, "B=%d H=%d must be >= 1", B, H);
+    if (!supported_d(dk) || dk != dv)
+        return fail(KDA_ERR_SHAPE, "dk=%d dv=%d: need dk == dv in {16, 32, 64, 128}", dk, dv);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "unsupported or inconsistent sizes";
+        case KDA_ERR_DTYPE: return "unknown dtype";
+        case KDA_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_ALIAS: return "output overlaps an input";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+int kda_chunk_fwd_auto_segments(int B, int T, int H, int dk, int dv) {
+    if (B < 1 || T < 1 || H < 1 || !supported_d(dk) || dk != dv) return 0;
+    // Aim for >= 512 workgroups in the output pass (two per compute unit on a
+    // 256-CU part) while keeping every segment at least 16 chunks long.
+    const int64_t bh = (int64_t)B * H;
+    const int64_t nchunks = ((int64_t)T + KDA_CHUNK - 1) / KDA_CHUNK;
+    if (bh >= 512) return 1;
+    int64_t want = (512 + bh - 1) / bh;
+    int64_t cap = nchunks / 16;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    return (int)kda::plan_segments(T, (int)want).nseg;
+}
+
+int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
+    int st = check_common(KDA_BF16, B, H, dk, dv);
+    if (st) return st;
+    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
+    const int nchunks = (T + KDA_CHUNK - 1) / KDA_CHUNK;
+    if (segments < 0 || segments > nchunks)
+        return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);
+    const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
+    const kda::SegPlan p = kda::plan_segments(T, req);
+    *bytes = kda::chunk_workspace_bytes(B, H, dk, dv, p.nseg);
+    return ok();
+}
+
+int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
+                  const void* k, const void* v, const float* theta, const float* beta,
+                  const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    int st = check_common(dtype, B, H, dk, dv);
+    if (st) return st;
+    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
+    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*d too large");
+    const int nchunks = (T + KDA_CHUNK - 1) / KDA_CHUNK;
+    if (segments < 0 || segments > nchunks)
+        return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);
+    if (!q || !k || !v || !theta || !beta || !o)
+        return fail(KDA_ERR_NULL, "q, k, v, theta, beta and o must be non-NULL");
+    const void* all[] = {q, k, v, theta, beta, S0, o, S_T, workspace};
+    const char* names[] = {"q", "k", "v", "theta", "beta", "S0", "o", "S_T", "workspace"};
+    for (int i = 0; i < 9; ++i)
+        if (all[i] && !aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+
+    const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
+    const kda::SegPlan plan = kda::plan_segments(T, req);
+    const size_t need = kda::chunk_workspace_bytes(B, H, dk, dv, plan.nseg);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+
+    const size_t es = dtype == KDA_BF16 ? 2 : 4;
+    const size_t tok = (size_t)B * T * H;
+    const size_t st_bytes = (size_t)B * H * dk * dv * 4;
+    const Range in[] = {rng("q", q, tok * dk * es), rng("k", k, tok * dk * es), rng("v", v, tok * dv * es),
+                        rng("theta", theta, tok * dk * 4), rng("beta", beta, tok * 4),
+                        rng("S0", S0, S0 ? st_bytes : 0)};
+    const Range r_o = rng("o", o, tok * dv * es);
+    const Range r_st = rng("S_T", S_T, S_T ? st_bytes : 0);
+    const Range r_ws = rng("workspace", workspace, need);
+    for (const Range& x : in) {
+        if (overlap(r_o, x)) return fail(KDA_ERR_ALIAS, "o overlaps %s", x.name);
+        if (overlap(r_ws, x)) return fail(KDA_ERR_ALIAS, "workspace overlaps %s", x.name);
+        if (overlap(r_st, x) && !(x.name[0] == 'S' && (const void*)S0 == (const void*)S_T))
+            return fail(KDA_ERR_ALIAS, "S_T overlaps %s (only S_T == S0 is allowed)", x.name);
+    }
+    if (overlap(r_o, r_st)) return fail(KDA_ERR_ALIAS, "o overlaps S_T");
+    if (overlap(r_o, r_ws)) return fail(KDA_ERR_ALIAS, "o overlaps workspace");
+    if (overlap(r_st, r_ws)) return fail(KDA_ERR_ALIAS, "S_T overlaps workspace");
+
+    hipError_t e = kda::launch_chunk_fwd(dtype == KDA_F32, B, T, H, dk, plan, q, k, v, theta, beta, S0,
+                                         o, S_T, need ? workspace : nullptr,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int kda_decode_step(int dtype, int B, int H, int dk, int dv, const void* q, const void* k,
+                    const void* v, const float* theta, const float* beta, float* S, void* o,
+                    void* stream) {
+    int st = check_common(dtype, B, H, dk, dv);
+    if (st) return st;
+    if (!sizes_fit(B, H, dk, dv) || (int64_t)B * H > 0x7fffffffLL)
+        return fail(KDA_ERR_SHAPE, "B*H too large");
+    if (!q || !k || !v || !theta || !beta || !S || !o)
+        return fail(KDA_ERR_NULL, "q, k, v, theta, beta, S and o must be non-NULL");
+    const void* all[] = {q, k, v, theta, beta, S, o};
+    const char* names[] = {"q", "k", "v", "theta", "beta", "S", "o"};
+    for (int i = 0; i < 7; ++i)
+        if (!aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t es = dtype == KDA_BF16 ? 2 : 4;
+    const size_t bh = (size_t)B * H;
+    const Range in[] = {rng("q", q, bh * dk * es), rng("k", k, bh * dk * es), rng("v", v, bh * dv * es),
+                        rng("theta", theta, bh * dk * 4), rng("beta", beta, bh * 4)};
+    const Range r_s = rng("S", S, bh * dk * dv * 4);
+    const Range r_o = rng("o", o, bh * dv * es);
+    for (const Range& x : in) {
+        if (overlap(r_o, x)) return fail(KDA_ERR_ALIAS, "o overlaps %s", x.name);
+        if (overlap(r_s, x)) return fail(KDA_ERR_ALIAS, "S overlaps %s", x.name);
+    }
+    if (overlap(r_o, r_s)) return fail(KDA_ERR_ALIAS, "o overlaps S");
+
+    hipError_t e = kda::launch_decode(dtype == KDA_F32, B, H, dk, q, k, v, theta, beta, S, o,
+                                      reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int kda_gate(int B, int T, int H, int dk, const float* theta, float* g, float* g_cum, void* stream) {
+    if (B < 1 || T < 1 || H < 1) return fail(KDA_ERR_SHAPE, "B=%d T=%d H=%d must be >= 1", B, T, H);
+    if (!supported_d(dk)) return fail(KDA_ERR_SHAPE, "dk=%d not in {16, 32, 64, 128}", dk);
+    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*dk too large");
+    if (!theta) return fail(KDA_ERR_NULL, "theta is NULL");
+    if (!g && !g_cum) return fail(KDA_ERR_NULL, "both g and g_cum are NULL");
+    const void* all[] = {theta, g, g_cum};
+    const char* names[] = {"theta", "g", "g_cum"};
+    for (int i = 0; i < 3; ++i)
+        if (all[i] && !aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t n = (size_t)B * T * H * dk * 4;
+    const Range rt = rng("theta", theta, n), rg_ = rng("g", g, g ? n : 0), rc = rng("g_cum", g_cum, g_cum ? n : 0);
+    if (overlap(rg_, rt) || overlap(rc, rt)) return fail(KDA_ERR_ALIAS, "g or g_cum overlaps theta");
+    if (overlap(rg_, rc)) return fail(KDA_ERR_ALIAS, "g overlaps g_cum");
+
+    hipError_t e = kda::launch_gate(B, T, H, dk, theta, g, g_cum, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// kda_device.hpp -- device-side building blocks shared by the libkda kernels
+// (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used throughout (64-lane wavefront, lane = 16*g + r,
+// r = lane & 15, g = lane >> 4):
+//   * a 16x16 fp32 accumulator tile D holds D[4*g + i][r] in element i (i = 0..3);
+//   * the A operand of a 16x16xK product supplies row r of A, the B operand
+//     supplies column r of B; lane group g supplies a group of consecutive
+//     k-slots (1 slot for K = 4 fp32, 4 for K = 16 bf16, 8 for K = 32 bf16).
+// Which logical contraction index sits in which (g, slot) only has to agree
+// between A and B, so every product below states the index map it uses.
+// An accumulator tile, read as B, puts row 4*g + i in slot i -- the same map a
+// 16x16x16 bf16 B operand uses -- so recurrent state and per-chunk results feed
+// the next product straight from registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+
+constexpr int CHUNK = 16;       // tokens per chunk
+constexpr float G_MIN = -5.0f;  // lower bound of the log-decay
+
+// ---------------------------------------------------------------- gate
+// g = G_MIN * sigmoid(theta); saturates to exactly 0 for theta -> -inf and
+// G_MIN for theta -> +inf.
+__device__ __forceinline__ float gate_logdecay(float theta) {
+    const float e = __expf(-theta);
+    return G_MIN * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+
+template <typename E> __device__ __forceinline__ E from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }  // RNE
+
+// Two adjacent elements of a storage type, loaded/stored as one unit.
+template <typename E> struct Pair;
+template <> struct Pair<float> { typedef f32x2 T; };
+template <> struct Pair<bf16> { typedef bf16x2 T; };
+
+template <typename E>
+__device__ __forceinline__ f32x2 load_pair(const E* p) {
+    typename Pair<E>::T v = *reinterpret_cast<const typename Pair<E>::T*>(p);
+    return f32x2{to_f(v[0]), to_f(v[1])};
+}
+template <typename E>
+__device__ __forceinline__ void store_pair(E* p, float a, float b) {
+    typename Pair<E>::T v;
+    v[0] = from_f<E>(a);
+    v[1] = from_f<E>(b);
+    *reinterpret_cast<typename Pair<E>::T*>(p) = v;
+}
+
+// ---------------------------------------------------------------- MFMA wrappers
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x4 ld_b4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ bf16x8 ld_b8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------- 16x16 products
+// Ops<E> evaluates D += A * B for 16x16 output tiles with operands of element
+// type E (bf16: bf16 matrix cores, fp32 accumulate; float: fp32 matrix cores).
+//
+// mm_ll<K>(A, lda, Bt, ldb, acc): A is 16 x K row-major at A (leading dim lda),
+//   B is K x 16 given transposed, Bt[n][k] = B[k][n], row-major at Bt.
+// mm_la<K>(A, lda, Bf, acc): A as above; B is K x 16 held as K/16 accumulator
+//   tiles converted with to_b (tile t holds B rows 16t..16t+15).
+template <typename E> struct Ops;
+
+template <> struct Ops<bf16> {
+    typedef bf16x4 BFrag;
+    static __device__ __forceinline__ BFrag to_b(f32x4 x) {
+        return BFrag{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+    }
+    // k-map: K = 16: slot s of group g is k = 4g + s;
+    //        K >= 32: block kb, slot s of group g is k = 32kb + 8g + s.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_ll(const bf16* A, int lda, const bf16* Bt, int ldb,
+                                                  f32x4 acc, int r, int g) {
+        if constexpr (K == 16) {
+            acc = mfma_k16(ld_b4(A + r * lda + 4 * g), ld_b4(Bt + r * ldb + 4 * g), acc);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb)
+                acc = mfma_k32(ld_b8(A + r * lda + 32 * kb + 8 * g),
+                               ld_b8(Bt + r * ldb + 32 * kb + 8 * g), acc);
+        }
+        return acc;
+    }
+    // k-map: K = 16: k = 4g + s;  K >= 32: block kb, slot s < 4 is k = 32kb + 4g + s
+    //        (tile 2kb), slot s >= 4 is k = 32kb + 16 + 4g + (s - 4) (tile 2kb + 1).
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_la(const bf16* A, int lda, const BFrag* Bf,
+                                                  f32x4 acc, int r, int g) {
+        if constexpr (K == 16) {
+            acc = mfma_k16(ld_b4(A + r * lda + 4 * g), Bf[0], acc);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const bf16* a = A + r * lda + 32 * kb + 4 * g;
+                acc = mfma_k32(cat8(ld_b4(a), ld_b4(a + 16)), cat8(Bf[2 * kb], Bf[2 * kb + 1]), acc);
+            }
+        }
+        return acc;
+    }
+
+    // As mm_la, with A read from global fp32 memory (row-major, leading dim lda)
+    // and rounded to bf16 on the fly.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_ga(const float* A, int64_t lda, const BFrag* Bf,
+                                                  f32x4 acc, int r, int g) {
+        if constexpr (K == 16) {
+            acc = mfma_k16(to_b(*reinterpret_cast<const f32x4*>(A + r * lda + 4 * g)), Bf[0], acc);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const float* a = A + r * lda + 32 * kb + 4 * g;
+                const bf16x4 lo = to_b(*reinterpret_cast<const f32x4*>(a));
+                const bf16x4 hi = to_b(*reinterpret_cast<const f32x4*>(a + 16));
+                acc = mfma_k32(cat8(lo, hi), cat8(Bf[2 * kb], Bf[2 * kb + 1]), acc);
+            }
+        }
+        return acc;
+    }
+};
+
+template <> struct Ops<float> {
+    typedef f32x4 BFrag;
+    static __device__ __forceinline__ BFrag to_b(f32x4 x) { return x; }
+    // k-map: step kk, group g is k = 4kk + g.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_ll(const float* A, int lda, const float* Bt, int ldb,
+                                                  f32x4 acc, int r, int g) {
+#pragma unroll
+        for (int kk = 0; kk < K / 4; ++kk)
+            acc = mfma_k4(A[r * lda + 4 * kk + g], Bt[r * ldb + 4 * kk + g], acc);
+        return acc;
+    }
+    // k-map: step (t, i), group g is k = 16t + 4g + i.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_la(const float* A, int lda, const BFrag* Bf,
+                                                  f32x4 acc, int r, int g) {
+#pragma unroll
+        for (int t = 0; t < K / 16; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], Bf[t][i], acc);
+        }
+        return acc;
+    }
+
+    // As mm_la, with A read from global fp32 memory.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_ga(const float* A, int64_t lda, const BFrag* Bf,
+                                                  f32x4 acc, int r, int g) {
+#pragma unroll
+        for (int t = 0; t < K / 16; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], Bf[t][i], acc);
+        }
+        return acc;
+    }
+};
+
+}  // namespace kda

@@ -1,0 +1,36 @@
+// kda_launch.hpp -- internal host-side launchers of the libkda kernels.
+// Arguments are validated by the C ABI layer before any of these is called;
+// each returns the hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Segmentation of a sequence of `nchunks` 16-token chunks into `nseg`
+// contiguous runs of `seg_len` chunks (the last one possibly shorter).
+struct SegPlan {
+    int nchunks;
+    int seg_len;
+    int nseg;
+};
+SegPlan plan_segments(int T, int requested);
+
+// Workspace bytes of a chunked prefill with `nseg` segments.
+size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg);
+
+hipError_t launch_gate(int B, int T, int H, int dk, const float* theta, float* g, float* gcum,
+                       hipStream_t stream);
+
+hipError_t launch_decode(bool f32, int B, int H, int d, const void* q, const void* k,
+                         const void* v, const float* theta, const float* beta, float* S, void* o,
+                         hipStream_t stream);
+
+hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
+                            const void* q, const void* k, const void* v, const float* theta,
+                            const float* beta, const float* S0, void* o, float* S_T,
+                            void* workspace, hipStream_t stream);
+
+}  // namespace kda

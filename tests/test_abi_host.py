@@ -1,0 +1,141 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+libkda validates every argument before its first HIP call, so each error path
+below is exercised with made-up device addresses that are never dereferenced.
+"""
+import ctypes
+
+import pytest
+
+import chunked_gated_delta_12_amd as kda
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, ALIAS = 0, 1, 2, 3, 4, 5, 6
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return kda.load_library()
+    except RuntimeError as e:   # not built in this checkout
+        pytest.skip(str(e))
+
+
+def test_exports_every_declared_function(lib):
+    names = kda.header_functions()
+    assert {"kda_chunk_fwd", "kda_decode_step", "kda_gate"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for s in range(8):
+        assert lib.kda_status_string(s).decode()
+    assert lib.kda_status_string(99).decode() == "unknown status"
+
+
+class Bufs:
+    """Disjoint, 16-byte aligned fake device addresses for a chunk_fwd call."""
+    def __init__(self, B=1, T=64, H=2, d=64, es=2):
+        tok = B * T * H
+        sizes = dict(q=tok * d * es, k=tok * d * es, v=tok * d * es, theta=tok * d * 4, beta=tok * 4,
+                     S0=B * H * d * d * 4, o=tok * d * es, S_T=B * H * d * d * 4, ws=64 * MB)
+        base = 1 << 40
+        self.addr = {}
+        for name, n in sizes.items():
+            self.addr[name] = base
+            base += (n + 4095) // 4096 * 4096 + 4096
+        self.B, self.T, self.H, self.d = B, T, H, d
+
+    def call(self, lib, dtype=0, segments=1, ws_bytes=64 * MB, **over):
+        a = dict(self.addr)
+        a.update(over)
+        p = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+        return lib.kda_chunk_fwd(dtype, self.B, self.T, self.H, a.get("dk", self.d), a.get("dv", self.d),
+                                 segments, p("q"), p("k"), p("v"), p("theta"), p("beta"), p("S0"),
+                                 p("o"), p("S_T"), p("ws"), ws_bytes, None)
+
+
+def test_chunk_fwd_rejects_bad_dtype_and_sizes(lib):
+    b = Bufs()
+    assert b.call(lib, dtype=2) == DTYPE
+    assert b.call(lib, dk=48, dv=48) == SHAPE
+    assert b.call(lib, dk=64, dv=32) == SHAPE
+    T0 = Bufs(T=64)
+    T0.T = 0
+    assert T0.call(lib) == SHAPE
+    assert b.call(lib, segments=-1) == SHAPE
+    assert b.call(lib, segments=5) == SHAPE          # only 4 chunks in T = 64
+    assert "segments" in lib.kda_last_error().decode()
+
+
+def test_chunk_fwd_rejects_null_misaligned_alias(lib):
+    b = Bufs()
+    for name in ("q", "k", "v", "theta", "beta", "o"):
+        assert b.call(lib, **{name: None}) == NULL, name
+    assert b.call(lib, q=b.addr["q"] + 8) == ALIGN
+    assert b.call(lib, S_T=b.addr["S_T"] + 4) == ALIGN
+    assert b.call(lib, o=b.addr["q"]) == ALIAS                    # o over an input
+    assert b.call(lib, o=b.addr["S_T"]) == ALIAS                  # o over the state
+    assert b.call(lib, S_T=b.addr["theta"]) == ALIAS
+    assert b.call(lib, S_T=b.addr["S0"] + 16) == ALIAS            # partial overlap with S0
+    assert b.call(lib, ws=b.addr["v"], segments=2) == ALIAS
+
+
+def test_chunk_fwd_workspace_checks(lib):
+    b = Bufs(T=1024, H=2, d=64)
+    need = kda.kda_chunk_fwd_workspace_size(1, 1024, 2, 64, 64, 4)
+    assert need > 0
+    assert b.call(lib, segments=4, ws_bytes=need - 1) == WORKSPACE
+    assert b.call(lib, segments=4, ws=None, ws_bytes=0) == WORKSPACE
+    assert kda.kda_chunk_fwd_workspace_size(1, 1024, 2, 64, 64, 1) == 0
+
+
+def test_workspace_formula_and_auto_segments(lib):
+    # [N | M] per segment but the last, plus a start state per segment, fp32
+    B, T, H, d, P = 1, 65536, 16, 128, 32
+    want = ((P - 1) * B * H * d * 2 * d + P * B * H * d * d) * 4
+    assert kda.kda_chunk_fwd_workspace_size(B, T, H, d, d, P) == want
+    assert kda.kda_chunk_fwd_auto_segments(1, 65536, 16, 128, 128) == 32
+    assert kda.kda_chunk_fwd_auto_segments(64, 4096, 16, 128, 128) == 1
+    assert kda.kda_chunk_fwd_auto_segments(1, 64, 1, 16, 16) == 1       # too short to split
+    assert kda.kda_chunk_fwd_auto_segments(1, 64, 1, 24, 24) <= 0       # unsupported size
+    with pytest.raises(kda.KdaError):
+        kda.kda_chunk_fwd_workspace_size(1, 0, 1, 16, 16)
+
+
+def test_decode_step_validation(lib):
+    base = 1 << 41
+    B, H, d = 4, 2, 64
+    addr = {}
+    for name, n in dict(q=B * H * d * 2, k=B * H * d * 2, v=B * H * d * 2, theta=B * H * d * 4,
+                        beta=B * H * 4, S=B * H * d * d * 4, o=B * H * d * 2).items():
+        addr[name] = base
+        base += (n + 4095) // 4096 * 4096 + 4096
+
+    def call(dtype=0, dk=d, dv=d, **over):
+        a = dict(addr)
+        a.update(over)
+        p = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+        return lib.kda_decode_step(dtype, B, H, dk, dv, p("q"), p("k"), p("v"), p("theta"), p("beta"),
+                                   p("S"), p("o"), None)
+
+    assert call(dtype=7) == DTYPE
+    assert call(dk=16, dv=32) == SHAPE
+    assert call(S=None) == NULL
+    assert call(o=addr["o"] + 2) == ALIGN
+    assert call(o=addr["S"]) == ALIAS
+    assert call(S=addr["q"]) == ALIAS
+
+
+def test_gate_validation(lib):
+    th, g, gc = 1 << 42, (1 << 42) + (64 << 20), (1 << 42) + (128 << 20)
+    vp = ctypes.c_void_p
+    assert lib.kda_gate(1, 64, 2, 16, None, vp(g), vp(gc), None) == NULL
+    assert lib.kda_gate(1, 64, 2, 16, vp(th), None, None, None) == NULL
+    assert lib.kda_gate(1, 0, 2, 16, vp(th), vp(g), vp(gc), None) == SHAPE
+    assert lib.kda_gate(1, 64, 2, 20, vp(th), vp(g), vp(gc), None) == SHAPE
+    assert lib.kda_gate(1, 64, 2, 16, vp(th), vp(th), vp(gc), None) == ALIAS
+    assert lib.kda_gate(1, 64, 2, 16, vp(th), vp(g), vp(g), None) == ALIAS
+    assert lib.kda_gate(1, 64, 2, 16, vp(th + 4), vp(g), None, None) == ALIGN

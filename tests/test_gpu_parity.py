@@ -1,0 +1,252 @@
+"""GPU parity of libkda against the fp64 oracle, through the C ABI.
+
+The bar: max|gpu - ref| / max|ref| <= 2e-2 for bf16 q/k/v and <= 1e-4 in the
+fp32 validation dtype, for o and for the final state; the gate to 1e-5.
+Inputs come from chunked_gated_delta_12_amd.inputs (seeded); the oracle reads
+the very same tensors widened to float64.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_gated_delta_12_amd as kda
+from chunked_gated_delta_12_amd import inputs as kin
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(gpu, ref):
+    gpu = gpu.detach().to("cpu").double().numpy() if isinstance(gpu, torch.Tensor) else gpu
+    scale = np.abs(ref).max()
+    diff = np.abs(gpu - ref).max()
+    if scale == 0:
+        return 0.0 if diff == 0 else float("inf")
+    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
+    return float(diff / scale)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kda.load_library()
+
+
+def to_dev(x):
+    return {k: (v.to(DEV) if v is not None else None) for k, v in x.items()}
+
+
+# ----------------------------------------------------------------------------- gate
+@pytest.mark.parametrize("B,T,H,dk", [(1, 64, 1, 16), (2, 100, 3, 64), (1, 37, 16, 128)])
+def test_gate_matches_oracle(oracle_mod, B, T, H, dk):
+    note(f"gate B={B} T={T} H={H} dk={dk}")
+    gen = torch.Generator().manual_seed(T)
+    theta = torch.randn(B, T, H, dk, generator=gen) * 3.0
+    g, gc = kda.kda_gate(theta.to(DEV))
+    torch.cuda.synchronize()
+    g_ref = oracle_mod.gate(theta)
+    gc_ref = oracle_mod.gate_cumsum(g_ref)
+    assert rel_err(g, g_ref) <= 1e-5
+    assert rel_err(gc, gc_ref) <= 1e-5
+    g_only, none = kda.kda_gate(theta.to(DEV), g_cum=False)
+    assert none is None and torch.equal(g_only, g)
+
+
+# ----------------------------------------------------------------------------- chunked prefill
+CHUNK_CASES = [
+    # (workload, overrides, dtype override, segments)
+    ("tiny", {}, None, 1),
+    ("tiny", {}, None, 3),
+    ("tiny", dict(T=61), None, 1),                                # ragged tail
+    ("tiny", dict(T=5), None, 0),                                 # shorter than one chunk
+    ("small", {}, None, 1),
+    ("small", {}, None, 4),
+    ("small", {}, None, 0),
+    ("small", dict(T=1000 + 7), None, 5),
+    ("small", {}, "f32", 4),                                      # fp32 re-run of the small case
+    ("small", dict(dk=32, dv=32, H=3), None, 2),
+    ("decay_stress", dict(H=4, T=1024), None, 1),
+    ("decay_stress", dict(H=4, T=1024), None, 8),
+    ("decay_stress", dict(H=2, T=512), "f32", 4),                 # fp32 re-run of the stress case
+    ("prefill_64k", dict(H=2, T=2048 + 9), None, 0),
+]
+
+
+def _chunk_case(name, over, dt):
+    w = kin.scaled(kin.WORKLOADS[name], **over)
+    if dt:
+        w = kin.scaled(w, dtype=dt)
+    return w
+
+
+@pytest.mark.parametrize("name,over,dt,segments", CHUNK_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}-seg{c[3]}" for c in CHUNK_CASES])
+def test_chunk_fwd_matches_oracle(oracle_mod, name, over, dt, segments):
+    w = _chunk_case(name, over, dt)
+    note(f"chunk_fwd {w} segments={segments}")
+    x = kin.chunk_inputs(w)
+    d = to_dev(x)
+    o = torch.full((w.B, w.T, w.H, w.dv), float("nan"), device=DEV, dtype=d["q"].dtype)
+    S_T = torch.full((w.B, w.H, w.dk, w.dv), float("nan"), device=DEV)
+    kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], d["S0"], segments=segments,
+                      o=o, S_T=S_T)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_mod.chunk_fwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], x["S0"])
+    eo, es = rel_err(o, o_ref), rel_err(S_T, s_ref)
+    note(f"  err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_chunk_fwd_in_place_state(oracle_mod):
+    """S_T may be the S0 buffer itself, with one segment and with several."""
+    w = kin.WORKLOADS["small"]
+    x = kin.chunk_inputs(w)
+    d = to_dev(x)
+    o_ref, s_ref = oracle_mod.chunk_fwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], x["S0"])
+    for seg in (1, 4):
+        S = d["S0"].clone()
+        o, S_T = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], S, segments=seg, S_T=S)
+        torch.cuda.synchronize()
+        assert S_T.data_ptr() == S.data_ptr()
+        assert rel_err(o, o_ref) <= 2e-2 and rel_err(S, s_ref) <= 2e-2
+
+
+def test_chunk_fwd_deterministic_and_head_equivariant():
+    w = kin.scaled(kin.WORKLOADS["small"], T=512)
+    d = to_dev(kin.chunk_inputs(w))
+    o1, s1 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], d["S0"], segments=3)
+    o2, s2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], d["S0"], segments=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    p = [2, 0, 3, 1]
+    perm = {k: v[:, :, p].contiguous() for k, v in d.items() if k != "S0"}
+    o3, s3 = kda.kda_chunk_fwd(perm["q"], perm["k"], perm["v"], perm["theta"], perm["beta"],
+                               d["S0"][:, p].contiguous(), segments=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o1[:, :, p]) and torch.equal(s3, s1[:, p])
+
+
+def test_chunk_fwd_split_and_resume():
+    w = kin.scaled(kin.WORKLOADS["small"], T=700)
+    d = to_dev(kin.chunk_inputs(w))
+    o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], d["S0"], segments=2)
+    T1 = 333
+    a = {k: v[:, :T1].contiguous() for k, v in d.items() if k != "S0"}
+    bb = {k: v[:, T1:].contiguous() for k, v in d.items() if k != "S0"}
+    o1, s1 = kda.kda_chunk_fwd(a["q"], a["k"], a["v"], a["theta"], a["beta"], d["S0"])
+    o2, s2 = kda.kda_chunk_fwd(bb["q"], bb["k"], bb["v"], bb["theta"], bb["beta"], s1, segments=3)
+    torch.cuda.synchronize()
+    ref_o = o.double().cpu().numpy()
+    assert rel_err(torch.cat([o1, o2], dim=1), ref_o) <= 2e-2
+    assert rel_err(s2, s.double().cpu().numpy()) <= 2e-2
+
+
+def test_chunk_fwd_equals_decode_chain():
+    """T decode steps from S0 give the same outputs as one chunked call."""
+    w = kin.scaled(kin.WORKLOADS["small"], T=40, B=2, H=3)
+    d = to_dev(kin.chunk_inputs(w))
+    o, s = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], d["S0"])
+    S = d["S0"].clone()
+    outs = []
+    for t in range(w.T):
+        outs.append(kda.kda_decode_step(d["q"][:, t].contiguous(), d["k"][:, t].contiguous(),
+                                        d["v"][:, t].contiguous(), d["theta"][:, t].contiguous(),
+                                        d["beta"][:, t].contiguous(), S))
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(outs, dim=1), o.double().cpu().numpy()) <= 2e-2
+    assert rel_err(S, s.double().cpu().numpy()) <= 2e-2
+
+
+# ----------------------------------------------------------------------------- decode
+DECODE_CASES = [(3, 2, 16, "f32", 6), (4, 4, 64, "bf16", 6), (8, 16, 128, "bf16", 4), (5, 3, 128, "f32", 3),
+                (2, 2, 32, "bf16", 5)]
+
+
+@pytest.mark.parametrize("B,H,d,dt,steps", DECODE_CASES)
+def test_decode_step_matches_oracle(oracle_mod, B, H, d, dt, steps):
+    note(f"decode B={B} H={H} d={d} {dt} steps={steps}")
+    w = kin.DecodeWorkload("t", B, H, d, d, steps, dt, 0.0, 2.0, 0.1, 11)
+    S, gen = kin.decode_state(w)
+    tok = kin.decode_token(w, gen, steps=steps)
+    S_dev = S.to(DEV)
+    S_ref = S.double().numpy()
+    for t in range(steps):
+        args = [tok[n][t] for n in ("q", "k", "v", "theta", "beta")]
+        o = torch.full((B, H, d), float("nan"), device=DEV, dtype=kin.torch_dtype(dt))
+        kda.kda_decode_step(*[a.to(DEV) for a in args], S_dev, o=o)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle_mod.decode_step(*args, S_ref)
+        assert rel_err(o, o_ref) <= TOL[dt], f"step {t}"
+    assert rel_err(S_dev, S_ref) <= TOL[dt]
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+def _sampled_chunk_check(oracle_mod, name, cols, heads=None, segments=0):
+    w = kin.WORKLOADS[name]
+    note(f"full-size chunk_fwd {name} {w}")
+    x = kin.chunk_inputs(w, device=DEV)
+    o, S_T = kda.kda_chunk_fwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], x["S0"], segments=segments)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S_T).all())
+    hs = list(range(w.H)) if heads is None else heads
+    sel = lambda t: t[:, :, hs].contiguous().cpu() if t is not None else None
+    o_ref, s_ref = oracle_mod.chunk_fwd(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["theta"]),
+                                        sel(x["beta"]), None, cols=cols)
+    eo = rel_err(o[:, :, hs][..., cols], o_ref)
+    es = rel_err(S_T[:, hs][..., cols], s_ref)
+    note(f"  err_o={eo:.3e} err_S={es:.3e} (heads {hs}, columns {cols})")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+@pytest.mark.slow
+def test_prefill_64k_full_size_sampled_columns(oracle_mod):
+    _sampled_chunk_check(oracle_mod, "prefill_64k", cols=[0, 37, 64, 101, 127])
+
+
+@pytest.mark.slow
+def test_decay_stress_full_size_sampled_columns(oracle_mod):
+    _sampled_chunk_check(oracle_mod, "decay_stress", cols=[1, 17, 50, 77, 126])
+
+
+@pytest.mark.slow
+def test_prefill_1m_sampled_heads_and_columns(oracle_mod):
+    _sampled_chunk_check(oracle_mod, "prefill_1m", cols=[5, 90], heads=[3, 12])
+
+
+@pytest.mark.slow
+def test_decode_b256_1024_steps_sampled_heads(oracle_mod):
+    """1,024 consecutive in-place steps over the full B=256, H=16 state; every step's o
+    and the final S checked on a sample of 48 (batch, head) pairs."""
+    w = kin.DECODE_WORKLOADS["decode_b256"]
+    note(f"decode full size {w}")
+    S, gen = kin.decode_state(w, device=DEV)
+    rng = np.random.default_rng(0)
+    bs = rng.choice(w.B, 48, replace=False)
+    hs = rng.integers(0, w.H, 48)
+    S_ref = S[bs, hs].double().cpu().numpy()[:, None]          # [48, 1, dk, dv]
+    o_buf = torch.empty((w.B, w.H, w.dv), device=DEV, dtype=torch.bfloat16)
+    worst = 0.0
+    for t0 in range(0, w.steps, 64):
+        tok = kin.decode_token(w, gen, device=DEV, steps=64)
+        outs = []
+        for t in range(64):
+            kda.kda_decode_step(tok["q"][t], tok["k"][t], tok["v"][t], tok["theta"][t], tok["beta"][t], S,
+                                o=o_buf)
+            outs.append(o_buf[bs, hs].float().cpu())
+        torch.cuda.synchronize()
+        for t in range(64):
+            args = [tok[n][t][bs, hs].cpu()[:, None] for n in ("q", "k", "v", "theta", "beta")]
+            o_ref, S_ref = oracle_mod.decode_step(*args, S_ref)
+            worst = max(worst, rel_err(outs[t], o_ref[:, 0]))
+    es = rel_err(S[bs, hs], S_ref[:, 0])
+    note(f"  worst per-step err_o={worst:.3e} err_S={es:.3e}")
+    assert worst <= 2e-2 and es <= 2e-2
