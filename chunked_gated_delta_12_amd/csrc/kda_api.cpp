@@ -10,7 +10,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_launch.hpp"
 
 namespace {

@@ -25,10 +25,12 @@
 //                  last segment).
 // With one segment only the out kernel runs, straight from S0.
 //
-// Workgroup = 4 wavefronts.  Per chunk: the gate and all decay-scaled operand
-// tiles are formed once in LDS; A, T, W are shared by the workgroup; the state
-// columns are split into 16-column tiles across the wavefronts, each tile
-// living in fp32 accumulator registers for the whole segment.  All products
+// Workgroup = 8 wavefronts (two per SIMD).  Per chunk: the gate and all
+// decay-scaled operand tiles are formed once in LDS; A, T, W are shared by the
+// workgroup; the state columns are split into 16-column tiles across the
+// wavefronts, each tile living in fp32 accumulator registers for the whole
+// segment.  The next chunk's inputs are loaded while the current one is being
+// processed, and each chunk's o tile is written out during the next chunk.  All products
 // are 16x16 matrix-core tiles (bf16 operands, fp32 accumulation; fp32
 // operands in the validation dtype).
 #include "kda_device.hpp"
@@ -38,7 +40,7 @@ namespace kda {
 
 template <int D, bool MAP>
 struct ChunkCfg {
-    static constexpr int NW = 4;                   // wavefronts per workgroup
+    static constexpr int NW = 8;                   // wavefronts per workgroup (2 per SIMD)
     static constexpr int NTHR = 64 * NW;
     static constexpr int NCOL = MAP ? 2 * D : D;   // state columns carried
     static constexpr int NT = NCOL / 16;           // 16-column tiles
@@ -46,10 +48,11 @@ struct ChunkCfg {
     static constexpr int KT = D / 16;              // 16-row tiles along d_k
     static constexpr int LDR = D + 8;              // padded row of [16][D] tiles
     static constexpr int LDC = 20;                 // padded row of [D][16] tiles
-    static constexpr int PPT = D >= 32 ? D / 32 : 1;  // tokens per thread, gate stage
+    static constexpr int PPT = D >= 128 ? D / 64 : 1;  // tokens per thread, gate stage
     static constexpr int NPG = CHUNK / PPT;           // token groups, gate stage
     static constexpr int NACT = (D / 2) * NPG;        // active threads, gate stage
     static_assert(NACT <= NTHR, "gate stage mapping");
+    static_assert(PPT <= 2, "gate stage packs at most two tokens per column write");
 };
 
 template <typename E, int D, bool MAP>
@@ -59,18 +62,25 @@ struct ChunkSmem {
     alignas(16) E km_row[16 * C::LDR];             // K-               [token][ch]
     alignas(16) E qp_row[MAP ? 8 : 16 * C::LDR];   // Q+               [token][ch]
     alignas(16) E wn_row[16 * C::LDR];             // -W               [token][ch]
+    alignas(16) E o_tile[MAP ? 8 : 16 * C::LDR];   // o of the chunk   [token][col]
     alignas(16) E kp_col[D * C::LDC];              // (beta*K+)^T      [ch][token]
     alignas(16) E ke_col[D * C::LDC];              // Kend^T           [ch][token]
     alignas(16) E vb_col[D * C::LDC];              // (beta*V)^T       [col][token]
     alignas(16) E t_row[16 * C::LDC];              // T                [token][token]
     alignas(16) E aqk_row[MAP ? 8 : 16 * C::LDC];  // LowerIncl(Q+K-^T)[token][token]
-    alignas(16) float akk[16 * 17];                // StrictLower(beta K+ K-^T), fp32
+    alignas(16) float akk_t[16 * 20];              // StrictLower(beta K+ K-^T)^T, fp32
     alignas(16) float gc[D];                       // Gamma_C per channel
     alignas(16) float part[C::NPG * D];            // per-group partial sums of g
 };
 
+// Store units of the o tile: SU bytes per thread and store (4, 8 or 16).
+template <int SU> struct StoreUnit;
+template <> struct StoreUnit<4> { typedef uint32_t T; };
+template <> struct StoreUnit<8> { typedef uint64_t T; };
+template <> struct StoreUnit<16> { typedef f32x4 T; };
+
 template <typename E, int D, bool MAP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
              const float* __restrict__ theta, const float* __restrict__ beta,
@@ -89,7 +99,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     const int c0 = seg * seg_len;
     const int c1 = min(nchunks, c0 + seg_len);
 
-    // gate-stage mapping: channel pair cp, token group pgi
+    // gate-stage mapping: channel pair cp, token group pgi (tokens pgi*PPT ..)
     const int cp = tid % (D / 2), pgi = tid / (D / 2);
     const int ch = 2 * cp;
     const bool gact = tid < C::NACT;
@@ -120,21 +130,48 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         }
     }
 
-    // ---- prefetch registers for one chunk (this thread's gate-stage elements)
-    f32x2 th_r[C::PPT], k_r[C::PPT], q_r[C::PPT], v_r[C::PPT];
+    // ---- prefetch registers for one chunk (this thread's gate-stage elements).
+    // Raw bits are loaded from a clamped, always valid token index so the loads
+    // carry no branch and stay in flight until the next chunk's gate stage;
+    // tokens past T (and idle threads) are masked when the values are used.
+    typedef typename Pair<E>::T RawPair;
+    f32x2 th_r[C::PPT];
+    RawPair k_r[C::PPT], q_r[C::PPT], v_r[C::PPT];
     float b_r[C::PPT];
     auto load_chunk = [&](int n) {
         const int t0 = n * CHUNK;
 #pragma unroll
         for (int p = 0; p < C::PPT; ++p) {
-            const int t = t0 + pgi * C::PPT + p;
-            const bool ok = gact && t < T;
-            const int64_t off = head_base + (int64_t)t * tok_stride + ch;
-            th_r[p] = ok ? *reinterpret_cast<const f32x2*>(theta + off) : f32x2{0.0f, 0.0f};
-            k_r[p] = ok ? load_pair(k + off) : f32x2{0.0f, 0.0f};
-            if constexpr (!MAP) q_r[p] = ok ? load_pair(q + off) : f32x2{0.0f, 0.0f};
-            v_r[p] = ok ? load_pair(v + off) : f32x2{0.0f, 0.0f};
-            b_r[p] = ok ? beta[((int64_t)b * T + t) * H + h] : 0.0f;
+            const int t = min(t0 + pgi * C::PPT + p, T - 1);
+            const int64_t off = head_base + (int64_t)t * tok_stride + (gact ? ch : 0);
+            th_r[p] = *reinterpret_cast<const f32x2*>(theta + off);
+            k_r[p] = *reinterpret_cast<const RawPair*>(k + off);
+            if constexpr (!MAP) q_r[p] = *reinterpret_cast<const RawPair*>(q + off);
+            v_r[p] = *reinterpret_cast<const RawPair*>(v + off);
+            b_r[p] = beta[((int64_t)b * T + t) * H + h];
+        }
+    };
+
+    // ---- write the o tile of chunk n (staged in LDS) with coalesced stores.
+    // Every thread stores the same number of units for a full chunk, so no
+    // branch guards the stores in the main loop; rows past T only occur in
+    // the final chunk, which is stored after the loop with a row mask.
+    constexpr int OB = 16 * D * (int)sizeof(E);             // bytes of one o tile
+    constexpr int SU = OB / C::NTHR >= 16 ? 16 : (OB / C::NTHR >= 8 ? 8 : 4);
+    constexpr int UPR = D * (int)sizeof(E) / SU;            // units per row
+    constexpr int NU = OB / SU;                             // units per tile
+    constexpr int UPT = (NU + C::NTHR - 1) / C::NTHR;       // units per thread
+    typedef typename StoreUnit<SU>::T Unit;
+    auto store_o = [&](int n, bool masked) {
+        const int t0 = n * CHUNK;
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int u = tid + C::NTHR * j;
+            const int row = u / UPR, ce = (u % UPR) * (SU / (int)sizeof(E));
+            if ((NU % C::NTHR == 0 || u < NU) && (!masked || t0 + row < T)) {
+                const Unit val = *reinterpret_cast<const Unit*>(&sm.o_tile[row * C::LDR + ce]);
+                *reinterpret_cast<Unit*>(o + head_base + (int64_t)(t0 + row) * tok_stride + ce) = val;
+            }
         }
     };
 
@@ -168,43 +205,64 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 tot0 += x0;
                 tot1 += x1;
             }
+            const float eC0 = __expf(tot0), eC1 = __expf(tot1);
             if (pgi == 0) {
-                sm.gc[ch] = __expf(tot0);
-                sm.gc[ch + 1] = __expf(tot1);
+                sm.gc[ch] = eC0;
+                sm.gc[ch + 1] = eC1;
             }
+            float kpa[C::PPT], kpb[C::PPT], kea[C::PPT], keb[C::PPT], vba[C::PPT], vbb[C::PPT];
 #pragma unroll
             for (int p = 0; p < C::PPT; ++p) {
                 const int pos = pgi * C::PPT + p;
+                const bool ok = t0 + pos < T;            // padding tokens: k = q = v = beta = 0
                 const float Ga = G0[p] + off0, Gb = G1[p] + off1;
                 const float eGa = __expf(Ga), eGb = __expf(Gb);
                 const float emGa = __expf(-Ga), emGb = __expf(-Gb);
-                const float eEa = __expf(tot0 - Ga), eEb = __expf(tot1 - Gb);
-                const float ka = k_r[p][0], kb = k_r[p][1], bt = b_r[p];
-                const float kpa = bt * ka * eGa, kpb = bt * kb * eGb;
-                store_pair(&sm.kp_row[pos * C::LDR + ch], kpa, kpb);
-                sm.kp_col[ch * C::LDC + pos] = from_f<E>(kpa);
-                sm.kp_col[(ch + 1) * C::LDC + pos] = from_f<E>(kpb);
+                const float ka = ok ? to_f(k_r[p][0]) : 0.0f, kb = ok ? to_f(k_r[p][1]) : 0.0f;
+                const float bt = ok ? b_r[p] : 0.0f;
+                kpa[p] = bt * ka * eGa;
+                kpb[p] = bt * kb * eGb;
+                kea[p] = ka * (eC0 * emGa);        // k * exp(G_C - G), every factor <= 1 in range
+                keb[p] = kb * (eC1 * emGb);
+                vba[p] = ok ? bt * to_f(v_r[p][0]) : 0.0f;
+                vbb[p] = ok ? bt * to_f(v_r[p][1]) : 0.0f;
+                store_pair(&sm.kp_row[pos * C::LDR + ch], kpa[p], kpb[p]);
                 store_pair(&sm.km_row[pos * C::LDR + ch], ka * emGa, kb * emGb);
                 if constexpr (!MAP)
-                    store_pair(&sm.qp_row[pos * C::LDR + ch], q_r[p][0] * eGa, q_r[p][1] * eGb);
-                sm.ke_col[ch * C::LDC + pos] = from_f<E>(ka * eEa);
-                sm.ke_col[(ch + 1) * C::LDC + pos] = from_f<E>(kb * eEb);
-                sm.vb_col[ch * C::LDC + pos] = from_f<E>(bt * v_r[p][0]);
-                sm.vb_col[(ch + 1) * C::LDC + pos] = from_f<E>(bt * v_r[p][1]);
+                    store_pair(&sm.qp_row[pos * C::LDR + ch], ok ? to_f(q_r[p][0]) * eGa : 0.0f,
+                               ok ? to_f(q_r[p][1]) * eGb : 0.0f);
+            }
+            const int pos0 = pgi * C::PPT;
+            if constexpr (C::PPT == 2) {
+                store_pair(&sm.kp_col[ch * C::LDC + pos0], kpa[0], kpa[1]);
+                store_pair(&sm.kp_col[(ch + 1) * C::LDC + pos0], kpb[0], kpb[1]);
+                store_pair(&sm.ke_col[ch * C::LDC + pos0], kea[0], kea[1]);
+                store_pair(&sm.ke_col[(ch + 1) * C::LDC + pos0], keb[0], keb[1]);
+                store_pair(&sm.vb_col[ch * C::LDC + pos0], vba[0], vba[1]);
+                store_pair(&sm.vb_col[(ch + 1) * C::LDC + pos0], vbb[0], vbb[1]);
+            } else {
+                sm.kp_col[ch * C::LDC + pos0] = from_f<E>(kpa[0]);
+                sm.kp_col[(ch + 1) * C::LDC + pos0] = from_f<E>(kpb[0]);
+                sm.ke_col[ch * C::LDC + pos0] = from_f<E>(kea[0]);
+                sm.ke_col[(ch + 1) * C::LDC + pos0] = from_f<E>(keb[0]);
+                sm.vb_col[ch * C::LDC + pos0] = from_f<E>(vba[0]);
+                sm.vb_col[(ch + 1) * C::LDC + pos0] = from_f<E>(vbb[0]);
             }
         }
-        if (n + 1 < c1) load_chunk(n + 1);   // overlaps the rest of this chunk
+        if constexpr (!MAP)
+            if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
+        if (n + 1 < c1) load_chunk(n + 1);        // in flight until the next chunk's gate stage
         __syncthreads();
 
         // ---------------- stage 2: diagonal tiles as dense products
         if (wave == 0) {
             const f32x4 a = MM::template mm_ll<D>(sm.kp_row, C::LDR, sm.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
+            // a[i] = A[row 4g+i][col r]; stored transposed: akk_t[col][row]
+            f32x4 m;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i;
-                sm.akk[row * 17 + r] = (r < row) ? a[i] : 0.0f;     // mask by select
-            }
+            for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? a[i] : 0.0f;   // mask by select
+            *reinterpret_cast<f32x4*>(&sm.akk_t[r * 20 + 4 * g]) = m;
         } else if (!MAP && wave == 1) {
             const f32x4 a = MM::template mm_ll<D>(sm.qp_row, C::LDR, sm.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
@@ -216,17 +274,32 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         }
         __syncthreads();
 
-        // ---------------- stage 3: T = (I + A)^-1 by forward substitution (fp32)
-        if (wave == 0 && lane < 16) {
-            const int j = lane;   // this lane solves column j
-            float tc[16];
+        // ---------------- stage 3: T = (I + A)^-1, column j per lane, right-looking
+        // substitution: once x[s] is final, every later row subtracts A[r][s] x[s].
+        if (wave == 0) {
+            const int j = lane & 15;
+            float x[16];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float acc = (rr == j) ? 1.0f : 0.0f;
+            for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.0f : 0.0f;
+            f32x4 col[4], nxt[4];
 #pragma unroll
-                for (int s = 0; s < rr; ++s) acc -= sm.akk[rr * 17 + s] * tc[s];
-                tc[rr] = acc;
-                sm.t_row[rr * C::LDC + j] = from_f<E>(acc);
+            for (int c = 0; c < 4; ++c) col[c] = *reinterpret_cast<const f32x4*>(&sm.akk_t[4 * c]);
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                if (s + 1 < 15) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        nxt[c] = *reinterpret_cast<const f32x4*>(&sm.akk_t[(s + 1) * 20 + 4 * c]);
+                }
+                const float xs = x[s];
+#pragma unroll
+                for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) col[c] = nxt[c];
+            }
+            if (lane < 16) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) sm.t_row[rr * C::LDC + j] = from_f<E>(x[rr]);
             }
         }
         __syncthreads();
@@ -264,10 +337,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 f32x4 oo = MM::template mm_la<D>(sm.qp_row, C::LDR, sb, f32x4{0, 0, 0, 0}, r, g);
                 oo = MM::template mm_la<16>(sm.aqk_row, C::LDC, &ub, oo, r, g);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = t0 + 4 * g + i;
-                    if (t < T) o[head_base + (int64_t)t * tok_stride + 16 * jt + r] = from_f<E>(oo[i]);
-                }
+                for (int i = 0; i < 4; ++i) sm.o_tile[(4 * g + i) * C::LDR + 16 * jt + r] = from_f<E>(oo[i]);
             }
 #pragma unroll
             for (int t = 0; t < C::KT; ++t) {
@@ -279,6 +349,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         }
         __syncthreads();
     }
+    if constexpr (!MAP) store_o(c1 - 1, true);
 
     // ---- write the segment's final state
 #pragma unroll
@@ -302,61 +373,108 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
 // Start state of every segment: S_0 = S0 (or 0), S_{s+1} = M_s S_s + N_s, where
 // [N_s | M_s] is the widened end state the map kernel stored for segment s.
-// One workgroup per head; 16-column tiles of the state across its wavefronts.
+// One workgroup of 8 wavefronts per head, one 16-column tile of the state per
+// wavefront.  M_s is staged through LDS (rounded to the operand type) while
+// M_{s+1} is already being fetched into registers; N_s is fetched at the start
+// of the step and added after the products, so no global load sits on the
+// per-step critical path.
 template <typename E, int D>
-__global__ void __launch_bounds__(256)
+struct CombineCfg {
+    static constexpr int NW = 8, NTHR = 64 * NW;
+    static constexpr int NT = D / 16, TPW = (NT + NW - 1) / NW, KT = D / 16;
+    static constexpr int LDM = D + 8;
+    static constexpr int MV = D * D / 4 / NTHR > 0 ? D * D / 4 / NTHR : 1;   // float4 of M per thread
+};
+
+template <typename E, int D>
+__global__ void __launch_bounds__(512)
 combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_mn,
                float* __restrict__ ws_start) {
-    constexpr int NW = 4, NT = D / 16, TPW = (NT + NW - 1) / NW, KT = D / 16;
+    typedef CombineCfg<E, D> C;
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
+    __shared__ alignas(16) E m_lds[D * C::LDM];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int bh = blockIdx.x;
 
-    f32x4 S[TPW][KT];
+    f32x4 S[C::TPW][C::KT];
 #pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) {
-        const int jt = wave + NW * jj;
+    for (int jj = 0; jj < C::TPW; ++jj) {
+        const int jt = wave + C::NW * jj;
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
+        for (int t = 0; t < C::KT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * t + 4 * g + i;
-                S[jj][t][i] = (S0 && jt < NT) ? S0[((int64_t)bh * D + row) * D + 16 * jt + r] : 0.0f;
+                S[jj][t][i] = (S0 && jt < C::NT) ? S0[((int64_t)bh * D + row) * D + 16 * jt + r] : 0.0f;
             }
     }
     auto store = [&](int s) {
         float* dst = ws_start + ((int64_t)s * BH + bh) * D * D;
 #pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) {
-            const int jt = wave + NW * jj;
-            if (jt >= NT) continue;
+        for (int jj = 0; jj < C::TPW; ++jj) {
+            const int jt = wave + C::NW * jj;
+            if (jt >= C::NT) continue;
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
+            for (int t = 0; t < C::KT; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * t + 4 * g + i) * D + 16 * jt + r] = S[jj][t][i];
         }
     };
+    // M_s: row-major [D][D] inside the [D][2D] block, read as float4s spread over the workgroup
+    f32x4 mreg[C::MV];
+    auto fetch_m = [&](int s) {
+        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);
+#pragma unroll
+        for (int j = 0; j < C::MV; ++j) {
+            const int f = min(tid + C::NTHR * j, D * D / 4 - 1);
+            const int row = f / (D / 4), c4 = f % (D / 4);
+            mreg[j] = *reinterpret_cast<const f32x4*>(X + (int64_t)row * (2 * D) + D + 4 * c4);
+        }
+    };
     store(0);
+    if (nseg > 1) fetch_m(0);
     for (int s = 0; s + 1 < nseg; ++s) {
-        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);   // [D][2D] = [N | M]
+        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);
 #pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) {
-            const int jt = wave + NW * jj;
-            if (jt >= NT) continue;
-            BFrag sb[KT];
+        for (int j = 0; j < C::MV; ++j) {
+            const int f = tid + C::NTHR * j;
+            if (f < D * D / 4) {
+                const int row = f / (D / 4), c4 = f % (D / 4);
 #pragma unroll
-            for (int t = 0; t < KT; ++t) sb[t] = MM::to_b(S[jj][t]);
+                for (int e = 0; e < 4; ++e) m_lds[row * C::LDM + 4 * c4 + e] = from_f<E>(mreg[j][e]);
+            }
+        }
+        f32x4 nreg[C::TPW][C::KT];
 #pragma unroll
-            for (int rt = 0; rt < KT; ++rt) {
-                f32x4 acc;
+        for (int jj = 0; jj < C::TPW; ++jj) {
+            const int jt = min(wave + C::NW * jj, C::NT - 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = X[(int64_t)(16 * rt + 4 * g + i) * (2 * D) + 16 * jt + r];
-                S[jj][rt] = MM::template mm_ga<D>(X + (int64_t)16 * rt * (2 * D) + D, 2 * D, sb, acc, r, g);
+            for (int t = 0; t < C::KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    nreg[jj][t][i] = X[(int64_t)(16 * t + 4 * g + i) * (2 * D) + 16 * jt + r];
+        }
+        if (s + 2 < nseg) fetch_m(s + 1);
+        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < C::TPW; ++jj) {
+            const int jt = wave + C::NW * jj;
+            if (jt >= C::NT) continue;
+            BFrag sb[C::KT];
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) sb[t] = MM::to_b(S[jj][t]);
+#pragma unroll
+            for (int rt = 0; rt < C::KT; ++rt) {
+                const f32x4 acc = MM::template mm_la<D>(m_lds + 16 * rt * C::LDM, C::LDM, sb,
+                                                        f32x4{0, 0, 0, 0}, r, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[jj][rt][i] = acc[i] + nreg[jj][rt][i];
             }
         }
         store(s + 1);
+        __syncthreads();
     }
 }
 
@@ -390,14 +508,14 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
     if (p.nseg > 1) {
         ws_mn = reinterpret_cast<float*>(workspace);
         ws_start = ws_mn + (size_t)(p.nseg - 1) * BH * D * (2 * D);
-        hipLaunchKernelGGL((chunk_kernel<E, D, true>), dim3((unsigned)(BH * (p.nseg - 1))), dim3(256), 0,
+        hipLaunchKernelGGL((chunk_kernel<E, D, true>), dim3((unsigned)(BH * (p.nseg - 1))), dim3(512), 0,
                            stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k,
                            (const E*)v, theta, beta, (const float*)nullptr, (const float*)nullptr, ws_mn,
                            (E*)nullptr, (float*)nullptr);
-        hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)BH), dim3(256), 0, stream, BH, p.nseg,
+        hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)BH), dim3(512), 0, stream, BH, p.nseg,
                            S0, (const float*)ws_mn, ws_start);
     }
-    hipLaunchKernelGGL((chunk_kernel<E, D, false>), dim3((unsigned)(BH * p.nseg)), dim3(256), 0, stream, T,
+    hipLaunchKernelGGL((chunk_kernel<E, D, false>), dim3((unsigned)(BH * p.nseg)), dim3(512), 0, stream, T,
                        H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
                        beta, S0, (const float*)ws_start, (float*)nullptr, (E*)o, S_T);
     return hipGetLastError();

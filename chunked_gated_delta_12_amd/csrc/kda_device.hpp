@@ -64,11 +64,18 @@ __device__ __forceinline__ void store_pair(E* p, float a, float b) {
 }
 
 // ---------------------------------------------------------------- MFMA wrappers
+// K = 16 bf16 products run on the 16x16x32 instruction with the upper four
+// k-slots of each lane group zeroed on both operands.  The legacy 16x16x16
+// bf16 instruction is not used: results read right after it (at the wait
+// states the compiler inserts for it) came back stale on gfx950.
 __device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                   c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mfma_k4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
