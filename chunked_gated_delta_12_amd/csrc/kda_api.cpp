@@ -121,6 +121,8 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, 
     if (st) return st;
     if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
     if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*d too large");
+    if ((int64_t)H * dk * KDA_CHUNK >= (1LL << 31))
+        return fail(KDA_ERR_SHAPE, "H*d=%lld too large (16*H*d must stay below 2^31)", (long long)H * dk);
     const int nchunks = (T + KDA_CHUNK - 1) / KDA_CHUNK;
     if (segments < 0 || segments > nchunks)
         return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);

@@ -7,6 +7,8 @@
 //     A  = StrictLower(diag(beta) K+ K-^T),   T = (I + A)^-1
 //     W  = T diag(beta) K+,   Ut = T diag(beta) V,   U = Ut - W S
 //     O  = Q+ S + LowerIncl(Q+ K-^T) U,   S' = Diag(Gamma_C) S + Kend^T U.
+// The kernels evaluate U as T (beta*V - beta*K+ S): the products with the
+// state then do not wait for T, and W is never formed.
 // Only K- carries an inverse decay, and the bounded gate keeps it below
 // exp(16*5) = 5.5e34 ("Architecture Deep Dive: Kimi K3...", section 3.2), so
 // the diagonal tiles A and LowerIncl(Q+ K-^T) are plain dense bf16 matrix-core
@@ -38,9 +40,9 @@
 
 namespace kda {
 
-template <int D, bool MAP>
+template <int D, bool MAP, int NW_>
 struct ChunkCfg {
-    static constexpr int NW = 8;                   // wavefronts per workgroup (2 per SIMD)
+    static constexpr int NW = NW_;                 // wavefronts per workgroup
     static constexpr int NTHR = 64 * NW;
     static constexpr int NCOL = MAP ? 2 * D : D;   // state columns carried
     static constexpr int NT = NCOL / 16;           // 16-column tiles
@@ -48,29 +50,31 @@ struct ChunkCfg {
     static constexpr int KT = D / 16;              // 16-row tiles along d_k
     static constexpr int LDR = D + 8;              // padded row of [16][D] tiles
     static constexpr int LDC = 20;                 // padded row of [D][16] tiles
-    static constexpr int PPT = D >= 128 ? D / 64 : 1;  // tokens per thread, gate stage
-    static constexpr int NPG = CHUNK / PPT;           // token groups, gate stage
-    static constexpr int NACT = (D / 2) * NPG;        // active threads, gate stage
+    // Gate stage: a thread owns one channel pair and PPT consecutive tokens; the
+    // NPG token groups of a pair sit in the same wavefront (PW pairs per
+    // wavefront), so the prefix over the chunk runs on cross-lane shuffles.
+    static constexpr int PPT = D / (8 * NW) > 1 ? D / (8 * NW) : 1;  // tokens per thread
+    static constexpr int NPG = CHUNK / PPT;           // token groups per pair
+    static constexpr int PW = 64 / NPG;               // channel pairs per wavefront
+    static constexpr int NACT = (D / 2) * NPG;        // active threads
     static_assert(NACT <= NTHR, "gate stage mapping");
-    static_assert(PPT <= 2, "gate stage packs at most two tokens per column write");
+    static_assert(NPG <= 64 && 64 % NPG == 0, "gate stage mapping");
+    static_assert(PPT == 1 || PPT == 2 || PPT == 4, "gate stage column writes");
 };
 
-template <typename E, int D, bool MAP>
+template <typename E, int D, bool MAP, int NW>
 struct ChunkSmem {
-    typedef ChunkCfg<D, MAP> C;
-    alignas(16) E kp_row[16 * C::LDR];             // beta*K+          [token][ch]
+    typedef ChunkCfg<D, MAP, NW> C;
+    alignas(16) E kn_row[16 * C::LDR];             // -beta*K+         [token][ch]
     alignas(16) E km_row[16 * C::LDR];             // K-               [token][ch]
     alignas(16) E qp_row[MAP ? 8 : 16 * C::LDR];   // Q+               [token][ch]
-    alignas(16) E wn_row[16 * C::LDR];             // -W               [token][ch]
     alignas(16) E o_tile[MAP ? 8 : 16 * C::LDR];   // o of the chunk   [token][col]
-    alignas(16) E kp_col[D * C::LDC];              // (beta*K+)^T      [ch][token]
     alignas(16) E ke_col[D * C::LDC];              // Kend^T           [ch][token]
     alignas(16) E vb_col[D * C::LDC];              // (beta*V)^T       [col][token]
-    alignas(16) E t_row[16 * C::LDC];              // T                [token][token]
+    alignas(16) E t_row[16 * C::LDC];              // T = (I + A)^-1   [token][token]
     alignas(16) E aqk_row[MAP ? 8 : 16 * C::LDC];  // LowerIncl(Q+K-^T)[token][token]
     alignas(16) float akk_t[16 * 20];              // StrictLower(beta K+ K-^T)^T, fp32
     alignas(16) float gc[D];                       // Gamma_C per channel
-    alignas(16) float part[C::NPG * D];            // per-group partial sums of g
 };
 
 // Store units of the o tile: SU bytes per thread and store (4, 8 or 16).
@@ -79,17 +83,27 @@ template <> struct StoreUnit<4> { typedef uint32_t T; };
 template <> struct StoreUnit<8> { typedef uint64_t T; };
 template <> struct StoreUnit<16> { typedef f32x4 T; };
 
-template <typename E, int D, bool MAP>
-__global__ void __launch_bounds__(512)
+// PPT consecutive tokens of one column of a [col][token] tile, as one store.
+template <typename E, int N>
+__device__ __forceinline__ void store_run(E* p, const float* x) {
+    typedef E V __attribute__((__vector_size__(N * sizeof(E))));
+    V v;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = from_f<E>(x[i]);
+    *reinterpret_cast<V*>(p) = v;
+}
+
+template <typename E, int D, bool MAP, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
              const float* __restrict__ theta, const float* __restrict__ beta,
              const float* S0, const float* __restrict__ ws_start, float* __restrict__ ws_mn,
              E* __restrict__ o, float* S_T) {
-    typedef ChunkCfg<D, MAP> C;
+    typedef ChunkCfg<D, MAP, NW> C;
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
-    __shared__ ChunkSmem<E, D, MAP> sm;
+    __shared__ ChunkSmem<E, D, MAP, NW> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -100,9 +114,10 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     const int c1 = min(nchunks, c0 + seg_len);
 
     // gate-stage mapping: channel pair cp, token group pgi (tokens pgi*PPT ..)
-    const int cp = tid % (D / 2), pgi = tid / (D / 2);
+    const int cp = wave * C::PW + lane % C::PW, pgi = lane / C::PW;
     const int ch = 2 * cp;
-    const bool gact = tid < C::NACT;
+    constexpr bool ALL_ACT = C::NACT == C::NTHR;
+    const bool gact = ALL_ACT || cp < D / 2;
     const int64_t tok_stride = (int64_t)H * D;
     const int64_t head_base = (int64_t)b * T * H * D + (int64_t)h * D;
 
@@ -131,24 +146,37 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     }
 
     // ---- prefetch registers for one chunk (this thread's gate-stage elements).
-    // Raw bits are loaded from a clamped, always valid token index so the loads
-    // carry no branch and stay in flight until the next chunk's gate stage;
-    // tokens past T (and idle threads) are masked when the values are used.
+    // The loads carry no branch and stay in flight until the next chunk's gate
+    // stage.  Addresses are a per-chunk uniform base plus a loop-invariant
+    // 32-bit lane offset; in the final, partial chunk tokens past T read the
+    // last token instead (and are masked when used).  Idle lanes read a valid
+    // element and ignore it.
     typedef typename Pair<E>::T RawPair;
     f32x2 th_r[C::PPT];
     RawPair k_r[C::PPT], q_r[C::PPT], v_r[C::PPT];
     float b_r[C::PPT];
+    const uint32_t lane_tok = (uint32_t)(pgi * C::PPT);          // first token of this lane in a chunk
+    const uint32_t lane_ch = gact ? (uint32_t)ch : 0u;
     auto load_chunk = [&](int n) {
         const int t0 = n * CHUNK;
+        const int64_t base = head_base + (int64_t)t0 * tok_stride;   // uniform
+        const int64_t bbase = ((int64_t)b * T + t0) * H + h;         // uniform
+        const float* thb = theta + base;
+        const E* kb = k + base;
+        const E* qb = q + base;
+        const E* vb = v + base;
+        const float* bb = beta + bbase;
+        const int nvalid = T - t0;                                   // uniform
 #pragma unroll
         for (int p = 0; p < C::PPT; ++p) {
-            const int t = min(t0 + pgi * C::PPT + p, T - 1);
-            const int64_t off = head_base + (int64_t)t * tok_stride + (gact ? ch : 0);
-            th_r[p] = *reinterpret_cast<const f32x2*>(theta + off);
-            k_r[p] = *reinterpret_cast<const RawPair*>(k + off);
-            if constexpr (!MAP) q_r[p] = *reinterpret_cast<const RawPair*>(q + off);
-            v_r[p] = *reinterpret_cast<const RawPair*>(v + off);
-            b_r[p] = beta[((int64_t)b * T + t) * H + h];
+            uint32_t tl = lane_tok + p;
+            if (nvalid < CHUNK) tl = min(tl, (uint32_t)(nvalid - 1));
+            const uint32_t off = tl * (uint32_t)tok_stride + lane_ch;
+            th_r[p] = *reinterpret_cast<const f32x2*>(thb + off);
+            k_r[p] = *reinterpret_cast<const RawPair*>(kb + off);
+            if constexpr (!MAP) q_r[p] = *reinterpret_cast<const RawPair*>(qb + off);
+            v_r[p] = *reinterpret_cast<const RawPair*>(vb + off);
+            b_r[p] = bb[tl * (uint32_t)H];
         }
     };
 
@@ -179,89 +207,99 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     for (int n = c0; n < c1; ++n) {
         const int t0 = n * CHUNK;
         // ---------------- stage 1: gate, cumulative decay, scaled operand tiles
+        // Everything is computed unconditionally; only the final, partial chunk
+        // masks its padding tokens (g = 0, beta = k = q = v = 0), which leaves
+        // the state unchanged.
+        const bool partial = t0 + CHUNK > T;   // uniform
+        float kx[C::PPT][2], qx[C::PPT][2], vx[C::PPT][2], bx[C::PPT];
         float G0[C::PPT], G1[C::PPT];
-        {
-            float run0 = 0.0f, run1 = 0.0f;
+        float run0 = 0.0f, run1 = 0.0f;
 #pragma unroll
-            for (int p = 0; p < C::PPT; ++p) {
+        for (int p = 0; p < C::PPT; ++p) {
+            float ga = gate_logdecay(th_r[p][0]), gb = gate_logdecay(th_r[p][1]);
+            kx[p][0] = to_f(k_r[p][0]);
+            kx[p][1] = to_f(k_r[p][1]);
+            if constexpr (!MAP) {
+                qx[p][0] = to_f(q_r[p][0]);
+                qx[p][1] = to_f(q_r[p][1]);
+            }
+            vx[p][0] = to_f(v_r[p][0]);
+            vx[p][1] = to_f(v_r[p][1]);
+            bx[p] = b_r[p];
+            if (!ALL_ACT || partial) {
                 const bool ok = gact && (t0 + pgi * C::PPT + p < T);
-                run0 += ok ? gate_logdecay(th_r[p][0]) : 0.0f;   // padding tokens: g = 0
-                run1 += ok ? gate_logdecay(th_r[p][1]) : 0.0f;
-                G0[p] = run0;
-                G1[p] = run1;
+                ga = ok ? ga : 0.0f;
+                gb = ok ? gb : 0.0f;
+                kx[p][0] = ok ? kx[p][0] : 0.0f;
+                kx[p][1] = ok ? kx[p][1] : 0.0f;
+                if constexpr (!MAP) {
+                    qx[p][0] = ok ? qx[p][0] : 0.0f;
+                    qx[p][1] = ok ? qx[p][1] : 0.0f;
+                }
+                vx[p][0] = ok ? vx[p][0] : 0.0f;
+                vx[p][1] = ok ? vx[p][1] : 0.0f;
+                bx[p] = ok ? bx[p] : 0.0f;
             }
-            if (gact) {
-                sm.part[pgi * D + ch] = run0;
-                sm.part[pgi * D + ch + 1] = run1;
-            }
+            run0 += ga;
+            run1 += gb;
+            G0[p] = run0;
+            G1[p] = run1;
         }
-        __syncthreads();
-        if (gact) {
-            float off0 = 0.0f, off1 = 0.0f, tot0 = 0.0f, tot1 = 0.0f;
+        // inclusive scan of the group totals across the NPG lanes of this pair
+        float inc0 = run0, inc1 = run1;
 #pragma unroll
-            for (int gi = 0; gi < C::NPG; ++gi) {
-                const float x0 = sm.part[gi * D + ch], x1 = sm.part[gi * D + ch + 1];
-                if (gi < pgi) { off0 += x0; off1 += x1; }
-                tot0 += x0;
-                tot1 += x1;
-            }
+        for (int d = 1; d < C::NPG; d <<= 1) {
+            const float u0 = __shfl_up(inc0, d * C::PW), u1 = __shfl_up(inc1, d * C::PW);
+            if (pgi >= d) { inc0 += u0; inc1 += u1; }
+        }
+        const float tot0 = __shfl(inc0, (C::NPG - 1) * C::PW + lane % C::PW);
+        const float tot1 = __shfl(inc1, (C::NPG - 1) * C::PW + lane % C::PW);
+        if (gact) {
+            const float off0 = inc0 - run0, off1 = inc1 - run1;
             const float eC0 = __expf(tot0), eC1 = __expf(tot1);
             if (pgi == 0) {
                 sm.gc[ch] = eC0;
                 sm.gc[ch + 1] = eC1;
             }
-            float kpa[C::PPT], kpb[C::PPT], kea[C::PPT], keb[C::PPT], vba[C::PPT], vbb[C::PPT];
+            float kea[C::PPT], keb[C::PPT], vba[C::PPT], vbb[C::PPT];
 #pragma unroll
             for (int p = 0; p < C::PPT; ++p) {
                 const int pos = pgi * C::PPT + p;
-                const bool ok = t0 + pos < T;            // padding tokens: k = q = v = beta = 0
                 const float Ga = G0[p] + off0, Gb = G1[p] + off1;
                 const float eGa = __expf(Ga), eGb = __expf(Gb);
                 const float emGa = __expf(-Ga), emGb = __expf(-Gb);
-                const float ka = ok ? to_f(k_r[p][0]) : 0.0f, kb = ok ? to_f(k_r[p][1]) : 0.0f;
-                const float bt = ok ? b_r[p] : 0.0f;
-                kpa[p] = bt * ka * eGa;
-                kpb[p] = bt * kb * eGb;
+                const float ka = kx[p][0], kb = kx[p][1], bt = bx[p];
                 kea[p] = ka * (eC0 * emGa);        // k * exp(G_C - G), every factor <= 1 in range
                 keb[p] = kb * (eC1 * emGb);
-                vba[p] = ok ? bt * to_f(v_r[p][0]) : 0.0f;
-                vbb[p] = ok ? bt * to_f(v_r[p][1]) : 0.0f;
-                store_pair(&sm.kp_row[pos * C::LDR + ch], kpa[p], kpb[p]);
+                vba[p] = bt * vx[p][0];
+                vbb[p] = bt * vx[p][1];
+                store_pair(&sm.kn_row[pos * C::LDR + ch], -bt * ka * eGa, -bt * kb * eGb);
                 store_pair(&sm.km_row[pos * C::LDR + ch], ka * emGa, kb * emGb);
                 if constexpr (!MAP)
-                    store_pair(&sm.qp_row[pos * C::LDR + ch], ok ? to_f(q_r[p][0]) * eGa : 0.0f,
-                               ok ? to_f(q_r[p][1]) * eGb : 0.0f);
+                    store_pair(&sm.qp_row[pos * C::LDR + ch], qx[p][0] * eGa, qx[p][1] * eGb);
             }
             const int pos0 = pgi * C::PPT;
-            if constexpr (C::PPT == 2) {
-                store_pair(&sm.kp_col[ch * C::LDC + pos0], kpa[0], kpa[1]);
-                store_pair(&sm.kp_col[(ch + 1) * C::LDC + pos0], kpb[0], kpb[1]);
-                store_pair(&sm.ke_col[ch * C::LDC + pos0], kea[0], kea[1]);
-                store_pair(&sm.ke_col[(ch + 1) * C::LDC + pos0], keb[0], keb[1]);
-                store_pair(&sm.vb_col[ch * C::LDC + pos0], vba[0], vba[1]);
-                store_pair(&sm.vb_col[(ch + 1) * C::LDC + pos0], vbb[0], vbb[1]);
-            } else {
-                sm.kp_col[ch * C::LDC + pos0] = from_f<E>(kpa[0]);
-                sm.kp_col[(ch + 1) * C::LDC + pos0] = from_f<E>(kpb[0]);
-                sm.ke_col[ch * C::LDC + pos0] = from_f<E>(kea[0]);
-                sm.ke_col[(ch + 1) * C::LDC + pos0] = from_f<E>(keb[0]);
-                sm.vb_col[ch * C::LDC + pos0] = from_f<E>(vba[0]);
-                sm.vb_col[(ch + 1) * C::LDC + pos0] = from_f<E>(vbb[0]);
-            }
+            store_run<E, C::PPT>(&sm.ke_col[ch * C::LDC + pos0], kea);
+            store_run<E, C::PPT>(&sm.ke_col[(ch + 1) * C::LDC + pos0], keb);
+            store_run<E, C::PPT>(&sm.vb_col[ch * C::LDC + pos0], vba);
+            store_run<E, C::PPT>(&sm.vb_col[(ch + 1) * C::LDC + pos0], vbb);
         }
         if constexpr (!MAP)
             if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
         if (n + 1 < c1) load_chunk(n + 1);        // in flight until the next chunk's gate stage
         __syncthreads();
 
-        // ---------------- stage 2: diagonal tiles as dense products
+        // ---------------- stage 2: diagonal tiles, then the state-side products
+        // for every column tile, overlapped with the triangular solve:
+        //   Y  = beta*V - beta*K+ S      (so that U = T Y = Ut - W S)
+        //   O1 = Q+ S
         if (wave == 0) {
-            const f32x4 a = MM::template mm_ll<D>(sm.kp_row, C::LDR, sm.km_row, C::LDR,
+            // A = StrictLower(beta K+ K-^T), kept transposed in LDS: akk_t[col][row]
+            const f32x4 a = MM::template mm_ll<D>(sm.kn_row, C::LDR, sm.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
-            // a[i] = A[row 4g+i][col r]; stored transposed: akk_t[col][row]
             f32x4 m;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? a[i] : 0.0f;   // mask by select
+            for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? -a[i] : 0.0f;   // mask by select
             *reinterpret_cast<f32x4*>(&sm.akk_t[r * 20 + 4 * g]) = m;
         } else if (!MAP && wave == 1) {
             const f32x4 a = MM::template mm_ll<D>(sm.qp_row, C::LDR, sm.km_row, C::LDR,
@@ -272,30 +310,40 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 sm.aqk_row[row * C::LDC + r] = from_f<E>((r <= row) ? a[i] : 0.0f);
             }
         }
-        __syncthreads();
-
-        // ---------------- stage 3: T = (I + A)^-1, column j per lane, right-looking
-        // substitution: once x[s] is final, every later row subtracts A[r][s] x[s].
+        f32x4 y[C::TPW], o1[C::TPW];
+#pragma unroll
+        for (int jj = 0; jj < C::TPW; ++jj) {
+            const int jt = wave + C::NW * jj;
+            if (jt >= C::NT) continue;
+            BFrag sb[C::KT];
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) sb[t] = MM::to_b(S[jj][t]);
+            f32x4 yc = f32x4{0, 0, 0, 0};
+            if (jt < D / 16) {   // value columns; the M part of a widened state has V = 0
+                const int cb = (16 * jt + r) * C::LDC + 4 * g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) yc[i] = to_f(sm.vb_col[cb + i]);
+            }
+            y[jj] = MM::template mm_la<D>(sm.kn_row, C::LDR, sb, yc, r, g);
+            if constexpr (!MAP) o1[jj] = MM::template mm_la<D>(sm.qp_row, C::LDR, sb, f32x4{0, 0, 0, 0}, r, g);
+        }
         if (wave == 0) {
+            // T = (I + A)^-1, column j per lane, right-looking substitution: once
+            // x[s] is final, every later row subtracts A[r][s] x[s].  (The LDS
+            // round trip stays inside this wavefront, which executes in order.)
             const int j = lane & 15;
             float x[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.0f : 0.0f;
-            f32x4 col[4], nxt[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) col[c] = *reinterpret_cast<const f32x4*>(&sm.akk_t[4 * c]);
 #pragma unroll
             for (int s = 0; s < 15; ++s) {
-                if (s + 1 < 15) {
+                f32x4 col[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        nxt[c] = *reinterpret_cast<const f32x4*>(&sm.akk_t[(s + 1) * 20 + 4 * c]);
-                }
+                for (int c = s / 4; c < 4; ++c)
+                    col[c] = *reinterpret_cast<const f32x4*>(&sm.akk_t[s * 20 + 4 * c]);
                 const float xs = x[s];
 #pragma unroll
                 for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) col[c] = nxt[c];
             }
             if (lane < 16) {
 #pragma unroll
@@ -304,38 +352,16 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         }
         __syncthreads();
 
-        // ---------------- stage 4: W (shared) and Ut (per column tile)
-        for (int tile = wave; tile < C::KT; tile += C::NW) {
-            const f32x4 w = MM::template mm_ll<16>(sm.kp_col + tile * 16 * C::LDC, C::LDC, sm.t_row,
-                                                   C::LDC, f32x4{0, 0, 0, 0}, r, g);
-            // w[i] = W[token r][ch 16*tile + 4g + i]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.wn_row[r * C::LDR + 16 * tile + 4 * g + i] = from_f<E>(-w[i]);
-        }
-        f32x4 ut[C::TPW];
-#pragma unroll
-        for (int jj = 0; jj < C::TPW; ++jj) {
-            const int jt = wave + C::NW * jj;
-            ut[jj] = f32x4{0, 0, 0, 0};
-            if (jt < D / 16)   // value columns; the M part of a widened state has Ut = 0
-                ut[jj] = MM::template mm_ll<16>(sm.t_row, C::LDC, sm.vb_col + jt * 16 * C::LDC, C::LDC,
-                                                ut[jj], r, g);
-        }
-        __syncthreads();
-
-        // ---------------- stage 5: inter-chunk step for this wavefront's column tiles
+        // ---------------- stage 3: U = T Y, output, state update per column tile
 #pragma unroll
         for (int jj = 0; jj < C::TPW; ++jj) {
             const int jt = wave + C::NW * jj;
             if (jt >= C::NT) continue;
-            BFrag sb[C::KT];
-#pragma unroll
-            for (int t = 0; t < C::KT; ++t) sb[t] = MM::to_b(S[jj][t]);
-            const f32x4 u = MM::template mm_la<D>(sm.wn_row, C::LDR, sb, ut[jj], r, g);  // Ut - W S
+            const BFrag yb = MM::to_b(y[jj]);
+            const f32x4 u = MM::template mm_la<16>(sm.t_row, C::LDC, &yb, f32x4{0, 0, 0, 0}, r, g);
             const BFrag ub = MM::to_b(u);
             if constexpr (!MAP) {
-                f32x4 oo = MM::template mm_la<D>(sm.qp_row, C::LDR, sb, f32x4{0, 0, 0, 0}, r, g);
-                oo = MM::template mm_la<16>(sm.aqk_row, C::LDC, &ub, oo, r, g);
+                const f32x4 oo = MM::template mm_la<16>(sm.aqk_row, C::LDC, &ub, o1[jj], r, g);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.o_tile[(4 * g + i) * C::LDR + 16 * jt + r] = from_f<E>(oo[i]);
             }
@@ -497,6 +523,11 @@ size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg) {
     return (mn + st) * sizeof(float);
 }
 
+// Wavefronts per workgroup: four, so that two workgroups share a compute unit
+// and one's gate/solve phases overlap the other's matrix-core phases.
+constexpr int CHUNK_NW_OUT = 4;
+constexpr int CHUNK_NW_MAP = 8;
+
 template <typename E, int D>
 static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const void* q,
                                  const void* k, const void* v, const float* theta,
@@ -508,14 +539,16 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
     if (p.nseg > 1) {
         ws_mn = reinterpret_cast<float*>(workspace);
         ws_start = ws_mn + (size_t)(p.nseg - 1) * BH * D * (2 * D);
-        hipLaunchKernelGGL((chunk_kernel<E, D, true>), dim3((unsigned)(BH * (p.nseg - 1))), dim3(512), 0,
+        hipLaunchKernelGGL((chunk_kernel<E, D, true, CHUNK_NW_MAP>), dim3((unsigned)(BH * (p.nseg - 1))),
+                           dim3(64 * CHUNK_NW_MAP), 0,
                            stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k,
                            (const E*)v, theta, beta, (const float*)nullptr, (const float*)nullptr, ws_mn,
                            (E*)nullptr, (float*)nullptr);
         hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)BH), dim3(512), 0, stream, BH, p.nseg,
                            S0, (const float*)ws_mn, ws_start);
     }
-    hipLaunchKernelGGL((chunk_kernel<E, D, false>), dim3((unsigned)(BH * p.nseg)), dim3(512), 0, stream, T,
+    hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT>), dim3((unsigned)(BH * p.nseg)),
+                       dim3(64 * CHUNK_NW_OUT), 0, stream, T,
                        H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
                        beta, S0, (const float*)ws_start, (float*)nullptr, (E*)o, S_T);
     return hipGetLastError();
