@@ -211,34 +211,16 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         // masks its padding tokens (g = 0, beta = k = q = v = 0), which leaves
         // the state unchanged.
         const bool partial = t0 + CHUNK > T;   // uniform
-        float kx[C::PPT][2], qx[C::PPT][2], vx[C::PPT][2], bx[C::PPT];
+        const bool mask = !ALL_ACT || partial;  // uniform
         float G0[C::PPT], G1[C::PPT];
         float run0 = 0.0f, run1 = 0.0f;
 #pragma unroll
         for (int p = 0; p < C::PPT; ++p) {
             float ga = gate_logdecay(th_r[p][0]), gb = gate_logdecay(th_r[p][1]);
-            kx[p][0] = to_f(k_r[p][0]);
-            kx[p][1] = to_f(k_r[p][1]);
-            if constexpr (!MAP) {
-                qx[p][0] = to_f(q_r[p][0]);
-                qx[p][1] = to_f(q_r[p][1]);
-            }
-            vx[p][0] = to_f(v_r[p][0]);
-            vx[p][1] = to_f(v_r[p][1]);
-            bx[p] = b_r[p];
-            if (!ALL_ACT || partial) {
+            if (mask) {
                 const bool ok = gact && (t0 + pgi * C::PPT + p < T);
                 ga = ok ? ga : 0.0f;
                 gb = ok ? gb : 0.0f;
-                kx[p][0] = ok ? kx[p][0] : 0.0f;
-                kx[p][1] = ok ? kx[p][1] : 0.0f;
-                if constexpr (!MAP) {
-                    qx[p][0] = ok ? qx[p][0] : 0.0f;
-                    qx[p][1] = ok ? qx[p][1] : 0.0f;
-                }
-                vx[p][0] = ok ? vx[p][0] : 0.0f;
-                vx[p][1] = ok ? vx[p][1] : 0.0f;
-                bx[p] = ok ? bx[p] : 0.0f;
             }
             run0 += ga;
             run1 += gb;
@@ -268,15 +250,23 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 const float Ga = G0[p] + off0, Gb = G1[p] + off1;
                 const float eGa = __expf(Ga), eGb = __expf(Gb);
                 const float emGa = __expf(-Ga), emGb = __expf(-Gb);
-                const float ka = kx[p][0], kb = kx[p][1], bt = bx[p];
+                float ka = to_f(k_r[p][0]), kb = to_f(k_r[p][1]), bt = b_r[p];
+                float va = to_f(v_r[p][0]), vb2 = to_f(v_r[p][1]);
+                float qa = 0.0f, qb = 0.0f;
+                if constexpr (!MAP) {
+                    qa = to_f(q_r[p][0]);
+                    qb = to_f(q_r[p][1]);
+                }
+                if (mask && !(t0 + pos < T)) {   // padding token: k = q = v = beta = 0
+                    ka = kb = bt = va = vb2 = qa = qb = 0.0f;
+                }
                 kea[p] = ka * (eC0 * emGa);        // k * exp(G_C - G), every factor <= 1 in range
                 keb[p] = kb * (eC1 * emGb);
-                vba[p] = bt * vx[p][0];
-                vbb[p] = bt * vx[p][1];
+                vba[p] = bt * va;
+                vbb[p] = bt * vb2;
                 store_pair(&sm.kn_row[pos * C::LDR + ch], -bt * ka * eGa, -bt * kb * eGb);
                 store_pair(&sm.km_row[pos * C::LDR + ch], ka * emGa, kb * emGb);
-                if constexpr (!MAP)
-                    store_pair(&sm.qp_row[pos * C::LDR + ch], qx[p][0] * eGa, qx[p][1] * eGb);
+                if constexpr (!MAP) store_pair(&sm.qp_row[pos * C::LDR + ch], qa * eGa, qb * eGb);
             }
             const int pos0 = pgi * C::PPT;
             store_run<E, C::PPT>(&sm.ke_col[ch * C::LDC + pos0], kea);
@@ -327,6 +317,10 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             y[jj] = MM::template mm_la<D>(sm.kn_row, C::LDR, sb, yc, r, g);
             if constexpr (!MAP) o1[jj] = MM::template mm_la<D>(sm.qp_row, C::LDR, sb, f32x4{0, 0, 0, 0}, r, g);
         }
+        // The products above are issued before the solve starts (matrix cores
+        // run them while the solve proceeds); keeping the two apart in the
+        // instruction stream also keeps their registers from being live at once.
+        __builtin_amdgcn_sched_barrier(0);
         if (wave == 0) {
             // T = (I + A)^-1, column j per lane, right-looking substitution: once
             // x[s] is final, every later row subtracts A[r][s] x[s].  (The LDS
