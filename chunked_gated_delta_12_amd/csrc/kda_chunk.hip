@@ -393,108 +393,110 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
 // Start state of every segment: S_0 = S0 (or 0), S_{s+1} = M_s S_s + N_s, where
 // [N_s | M_s] is the widened end state the map kernel stored for segment s.
-// One workgroup of 8 wavefronts per head, one 16-column tile of the state per
-// wavefront.  M_s is staged through LDS (rounded to the operand type) while
-// M_{s+1} is already being fetched into registers; N_s is fetched at the start
-// of the step and added after the products, so no global load sits on the
-// per-step critical path.
+// Columns of the state are independent, so one workgroup owns one 16-column
+// tile of one head; its 4 wavefronts split the 16-row tiles of the product.
+// The column tile is shared through LDS (transposed, rounded to the operand
+// type) at every step; the rows of M_s and the N_s tile each wavefront needs
+// are fetched two steps ahead into a three-slot register ring.
 template <typename E, int D>
 struct CombineCfg {
-    static constexpr int NW = 8, NTHR = 64 * NW;
-    static constexpr int NT = D / 16, TPW = (NT + NW - 1) / NW, KT = D / 16;
-    static constexpr int LDM = D + 8;
-    static constexpr int MV = D * D / 4 / NTHR > 0 ? D * D / 4 / NTHR : 1;   // float4 of M per thread
+    static constexpr int NW = 4, NTHR = 64 * NW;
+    static constexpr int KT = D / 16, NT = D / 16;
+    static constexpr int RPW = (KT + NW - 1) / NW;   // row tiles per wavefront
+    static constexpr int LDT = D + 8;                // padded row of the transposed tile
 };
 
 template <typename E, int D>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(256)
 combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_mn,
                float* __restrict__ ws_start) {
     typedef CombineCfg<E, D> C;
-    typedef Ops<E> MM;
-    typedef typename MM::BFrag BFrag;
-    __shared__ alignas(16) E m_lds[D * C::LDM];
+    __shared__ alignas(16) E st[16 * C::LDT];   // st[col][row]: the state column tile
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / C::NT, jt = blockIdx.x % C::NT;
 
-    f32x4 S[C::TPW][C::KT];
+    struct Pref {
+        f32x4 m[C::RPW][C::KT];   // M rows 16rt + r, columns 16t + 4g .. +3
+        f32x4 n[C::RPW];          // N rows 16rt + 4g + i, column 16jt + r
+    };
+    auto fetch = [&](int s, Pref& pf) {
+        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);   // [D][2D] = [N | M]
 #pragma unroll
-    for (int jj = 0; jj < C::TPW; ++jj) {
-        const int jt = wave + C::NW * jj;
+        for (int k = 0; k < C::RPW; ++k) {
+            const int rt = min(wave + C::NW * k, C::KT - 1);
 #pragma unroll
-        for (int t = 0; t < C::KT; ++t)
+            for (int t = 0; t < C::KT; ++t)
+                pf.m[k][t] = *reinterpret_cast<const f32x4*>(X + (int64_t)(16 * rt + r) * (2 * D) + D + 16 * t + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * t + 4 * g + i;
-                S[jj][t][i] = (S0 && jt < C::NT) ? S0[((int64_t)bh * D + row) * D + 16 * jt + r] : 0.0f;
-            }
-    }
-    auto store = [&](int s) {
+            for (int i = 0; i < 4; ++i) pf.n[k][i] = X[(int64_t)(16 * rt + 4 * g + i) * (2 * D) + 16 * jt + r];
+        }
+    };
+    auto publish = [&](int s, const f32x4* acc) {   // acc[k]: rows 16rt + 4g + i, column 16jt + r
         float* dst = ws_start + ((int64_t)s * BH + bh) * D * D;
 #pragma unroll
-        for (int jj = 0; jj < C::TPW; ++jj) {
-            const int jt = wave + C::NW * jj;
-            if (jt >= C::NT) continue;
+        for (int k = 0; k < C::RPW; ++k) {
+            const int rt = wave + C::NW * k;
+            if (rt >= C::KT) continue;
 #pragma unroll
-            for (int t = 0; t < C::KT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * t + 4 * g + i) * D + 16 * jt + r] = S[jj][t][i];
-        }
-    };
-    // M_s: row-major [D][D] inside the [D][2D] block, read as float4s spread over the workgroup
-    f32x4 mreg[C::MV];
-    auto fetch_m = [&](int s) {
-        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);
-#pragma unroll
-        for (int j = 0; j < C::MV; ++j) {
-            const int f = min(tid + C::NTHR * j, D * D / 4 - 1);
-            const int row = f / (D / 4), c4 = f % (D / 4);
-            mreg[j] = *reinterpret_cast<const f32x4*>(X + (int64_t)row * (2 * D) + D + 4 * c4);
-        }
-    };
-    store(0);
-    if (nseg > 1) fetch_m(0);
-    for (int s = 0; s + 1 < nseg; ++s) {
-        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);
-#pragma unroll
-        for (int j = 0; j < C::MV; ++j) {
-            const int f = tid + C::NTHR * j;
-            if (f < D * D / 4) {
-                const int row = f / (D / 4), c4 = f % (D / 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) m_lds[row * C::LDM + 4 * c4 + e] = from_f<E>(mreg[j][e]);
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rt + 4 * g + i;
+                dst[(int64_t)row * D + 16 * jt + r] = acc[k][i];
+                st[r * C::LDT + row] = from_f<E>(acc[k][i]);
             }
         }
-        f32x4 nreg[C::TPW][C::KT];
+    };
+
+    f32x4 acc[C::RPW];
 #pragma unroll
-        for (int jj = 0; jj < C::TPW; ++jj) {
-            const int jt = min(wave + C::NW * jj, C::NT - 1);
+    for (int k = 0; k < C::RPW; ++k) {
+        const int rt = min(wave + C::NW * k, C::KT - 1);
 #pragma unroll
-            for (int t = 0; t < C::KT; ++t)
+        for (int i = 0; i < 4; ++i)
+            acc[k][i] = S0 ? S0[((int64_t)bh * D + 16 * rt + 4 * g + i) * D + 16 * jt + r] : 0.0f;
+    }
+    publish(0, acc);
+    const int nsteps = nseg - 1;
+    Pref ring0, ring1, ring2;
+    if (nsteps > 0) fetch(0, ring0);
+    if (nsteps > 1) fetch(1, ring1);
+    __syncthreads();
+
+    // one step: S <- M_s S + N_s, using the prefetched slot `cur`, refilling `nxt2`
+    auto step = [&](int s, const Pref& cur, Pref& nxt2) {
+        if (s + 2 < nsteps) fetch(s + 2, nxt2);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    nreg[jj][t][i] = X[(int64_t)(16 * t + 4 * g + i) * (2 * D) + 16 * jt + r];
-        }
-        if (s + 2 < nseg) fetch_m(s + 1);
-        __syncthreads();
+        for (int k = 0; k < C::RPW; ++k) {
+            f32x4 a = cur.n[k];
+            if constexpr (sizeof(E) == 2) {   // bf16 operands, k-map of the accumulator-as-B form
+                if constexpr (D == 16) {
+                    a = mfma_k16(Ops<bf16>::to_b(cur.m[k][0]), ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
+                } else {
 #pragma unroll
-        for (int jj = 0; jj < C::TPW; ++jj) {
-            const int jt = wave + C::NW * jj;
-            if (jt >= C::NT) continue;
-            BFrag sb[C::KT];
+                    for (int kb = 0; kb < D / 32; ++kb) {
+                        const bf16* bp = (const bf16*)&st[r * C::LDT + 32 * kb + 4 * g];
+                        a = mfma_k32(cat8(Ops<bf16>::to_b(cur.m[k][2 * kb]), Ops<bf16>::to_b(cur.m[k][2 * kb + 1])),
+                                     cat8(ld_b4(bp), ld_b4(bp + 16)), a);
+                    }
+                }
+            } else {                          // fp32 operands: step (t, i) contracts row 16t + 4g + i
 #pragma unroll
-            for (int t = 0; t < C::KT; ++t) sb[t] = MM::to_b(S[jj][t]);
+                for (int t = 0; t < C::KT; ++t) {
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(&st[r * C::LDT + 16 * t + 4 * g]);
 #pragma unroll
-            for (int rt = 0; rt < C::KT; ++rt) {
-                const f32x4 acc = MM::template mm_la<D>(m_lds + 16 * rt * C::LDM, C::LDM, sb,
-                                                        f32x4{0, 0, 0, 0}, r, g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[jj][rt][i] = acc[i] + nreg[jj][rt][i];
+                    for (int i = 0; i < 4; ++i) a = mfma_k4(cur.m[k][t][i], b[i], a);
+                }
             }
+            acc[k] = a;
         }
-        store(s + 1);
+        __syncthreads();              // every wavefront has read the old column tile
+        publish(s + 1, acc);
         __syncthreads();
+    };
+    for (int s = 0; s < nsteps; s += 3) {
+        step(s, ring0, ring2);
+        if (s + 1 < nsteps) step(s + 1, ring1, ring0);
+        if (s + 2 < nsteps) step(s + 2, ring2, ring1);
     }
 }
 
@@ -538,7 +540,8 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
                            stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k,
                            (const E*)v, theta, beta, (const float*)nullptr, (const float*)nullptr, ws_mn,
                            (E*)nullptr, (float*)nullptr);
-        hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)BH), dim3(512), 0, stream, BH, p.nseg,
+        hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, stream,
+                           BH, p.nseg,
                            S0, (const float*)ws_mn, ws_start);
     }
     hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT>), dim3((unsigned)(BH * p.nseg)),
