@@ -63,6 +63,49 @@ def time_calls(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall / steps * 1e3
 
 
+CHUNK_SOURCES = ("kda_chunk.hip", "kda_device.hpp", "kda_launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def chunk_source_digest():
+    """sha256 over the sources of the chunked-prefill kernels: stored counter readings
+    are only reported while the kernels they were taken on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_gated_delta_12_amd", "csrc")
+    for name in CHUNK_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload, segments):
+    """HBM bytes per kda_chunk_fwd call measured with FETCH_SIZE / WRITE_SIZE (rocprofv3
+    --pmc, scaled by the counters of a copy of known size), or None when no reading exists
+    for these kernel sources, workload and segment count."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("segments") != segments or rec.get("source_sha256") != chunk_source_digest():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def copy_calibration(mib, dev):
+    """One elementwise copy (negation) of `mib` MiB of fp32: reads and writes exactly
+    mib MiB each, so its FETCH_SIZE / WRITE_SIZE readings convert counter units to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(x, T_sample, threads):
     """The oracle as it stands, on the first T_sample tokens of every head."""
     import oracle
@@ -88,6 +131,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run one elementwise copy of MIB MiB (for counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -142,7 +187,7 @@ def main():
                    "theta": f"N({w.theta_mu},{w.theta_sigma})", "segments": seg,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": stored_traffic(w.name, seg),
                      "kernel": "kda_chunk_fwd (map + combine + out kernels, one call)",
                      "algorithmic_bytes": nbytes},
         "mfma": {"achieved": achieved_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -171,6 +216,9 @@ def main():
                          "tokens_per_s": dw.B / (dms * 1e-3), "algorithmic_bytes": dby,
                          "steps_timed": args.decode_steps}
         del S, tok
+
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, dev)
 
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))

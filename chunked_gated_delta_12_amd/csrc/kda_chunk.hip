@@ -27,7 +27,8 @@
 //                  last segment).
 // With one segment only the out kernel runs, straight from S0.
 //
-// Workgroup = 8 wavefronts (two per SIMD).  Per chunk: the gate and all
+// Workgroups of 4 (out kernel, two workgroups per compute unit) or 8 (map
+// kernel, which carries the twice-as-wide state) wavefronts.  Per chunk: the gate and all
 // decay-scaled operand tiles are formed once in LDS; A, T, W are shared by the
 // workgroup; the state columns are split into 16-column tiles across the
 // wavefronts, each tile living in fp32 accumulator registers for the whole
