@@ -36,6 +36,8 @@
 // processed, and each chunk's o tile is written out during the next chunk.  All products
 // are 16x16 matrix-core tiles (bf16 operands, fp32 accumulation; fp32
 // operands in the validation dtype).
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -66,16 +68,18 @@ struct ChunkCfg {
 template <typename E, int D, bool MAP, int NW>
 struct ChunkSmem {
     typedef ChunkCfg<D, MAP, NW> C;
-    alignas(16) E kn_row[16 * C::LDR];             // -beta*K+         [token][ch]
-    alignas(16) E km_row[16 * C::LDR];             // K-               [token][ch]
-    alignas(16) E qp_row[MAP ? 8 : 16 * C::LDR];   // Q+               [token][ch]
-    alignas(16) E o_tile[MAP ? 8 : 16 * C::LDR];   // o of the chunk   [token][col]
-    alignas(16) E ke_col[D * C::LDC];              // Kend^T           [ch][token]
-    alignas(16) E vb_col[D * C::LDC];              // (beta*V)^T       [col][token]
-    alignas(16) E t_row[16 * C::LDC];              // T = (I + A)^-1   [token][token]
-    alignas(16) E aqk_row[MAP ? 8 : 16 * C::LDC];  // LowerIncl(Q+K-^T)[token][token]
+    static constexpr int LDP = Ops<E>::PAD_ROW;    // padded K = 16 operand rows
+    alignas(16) E kn_row[16 * C::LDR];             // -K+ = -K*Gamma           [token][ch]
+    alignas(16) E km_row[16 * C::LDR];             // K- = K/Gamma             [token][ch]
+    alignas(16) E qp_row[MAP ? 8 : 16 * C::LDR];   // Q+ = Q*Gamma             [token][ch]
+    alignas(16) E o_tile[MAP ? 8 : 16 * C::LDR];   // o of the chunk           [token][col]
+    alignas(16) E ke_pad[D * LDP];                 // Kend^T, padded           [ch][token]
+    alignas(16) E v_col[D * C::LDC];               // V^T                      [col][token]
+    alignas(16) E t_pad[16 * LDP];                 // T = (I + A)^-1, padded   [token][token]
+    alignas(16) E aqk_pad[MAP ? 8 : 16 * LDP];     // LowerIncl(Q+K-^T), padded [token][token]
     alignas(16) float akk_t[16 * 20];              // StrictLower(beta K+ K-^T)^T, fp32
     alignas(16) float gc[D];                       // Gamma_C per channel
+    alignas(16) float bt[CHUNK];                   // beta per token
 };
 
 // Store units of the o tile: SU bytes per thread and store (4, 8 or 16).
@@ -84,7 +88,7 @@ template <> struct StoreUnit<4> { typedef uint32_t T; };
 template <> struct StoreUnit<8> { typedef uint64_t T; };
 template <> struct StoreUnit<16> { typedef f32x4 T; };
 
-// PPT consecutive tokens of one column of a [col][token] tile, as one store.
+// N consecutive values as one store of the storage type.
 template <typename E, int N>
 __device__ __forceinline__ void store_run(E* p, const float* x) {
     typedef E V __attribute__((__vector_size__(N * sizeof(E))));
@@ -92,6 +96,31 @@ __device__ __forceinline__ void store_run(E* p, const float* x) {
 #pragma unroll
     for (int i = 0; i < N; ++i) v[i] = from_f<E>(x[i]);
     *reinterpret_cast<V*>(p) = v;
+}
+
+// Four values of an accumulator tile as one store of the storage type.
+template <typename E>
+__device__ __forceinline__ void store4(E* p, f32x4 x) {
+    typedef E V __attribute__((__vector_size__(4 * sizeof(E))));
+    V v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = from_f<E>(x[i]);
+    *reinterpret_cast<V*>(p) = v;
+}
+
+// Scatter PPT loaded pairs (channel c, c+1 of consecutive tokens) into two
+// token runs, one per channel, without a round trip through fp32.
+template <typename E, int N>
+__device__ __forceinline__ void store_pair_runs(E* pa, E* pb, const typename Pair<E>::T* x) {
+    typedef E V __attribute__((__vector_size__(N * sizeof(E))));
+    V a, b;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        a[i] = x[i][0];
+        b[i] = x[i][1];
+    }
+    *reinterpret_cast<V*>(pa) = a;
+    *reinterpret_cast<V*>(pb) = b;
 }
 
 template <typename E, int D, bool MAP, int NW>
@@ -102,9 +131,12 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const float* S0, const float* __restrict__ ws_start, float* __restrict__ ws_mn,
              E* __restrict__ o, float* S_T) {
     typedef ChunkCfg<D, MAP, NW> C;
+    typedef ChunkSmem<E, D, MAP, NW> SM;
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
-    __shared__ ChunkSmem<E, D, MAP, NW> sm;
+    typedef typename MM::PFrag PFrag;
+    constexpr int LDP = SM::LDP;
+    __shared__ SM sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
@@ -113,6 +145,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     const int b = bh / H, h = bh % H;
     const int c0 = seg * seg_len;
     const int c1 = min(nchunks, c0 + seg_len);
+    const int c_full = min(c1, T / CHUNK);         // chunks [c0, c_full) hold 16 tokens
 
     // gate-stage mapping: channel pair cp, token group pgi (tokens pgi*PPT ..)
     const int cp = wave * C::PW + lane % C::PW, pgi = lane / C::PW;
@@ -121,6 +154,14 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     const bool gact = ALL_ACT || cp < D / 2;
     const int64_t tok_stride = (int64_t)H * D;
     const int64_t head_base = (int64_t)b * T * H * D + (int64_t)h * D;
+
+    // The padded operand tiles carry zeros in the upper half of every group;
+    // only the lower halves are rewritten per chunk.
+    for (int i = tid; i < D * LDP; i += C::NTHR) sm.ke_pad[i] = from_f<E>(0.0f);
+    for (int i = tid; i < 16 * LDP; i += C::NTHR) {
+        sm.t_pad[i] = from_f<E>(0.0f);
+        if constexpr (!MAP) sm.aqk_pad[i] = from_f<E>(0.0f);
+    }
 
     // ---- state tiles: S[jj][t] = rows 16t.., columns 16*(wave + NW*jj)..
     f32x4 S[C::TPW][C::KT];
@@ -147,37 +188,49 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     }
 
     // ---- prefetch registers for one chunk (this thread's gate-stage elements).
-    // The loads carry no branch and stay in flight until the next chunk's gate
-    // stage.  Addresses are a per-chunk uniform base plus a loop-invariant
-    // 32-bit lane offset; in the final, partial chunk tokens past T read the
-    // last token instead (and are masked when used).  Idle lanes read a valid
-    // element and ignore it.
+    // Buffer loads: the chunk's base address and the per-token offsets are
+    // scalars, the lane offset is loop invariant; the loads stay in flight until
+    // the next chunk's gate stage.  In the final, partial chunk, tokens past T
+    // read the last valid token instead (and are masked when used).  Idle lanes
+    // read a valid element and ignore it.
     typedef typename Pair<E>::T RawPair;
     f32x2 th_r[C::PPT];
     RawPair k_r[C::PPT], q_r[C::PPT], v_r[C::PPT];
     float b_r[C::PPT];
     const uint32_t lane_tok = (uint32_t)(pgi * C::PPT);          // first token of this lane in a chunk
     const uint32_t lane_ch = gact ? (uint32_t)ch : 0u;
+    const uint32_t tstr = (uint32_t)tok_stride;                  // elements between tokens
+    const uint32_t lane_el = lane_tok * tstr + lane_ch;          // element offset in a chunk
     auto load_chunk = [&](int n) {
         const int t0 = n * CHUNK;
         const int64_t base = head_base + (int64_t)t0 * tok_stride;   // uniform
-        const int64_t bbase = ((int64_t)b * T + t0) * H + h;         // uniform
-        const float* thb = theta + base;
-        const E* kb = k + base;
-        const E* qb = q + base;
-        const E* vb = v + base;
-        const float* bb = beta + bbase;
-        const int nvalid = T - t0;                                   // uniform
+        const Rsrc rth = make_rsrc(theta + base);
+        const Rsrc rk = make_rsrc(k + base);
+        const Rsrc rq = make_rsrc(q + base);
+        const Rsrc rv = make_rsrc(v + base);
+        const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h);
+        if (t0 + CHUNK <= T) {
 #pragma unroll
-        for (int p = 0; p < C::PPT; ++p) {
-            uint32_t tl = lane_tok + p;
-            if (nvalid < CHUNK) tl = min(tl, (uint32_t)(nvalid - 1));
-            const uint32_t off = tl * (uint32_t)tok_stride + lane_ch;
-            th_r[p] = *reinterpret_cast<const f32x2*>(thb + off);
-            k_r[p] = *reinterpret_cast<const RawPair*>(kb + off);
-            if constexpr (!MAP) q_r[p] = *reinterpret_cast<const RawPair*>(qb + off);
-            v_r[p] = *reinterpret_cast<const RawPair*>(vb + off);
-            b_r[p] = bb[tl * (uint32_t)H];
+            for (int p = 0; p < C::PPT; ++p) {
+                const uint32_t so = (uint32_t)p * tstr;             // uniform
+                th_r[p] = buf_ld_f2(rth, lane_el * 4u, so * 4u);
+                k_r[p] = BufPair<E>::ld(rk, lane_el * (uint32_t)sizeof(E), so * (uint32_t)sizeof(E));
+                if constexpr (!MAP) q_r[p] = BufPair<E>::ld(rq, lane_el * (uint32_t)sizeof(E), so * (uint32_t)sizeof(E));
+                v_r[p] = BufPair<E>::ld(rv, lane_el * (uint32_t)sizeof(E), so * (uint32_t)sizeof(E));
+                b_r[p] = __builtin_bit_cast(float, buf_ld32(rb, lane_tok * (uint32_t)H * 4u, (uint32_t)(p * H) * 4u));
+            }
+        } else {
+            const uint32_t last = (uint32_t)(T - t0 - 1);
+#pragma unroll
+            for (int p = 0; p < C::PPT; ++p) {
+                const uint32_t tl = min(lane_tok + (uint32_t)p, last);
+                const uint32_t el = tl * tstr + lane_ch;
+                th_r[p] = buf_ld_f2(rth, el * 4u, 0u);
+                k_r[p] = BufPair<E>::ld(rk, el * (uint32_t)sizeof(E), 0u);
+                if constexpr (!MAP) q_r[p] = BufPair<E>::ld(rq, el * (uint32_t)sizeof(E), 0u);
+                v_r[p] = BufPair<E>::ld(rv, el * (uint32_t)sizeof(E), 0u);
+                b_r[p] = __builtin_bit_cast(float, buf_ld32(rb, tl * (uint32_t)H * 4u, 0u));
+            }
         }
     };
 
@@ -204,22 +257,25 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         }
     };
 
-    load_chunk(c0);
-    for (int n = c0; n < c1; ++n) {
+    // Gate arithmetic in base 2: g2 = g*log2(e), G2 its in-chunk prefix sum,
+    // Gamma = 2^G2.
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr float GMIN2 = G_MIN * LOG2E;
+
+    // ---- one chunk.  PARTIAL: the final chunk with fewer than 16 tokens; its
+    // padding tokens get g = 0, beta = k = q = v = 0, which leave the state unchanged.
+    auto chunk = [&](auto partial_tag, int n) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
         const int t0 = n * CHUNK;
         // ---------------- stage 1: gate, cumulative decay, scaled operand tiles
-        // Everything is computed unconditionally; only the final, partial chunk
-        // masks its padding tokens (g = 0, beta = k = q = v = 0), which leaves
-        // the state unchanged.
-        const bool partial = t0 + CHUNK > T;   // uniform
-        const bool mask = !ALL_ACT || partial;  // uniform
         float G0[C::PPT], G1[C::PPT];
         float run0 = 0.0f, run1 = 0.0f;
 #pragma unroll
         for (int p = 0; p < C::PPT; ++p) {
-            float ga = gate_logdecay(th_r[p][0]), gb = gate_logdecay(th_r[p][1]);
-            if (mask) {
-                const bool ok = gact && (t0 + pgi * C::PPT + p < T);
+            float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th_r[p][0]));
+            float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th_r[p][1]));
+            if (PARTIAL || !ALL_ACT) {
+                const bool ok = gact && (!PARTIAL || t0 + pgi * C::PPT + p < T);
                 ga = ok ? ga : 0.0f;
                 gb = ok ? gb : 0.0f;
             }
@@ -239,41 +295,49 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         const float tot1 = __shfl(inc1, (C::NPG - 1) * C::PW + lane % C::PW);
         if (gact) {
             const float off0 = inc0 - run0, off1 = inc1 - run1;
-            const float eC0 = __expf(tot0), eC1 = __expf(tot1);
+            const float eC0 = __builtin_amdgcn_exp2f(tot0), eC1 = __builtin_amdgcn_exp2f(tot1);
             if (pgi == 0) {
                 sm.gc[ch] = eC0;
                 sm.gc[ch + 1] = eC1;
             }
-            float kea[C::PPT], keb[C::PPT], vba[C::PPT], vbb[C::PPT];
+            if (cp == 0) {
+#pragma unroll
+                for (int p = 0; p < C::PPT; ++p) {
+                    const bool ok = !PARTIAL || t0 + pgi * C::PPT + p < T;
+                    sm.bt[pgi * C::PPT + p] = ok ? b_r[p] : 0.0f;
+                }
+            }
+            float kea[C::PPT], keb[C::PPT];
+            RawPair vr[C::PPT];
 #pragma unroll
             for (int p = 0; p < C::PPT; ++p) {
                 const int pos = pgi * C::PPT + p;
                 const float Ga = G0[p] + off0, Gb = G1[p] + off1;
-                const float eGa = __expf(Ga), eGb = __expf(Gb);
-                const float emGa = __expf(-Ga), emGb = __expf(-Gb);
-                float ka = to_f(k_r[p][0]), kb = to_f(k_r[p][1]), bt = b_r[p];
-                float va = to_f(v_r[p][0]), vb2 = to_f(v_r[p][1]);
+                const float eGa = __builtin_amdgcn_exp2f(Ga), eGb = __builtin_amdgcn_exp2f(Gb);
+                const float emGa = __builtin_amdgcn_exp2f(-Ga), emGb = __builtin_amdgcn_exp2f(-Gb);
+                float ka = to_f(k_r[p][0]), kb = to_f(k_r[p][1]);
                 float qa = 0.0f, qb = 0.0f;
                 if constexpr (!MAP) {
                     qa = to_f(q_r[p][0]);
                     qb = to_f(q_r[p][1]);
                 }
-                if (mask && !(t0 + pos < T)) {   // padding token: k = q = v = beta = 0
-                    ka = kb = bt = va = vb2 = qa = qb = 0.0f;
+                vr[p] = v_r[p];
+                if (PARTIAL && !(t0 + pos < T)) {   // padding token: k = q = v = 0
+                    ka = kb = qa = qb = 0.0f;
+                    vr[p][0] = vr[p][1] = from_f<E>(0.0f);
                 }
-                kea[p] = ka * (eC0 * emGa);        // k * exp(G_C - G), every factor <= 1 in range
-                keb[p] = kb * (eC1 * emGb);
-                vba[p] = bt * va;
-                vbb[p] = bt * vb2;
-                store_pair(&sm.kn_row[pos * C::LDR + ch], -bt * ka * eGa, -bt * kb * eGb);
-                store_pair(&sm.km_row[pos * C::LDR + ch], ka * emGa, kb * emGb);
+                const float kma = ka * emGa, kmb = kb * emGb;
+                kea[p] = kma * eC0;                 // k * exp(G_C - G), every factor <= 1 in range
+                keb[p] = kmb * eC1;
+                store_pair(&sm.kn_row[pos * C::LDR + ch], -ka * eGa, -kb * eGb);
+                store_pair(&sm.km_row[pos * C::LDR + ch], kma, kmb);
                 if constexpr (!MAP) store_pair(&sm.qp_row[pos * C::LDR + ch], qa * eGa, qb * eGb);
             }
             const int pos0 = pgi * C::PPT;
-            store_run<E, C::PPT>(&sm.ke_col[ch * C::LDC + pos0], kea);
-            store_run<E, C::PPT>(&sm.ke_col[(ch + 1) * C::LDC + pos0], keb);
-            store_run<E, C::PPT>(&sm.vb_col[ch * C::LDC + pos0], vba);
-            store_run<E, C::PPT>(&sm.vb_col[(ch + 1) * C::LDC + pos0], vbb);
+            const int kp = 8 * (pos0 >> 2) + (pos0 & 3);   // padded slot of token pos0
+            store_run<E, C::PPT>(&sm.ke_pad[ch * LDP + kp], kea);
+            store_run<E, C::PPT>(&sm.ke_pad[(ch + 1) * LDP + kp], keb);
+            store_pair_runs<E, C::PPT>(&sm.v_col[ch * C::LDC + pos0], &sm.v_col[(ch + 1) * C::LDC + pos0], vr);
         }
         if constexpr (!MAP)
             if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
@@ -282,24 +346,26 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
         // ---------------- stage 2: diagonal tiles, then the state-side products
         // for every column tile, overlapped with the triangular solve:
-        //   Y  = beta*V - beta*K+ S      (so that U = T Y = Ut - W S)
-        //   O1 = Q+ S
+        //   Y   = beta*(V - K+ S)      (so that U = T Y = Ut - W S)
+        //   O1^T = S^T Q+^T
+        const f32x4 btv = *reinterpret_cast<const f32x4*>(&sm.bt[4 * g]);   // beta of rows 4g+i
         if (wave == 0) {
             // A = StrictLower(beta K+ K-^T), kept transposed in LDS: akk_t[col][row]
             const f32x4 a = MM::template mm_ll<D>(sm.kn_row, C::LDR, sm.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
             f32x4 m;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? -a[i] : 0.0f;   // mask by select
+            for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? -btv[i] * a[i] : 0.0f;   // mask by select
             *reinterpret_cast<f32x4*>(&sm.akk_t[r * 20 + 4 * g]) = m;
         } else if (!MAP && wave == 1) {
-            const f32x4 a = MM::template mm_ll<D>(sm.qp_row, C::LDR, sm.km_row, C::LDR,
+            // A_qk^T = K- Q+^T; lane (g, r) holds A_qk[r][4g+i], i.e. four
+            // consecutive k-slots of row r of the padded tile
+            const f32x4 a = MM::template mm_ll<D>(sm.km_row, C::LDR, sm.qp_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
+            f32x4 m;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * g + i;
-                sm.aqk_row[row * C::LDC + r] = from_f<E>((r <= row) ? a[i] : 0.0f);
-            }
+            for (int i = 0; i < 4; ++i) m[i] = (4 * g + i <= r) ? a[i] : 0.0f;
+            store4<E>(&sm.aqk_pad[r * LDP + 8 * g], m);
         }
         f32x4 y[C::TPW], o1[C::TPW];
 #pragma unroll
@@ -313,10 +379,10 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             if (jt < D / 16) {   // value columns; the M part of a widened state has V = 0
                 const int cb = (16 * jt + r) * C::LDC + 4 * g;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) yc[i] = to_f(sm.vb_col[cb + i]);
+                for (int i = 0; i < 4; ++i) yc[i] = to_f(sm.v_col[cb + i]);
             }
             y[jj] = MM::template mm_la<D>(sm.kn_row, C::LDR, sb, yc, r, g);
-            if constexpr (!MAP) o1[jj] = MM::template mm_la<D>(sm.qp_row, C::LDR, sb, f32x4{0, 0, 0, 0}, r, g);
+            if constexpr (!MAP) o1[jj] = MM::template mm_al<D>(sb, sm.qp_row, C::LDR, f32x4{0, 0, 0, 0}, r, g);
         }
         // The products above are issued before the solve starts (matrix cores
         // run them while the solve proceeds); keeping the two apart in the
@@ -342,7 +408,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             }
             if (lane < 16) {
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) sm.t_row[rr * C::LDC + j] = from_f<E>(x[rr]);
+                for (int rr = 0; rr < 16; ++rr) sm.t_pad[rr * LDP + 8 * (j >> 2) + (j & 3)] = from_f<E>(x[rr]);
             }
         }
         __syncthreads();
@@ -352,24 +418,31 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         for (int jj = 0; jj < C::TPW; ++jj) {
             const int jt = wave + C::NW * jj;
             if (jt >= C::NT) continue;
-            const BFrag yb = MM::to_b(y[jj]);
-            const f32x4 u = MM::template mm_la<16>(sm.t_row, C::LDC, &yb, f32x4{0, 0, 0, 0}, r, g);
-            const BFrag ub = MM::to_b(u);
-            if constexpr (!MAP) {
-                const f32x4 oo = MM::template mm_la<16>(sm.aqk_row, C::LDC, &ub, o1[jj], r, g);
+            f32x4 yy = y[jj];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.o_tile[(4 * g + i) * C::LDR + 16 * jt + r] = from_f<E>(oo[i]);
+            for (int i = 0; i < 4; ++i) yy[i] *= btv[i];
+            const f32x4 u = MM::mm16_pa(&sm.t_pad[r * LDP], MM::to_p(yy), f32x4{0, 0, 0, 0}, g);
+            const PFrag up = MM::to_p(u);
+            if constexpr (!MAP) {
+                // O^T = O1^T + U^T A_qk^T: lane (g, r) holds o[token r][16jt + 4g + i]
+                const f32x4 ot = MM::mm16_ap(up, &sm.aqk_pad[r * LDP], o1[jj], g);
+                store4<E>(&sm.o_tile[r * C::LDR + 16 * jt + 4 * g], ot);
             }
 #pragma unroll
             for (int t = 0; t < C::KT; ++t) {
                 const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * t + 4 * g]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[jj][t][i] *= gcv[i];
-                S[jj][t] = MM::template mm_la<16>(sm.ke_col + 16 * t * C::LDC, C::LDC, &ub, S[jj][t], r, g);
+                S[jj][t] = MM::mm16_pa(&sm.ke_pad[(16 * t + r) * LDP], up, S[jj][t], g);
             }
         }
         __syncthreads();
-    }
+    };
+
+    load_chunk(c0);
+    __syncthreads();   // zero-filled padding visible to every wavefront
+    for (int n = c0; n < c_full; ++n) chunk(std::false_type{}, n);
+    if (c_full < c1) chunk(std::true_type{}, c_full);
     if constexpr (!MAP) store_o(c1 - 1, true);
 
     // ---- write the segment's final state

@@ -81,6 +81,35 @@ __device__ __forceinline__ f32x4 mfma_k4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- buffer loads
+// Global loads through a buffer resource: the base address and the per-chunk
+// offsets live in scalar registers, the per-lane offset is one loop-invariant
+// 32-bit register, so a load costs no vector address arithmetic.  The range is
+// left unbounded (callers only address memory they own).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
+    // dword3 0x00020000: 32-bit data format, the raw-buffer setting for gfx9 parts.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ f32x2 buf_ld_f2(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+// Two adjacent storage elements as one load.
+template <typename E> struct BufPair;
+template <> struct BufPair<bf16> {
+    static __device__ __forceinline__ bf16x2 ld(Rsrc r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(bf16x2, buf_ld32(r, voff, soff));
+    }
+};
+template <> struct BufPair<float> {
+    static __device__ __forceinline__ f32x2 ld(Rsrc r, uint32_t voff, uint32_t soff) {
+        return buf_ld_f2(r, voff, soff);
+    }
+};
+
 __device__ __forceinline__ bf16x4 ld_b4(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 __device__ __forceinline__ bf16x8 ld_b8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
@@ -134,6 +163,42 @@ template <> struct Ops<bf16> {
         return acc;
     }
 
+    // mm_la with the operands' roles exchanged: D += B^T A^T, i.e. the B
+    // fragments (accumulator tiles of a K x 16 matrix X) act as the A operand
+    // (rows of X^T) and rows of the LDS matrix A act as the B operand.  Same k-map.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_al(const BFrag* Bf, const bf16* A, int lda,
+                                                  f32x4 acc, int r, int g) {
+        if constexpr (K == 16) {
+            acc = mfma_k16(Bf[0], ld_b4(A + r * lda + 4 * g), acc);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const bf16* a = A + r * lda + 32 * kb + 4 * g;
+                acc = mfma_k32(cat8(Bf[2 * kb], Bf[2 * kb + 1]), cat8(ld_b4(a), ld_b4(a + 16)), acc);
+            }
+        }
+        return acc;
+    }
+
+    // K = 16 products against "padded" LDS tiles: row m of the 16 x 16 operand
+    // is stored as 4 groups of 8 elements, group g holding k = 4g .. 4g+3 and
+    // four zeros, so one 16-byte load yields a complete 16x16x32 operand.
+    typedef bf16x8 PFrag;   // a register operand in the same padded form
+    static constexpr int PAD_ROW = 40;   // elements per padded row (32 + 8 against bank conflicts)
+    static __device__ __forceinline__ PFrag to_p(f32x4 x) {
+        const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+        return cat8(to_b(x), z);
+    }
+    // D += A B, A from the padded LDS row at Arow, B a register fragment.
+    static __device__ __forceinline__ f32x4 mm16_pa(const bf16* Arow, PFrag b, f32x4 acc, int g) {
+        return mfma_k32(ld_b8(Arow + 8 * g), b, acc);
+    }
+    // D += A B, A a register fragment, B from the padded LDS row at Brow (column r of B).
+    static __device__ __forceinline__ f32x4 mm16_ap(PFrag a, const bf16* Brow, f32x4 acc, int g) {
+        return mfma_k32(a, ld_b8(Brow + 8 * g), acc);
+    }
+
     // As mm_la, with A read from global fp32 memory (row-major, leading dim lda)
     // and rounded to bf16 on the fly.
     template <int K>
@@ -176,6 +241,37 @@ template <> struct Ops<float> {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], Bf[t][i], acc);
         }
+        return acc;
+    }
+
+    // Exchanged roles, as in the bf16 version.
+    template <int K>
+    static __device__ __forceinline__ f32x4 mm_al(const BFrag* Bf, const float* A, int lda,
+                                                  f32x4 acc, int r, int g) {
+#pragma unroll
+        for (int t = 0; t < K / 16; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma_k4(Bf[t][i], a[i], acc);
+        }
+        return acc;
+    }
+
+    // Padded K = 16 tiles (see the bf16 version); in fp32 only the first four
+    // elements of each group are used, one k-step per element.
+    typedef f32x4 PFrag;
+    static constexpr int PAD_ROW = 36;
+    static __device__ __forceinline__ PFrag to_p(f32x4 x) { return x; }
+    static __device__ __forceinline__ f32x4 mm16_pa(const float* Arow, PFrag b, f32x4 acc, int g) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(Arow + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], b[i], acc);
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 mm16_ap(PFrag a, const float* Brow, f32x4 acc, int g) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(Brow + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], b[i], acc);
         return acc;
     }
 
