@@ -138,7 +138,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     constexpr int LDP = SM::LDP;
     __shared__ SM sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index as a scalar, so that branches on it stay scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int nblk_seg = MAP ? nseg - 1 : nseg;
     const int bh = blockIdx.x / nblk_seg, seg = blockIdx.x % nblk_seg;
@@ -342,7 +343,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         if constexpr (!MAP)
             if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
         if (n + 1 < c1) load_chunk(n + 1);        // in flight until the next chunk's gate stage
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- stage 2: diagonal tiles, then the state-side products
         // for every column tile, overlapped with the triangular solve:
@@ -367,23 +368,26 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             for (int i = 0; i < 4; ++i) m[i] = (4 * g + i <= r) ? a[i] : 0.0f;
             store4<E>(&sm.aqk_pad[r * LDP + 8 * g], m);
         }
+        // Tiles of this wavefront: jt = wave + NW*jj for jj < nv (wave-uniform).
+        const int nv = C::NT % C::NW == 0 ? C::TPW : (wave < C::NT ? min(C::TPW, (C::NT - 1 - wave) / C::NW + 1) : 0);
         f32x4 y[C::TPW], o1[C::TPW];
+        BFrag sb[C::TPW * C::KT];
 #pragma unroll
         for (int jj = 0; jj < C::TPW; ++jj) {
             const int jt = wave + C::NW * jj;
-            if (jt >= C::NT) continue;
-            BFrag sb[C::KT];
 #pragma unroll
-            for (int t = 0; t < C::KT; ++t) sb[t] = MM::to_b(S[jj][t]);
+            for (int t = 0; t < C::KT; ++t) sb[jj * C::KT + t] = MM::to_b(S[jj][t]);
             f32x4 yc = f32x4{0, 0, 0, 0};
-            if (jt < D / 16) {   // value columns; the M part of a widened state has V = 0
+            if (jj < nv && jt < D / 16) {   // value columns; the M part of a widened state has V = 0
                 const int cb = (16 * jt + r) * C::LDC + 4 * g;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) yc[i] = to_f(sm.v_col[cb + i]);
             }
-            y[jj] = MM::template mm_la<D>(sm.kn_row, C::LDR, sb, yc, r, g);
-            if constexpr (!MAP) o1[jj] = MM::template mm_al<D>(sb, sm.qp_row, C::LDR, f32x4{0, 0, 0, 0}, r, g);
+            y[jj] = yc;
+            o1[jj] = f32x4{0, 0, 0, 0};
         }
+        MM::template mm_la_n<D, C::TPW>(sm.kn_row, C::LDR, sb, y, nv, r, g);
+        if constexpr (!MAP) MM::template mm_al_n<D, C::TPW>(sb, sm.qp_row, C::LDR, o1, nv, r, g);
         // The products above are issued before the solve starts (matrix cores
         // run them while the solve proceeds); keeping the two apart in the
         // instruction stream also keeps their registers from being live at once.
@@ -411,36 +415,52 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 for (int rr = 0; rr < 16; ++rr) sm.t_pad[rr * LDP + 8 * (j >> 2) + (j & 3)] = from_f<E>(x[rr]);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- stage 3: U = T Y, output, state update per column tile
+        // (operand fragments shared by the tiles are loaded once)
+        PFrag up[C::TPW];
+        {
+            const PFrag tf = MM::ld_p(&sm.t_pad[r * LDP], g);
+            PFrag qf;
+            if constexpr (!MAP) qf = MM::ld_p(&sm.aqk_pad[r * LDP], g);
 #pragma unroll
-        for (int jj = 0; jj < C::TPW; ++jj) {
-            const int jt = wave + C::NW * jj;
-            if (jt >= C::NT) continue;
-            f32x4 yy = y[jj];
+            for (int jj = 0; jj < C::TPW; ++jj) {
+                if (jj >= nv) continue;
+                const int jt = wave + C::NW * jj;
+                f32x4 yy = y[jj];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) yy[i] *= btv[i];
-            const f32x4 u = MM::mm16_pa(&sm.t_pad[r * LDP], MM::to_p(yy), f32x4{0, 0, 0, 0}, g);
-            const PFrag up = MM::to_p(u);
-            if constexpr (!MAP) {
-                // O^T = O1^T + U^T A_qk^T: lane (g, r) holds o[token r][16jt + 4g + i]
-                const f32x4 ot = MM::mm16_ap(up, &sm.aqk_pad[r * LDP], o1[jj], g);
-                store4<E>(&sm.o_tile[r * C::LDR + 16 * jt + 4 * g], ot);
-            }
-#pragma unroll
-            for (int t = 0; t < C::KT; ++t) {
-                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * t + 4 * g]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[jj][t][i] *= gcv[i];
-                S[jj][t] = MM::mm16_pa(&sm.ke_pad[(16 * t + r) * LDP], up, S[jj][t], g);
+                for (int i = 0; i < 4; ++i) yy[i] *= btv[i];
+                up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(yy), f32x4{0, 0, 0, 0}));
+                if constexpr (!MAP) {
+                    // O^T = O1^T + U^T A_qk^T: lane (g, r) holds o[token r][16jt + 4g + i]
+                    const f32x4 ot = MM::mm16(up[jj], qf, o1[jj]);
+                    store4<E>(&sm.o_tile[r * C::LDR + 16 * jt + 4 * g], ot);
+                }
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < C::KT; ++t) {
+            const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * t + 4 * g]);
+            const PFrag kf = MM::ld_p(&sm.ke_pad[(16 * t + r) * LDP], g);
+#pragma unroll
+            for (int jj = 0; jj < C::TPW; ++jj) {
+                if (jj >= nv) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[jj][t][i] *= gcv[i];
+                S[jj][t] = MM::mm16(kf, up[jj], S[jj][t]);
+            }
+        }
+        lds_barrier();
     };
 
     load_chunk(c0);
-    __syncthreads();   // zero-filled padding visible to every wavefront
+    // Retire every load issued so far (start state, first chunk) before the
+    // loop: otherwise the compiler's wait-counter analysis carries them into the
+    // loop and makes uses of the state registers wait for the next chunk's
+    // prefetch as well.
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();   // zero-filled padding visible to every wavefront
     for (int n = c0; n < c_full; ++n) chunk(std::false_type{}, n);
     if (c_full < c1) chunk(std::true_type{}, c_full);
     if constexpr (!MAP) store_o(c1 - 1, true);
@@ -472,6 +492,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 // The column tile is shared through LDS (transposed, rounded to the operand
 // type) at every step; the rows of M_s and the N_s tile each wavefront needs
 // are fetched two steps ahead into a three-slot register ring.
+constexpr int COMBINE_XCDS = 8;   // accelerator complex dies of an MI355X
+
 template <typename E, int D>
 struct CombineCfg {
     static constexpr int NW = 4, NTHR = 64 * NW;
@@ -488,7 +510,12 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
     __shared__ alignas(16) E st[16 * C::LDT];   // st[col][row]: the state column tile
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int bh = blockIdx.x / C::NT, jt = blockIdx.x % C::NT;
+    // Workgroups are dealt to the 8 XCDs round-robin by index; all column tiles
+    // of one head go to the same XCD so that its L2 serves the segment maps
+    // (read by every tile) once from HBM.
+    const int xcd = blockIdx.x % COMBINE_XCDS, i = blockIdx.x / COMBINE_XCDS;
+    const int bh = xcd + COMBINE_XCDS * (i / C::NT), jt = i % C::NT;
+    if (bh >= BH) return;
 
     struct Pref {
         f32x4 m[C::RPW][C::KT];   // M rows 16rt + r, columns 16t + 4g .. +3
@@ -534,7 +561,7 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
     Pref ring0, ring1, ring2;
     if (nsteps > 0) fetch(0, ring0);
     if (nsteps > 1) fetch(1, ring1);
-    __syncthreads();
+    lds_barrier();
 
     // one step: S <- M_s S + N_s, using the prefetched slot `cur`, refilling `nxt2`
     auto step = [&](int s, const Pref& cur, Pref& nxt2) {
@@ -563,9 +590,9 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
             }
             acc[k] = a;
         }
-        __syncthreads();              // every wavefront has read the old column tile
+        lds_barrier();              // every wavefront has read the old column tile
         publish(s + 1, acc);
-        __syncthreads();
+        lds_barrier();
     };
     for (int s = 0; s < nsteps; s += 3) {
         step(s, ring0, ring2);
@@ -614,7 +641,9 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
                            stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k,
                            (const E*)v, theta, beta, (const float*)nullptr, (const float*)nullptr, ws_mn,
                            (E*)nullptr, (float*)nullptr);
-        hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, stream,
+        const int heads_per_xcd = (BH + COMBINE_XCDS - 1) / COMBINE_XCDS;
+        hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(COMBINE_XCDS * heads_per_xcd * (D / 16))),
+                           dim3(256), 0, stream,
                            BH, p.nseg,
                            S0, (const float*)ws_mn, ws_start);
     }

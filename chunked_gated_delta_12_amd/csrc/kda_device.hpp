@@ -37,6 +37,17 @@ __device__ __forceinline__ float gate_logdecay(float theta) {
     return G_MIN * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// ---------------------------------------------------------------- synchronisation
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// orders global memory, for which the compiler waits until every outstanding
+// global load has returned -- which would drain loads issued early on purpose.
+// Use this where the wavefronts exchange data through LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
@@ -198,6 +209,51 @@ template <> struct Ops<bf16> {
     static __device__ __forceinline__ f32x4 mm16_ap(PFrag a, const bf16* Brow, f32x4 acc, int g) {
         return mfma_k32(a, ld_b8(Brow + 8 * g), acc);
     }
+    // The padded operand of one lane, loaded once and reused by several products.
+    static __device__ __forceinline__ PFrag ld_p(const bf16* row, int g) { return ld_b8(row + 8 * g); }
+    static __device__ __forceinline__ f32x4 mm16(PFrag a, PFrag b, f32x4 acc) { return mfma_k32(a, b, acc); }
+
+    // mm_la and mm_al over NTL column tiles at once (tiles n < nv only): each
+    // fragment of the LDS operand is loaded once and used by every tile.
+    // Bf holds the tiles' fragments as Bf[n * (K / 16) + t].
+    template <int K, int NTL>
+    static __device__ __forceinline__ void mm_la_n(const bf16* A, int lda, const BFrag* Bf, f32x4* acc,
+                                                   int nv, int r, int g) {
+        if constexpr (K == 16) {
+            const bf16x4 a = ld_b4(A + r * lda + 4 * g);
+#pragma unroll
+            for (int n = 0; n < NTL; ++n)
+                if (n < nv) acc[n] = mfma_k16(a, Bf[n], acc[n]);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const bf16* ap = A + r * lda + 32 * kb + 4 * g;
+                const bf16x8 a = cat8(ld_b4(ap), ld_b4(ap + 16));
+#pragma unroll
+                for (int n = 0; n < NTL; ++n)
+                    if (n < nv) acc[n] = mfma_k32(a, cat8(Bf[n * (K / 16) + 2 * kb], Bf[n * (K / 16) + 2 * kb + 1]), acc[n]);
+            }
+        }
+    }
+    template <int K, int NTL>
+    static __device__ __forceinline__ void mm_al_n(const BFrag* Bf, const bf16* A, int lda, f32x4* acc,
+                                                   int nv, int r, int g) {
+        if constexpr (K == 16) {
+            const bf16x4 a = ld_b4(A + r * lda + 4 * g);
+#pragma unroll
+            for (int n = 0; n < NTL; ++n)
+                if (n < nv) acc[n] = mfma_k16(Bf[n], a, acc[n]);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const bf16* ap = A + r * lda + 32 * kb + 4 * g;
+                const bf16x8 a = cat8(ld_b4(ap), ld_b4(ap + 16));
+#pragma unroll
+                for (int n = 0; n < NTL; ++n)
+                    if (n < nv) acc[n] = mfma_k32(cat8(Bf[n * (K / 16) + 2 * kb], Bf[n * (K / 16) + 2 * kb + 1]), a, acc[n]);
+            }
+        }
+    }
 
     // As mm_la, with A read from global fp32 memory (row-major, leading dim lda)
     // and rounded to bf16 on the fly.
@@ -273,6 +329,44 @@ template <> struct Ops<float> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], b[i], acc);
         return acc;
+    }
+    static __device__ __forceinline__ PFrag ld_p(const float* row, int g) {
+        return *reinterpret_cast<const f32x4*>(row + 8 * g);
+    }
+    static __device__ __forceinline__ f32x4 mm16(PFrag a, PFrag b, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], b[i], acc);
+        return acc;
+    }
+
+    // Multi-tile forms, as in the bf16 version.
+    template <int K, int NTL>
+    static __device__ __forceinline__ void mm_la_n(const float* A, int lda, const BFrag* Bf, f32x4* acc,
+                                                   int nv, int r, int g) {
+#pragma unroll
+        for (int t = 0; t < K / 16; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+            for (int n = 0; n < NTL; ++n)
+                if (n < nv) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[n] = mfma_k4(a[i], Bf[n * (K / 16) + t][i], acc[n]);
+                }
+        }
+    }
+    template <int K, int NTL>
+    static __device__ __forceinline__ void mm_al_n(const BFrag* Bf, const float* A, int lda, f32x4* acc,
+                                                   int nv, int r, int g) {
+#pragma unroll
+        for (int t = 0; t < K / 16; ++t) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(A + r * lda + 16 * t + 4 * g);
+#pragma unroll
+            for (int n = 0; n < NTL; ++n)
+                if (n < nv) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[n] = mfma_k4(Bf[n * (K / 16) + t][i], a[i], acc[n]);
+                }
+        }
     }
 
     // As mm_la, with A read from global fp32 memory.
