@@ -109,7 +109,7 @@ int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segmen
         return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);
     const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
     const kda::SegPlan p = kda::plan_segments(T, req);
-    *bytes = kda::chunk_workspace_bytes(B, H, dk, dv, p.nseg);
+    *bytes = kda::chunk_workspace_bytes(B, H, dk, dv, p.nseg, p.nchunks);
     return ok();
 }
 
@@ -135,7 +135,7 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, 
 
     const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
     const kda::SegPlan plan = kda::plan_segments(T, req);
-    const size_t need = kda::chunk_workspace_bytes(B, H, dk, dv, plan.nseg);
+    const size_t need = kda::chunk_workspace_bytes(B, H, dk, dv, plan.nseg, plan.nchunks);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
                     workspace_bytes, workspace ? "" : " (NULL)");

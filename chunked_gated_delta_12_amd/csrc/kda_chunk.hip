@@ -123,13 +123,18 @@ __device__ __forceinline__ void store_pair_runs(E* pa, E* pb, const typename Pai
     *reinterpret_cast<V*>(pb) = b;
 }
 
-template <typename E, int D, bool MAP, int NW>
+// MAP: the map kernel (one workgroup per segment and head; widened state; it
+// also stores every chunk's T = (I + A)^-1 to ws_t, and the last segment's
+// workgroups exist only for that).  TWS: the out kernel reads T from ws_t
+// instead of forming A and solving for T itself.
+template <typename E, int D, bool MAP, int NW, bool TWS>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
              const float* __restrict__ theta, const float* __restrict__ beta,
              const float* S0, const float* __restrict__ ws_start, float* __restrict__ ws_mn,
-             E* __restrict__ o, float* S_T) {
+             E* ws_t, E* __restrict__ o, float* S_T) {
+    static_assert(!(MAP && TWS), "the map kernel forms T itself");
     typedef ChunkCfg<D, MAP, NW> C;
     typedef ChunkSmem<E, D, MAP, NW> SM;
     typedef Ops<E> MM;
@@ -141,8 +146,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     // wave index as a scalar, so that branches on it stay scalar branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int nblk_seg = MAP ? nseg - 1 : nseg;
-    const int bh = blockIdx.x / nblk_seg, seg = blockIdx.x % nblk_seg;
+    const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
     const int b = bh / H, h = bh % H;
     const int c0 = seg * seg_len;
     const int c1 = min(nchunks, c0 + seg_len);
@@ -195,6 +199,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     // read the last valid token instead (and are masked when used).  Idle lanes
     // read a valid element and ignore it.
     typedef typename Pair<E>::T RawPair;
+    typedef typename BufQuad<E>::T TQuad;
+    TQuad t_r;                                                   // T[r][4g .. 4g+3] (TWS)
     f32x2 th_r[C::PPT];
     RawPair k_r[C::PPT], q_r[C::PPT], v_r[C::PPT];
     float b_r[C::PPT];
@@ -210,6 +216,9 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         const Rsrc rq = make_rsrc(q + base);
         const Rsrc rv = make_rsrc(v + base);
         const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h);
+        if constexpr (TWS)
+            t_r = BufQuad<E>::ld(make_rsrc(ws_t + ((int64_t)bh * nchunks + n) * 256),
+                                 (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E), 0u);
         if (t0 + CHUNK <= T) {
 #pragma unroll
             for (int p = 0; p < C::PPT; ++p) {
@@ -268,6 +277,9 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     auto chunk = [&](auto partial_tag, int n) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
         const int t0 = n * CHUNK;
+        // T of this chunk is used in stage 3, after the next chunk's loads have
+        // been issued into t_r: keep this chunk's copy.
+        const TQuad t_cur = t_r;
         // ---------------- stage 1: gate, cumulative decay, scaled operand tiles
         float G0[C::PPT], G1[C::PPT];
         float run0 = 0.0f, run1 = 0.0f;
@@ -350,7 +362,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         //   Y   = beta*(V - K+ S)      (so that U = T Y = Ut - W S)
         //   O1^T = S^T Q+^T
         const f32x4 btv = *reinterpret_cast<const f32x4*>(&sm.bt[4 * g]);   // beta of rows 4g+i
-        if (wave == 0) {
+        if (!TWS && wave == 0) {
             // A = StrictLower(beta K+ K-^T), kept transposed in LDS: akk_t[col][row]
             const f32x4 a = MM::template mm_ll<D>(sm.kn_row, C::LDR, sm.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
@@ -358,7 +370,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 #pragma unroll
             for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? -btv[i] * a[i] : 0.0f;   // mask by select
             *reinterpret_cast<f32x4*>(&sm.akk_t[r * 20 + 4 * g]) = m;
-        } else if (!MAP && wave == 1) {
+        } else if (!MAP && wave == (TWS ? 0 : 1)) {
             // A_qk^T = K- Q+^T; lane (g, r) holds A_qk[r][4g+i], i.e. four
             // consecutive k-slots of row r of the padded tile
             const f32x4 a = MM::template mm_ll<D>(sm.km_row, C::LDR, sm.qp_row, C::LDR,
@@ -392,7 +404,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         // run them while the solve proceeds); keeping the two apart in the
         // instruction stream also keeps their registers from being live at once.
         __builtin_amdgcn_sched_barrier(0);
-        if (wave == 0) {
+        if (!TWS && wave == 0) {
             // T = (I + A)^-1, column j per lane, right-looking substitution: once
             // x[s] is final, every later row subtracts A[r][s] x[s].  (The LDS
             // round trip stays inside this wavefront, which executes in order.)
@@ -421,7 +433,19 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         // (operand fragments shared by the tiles are loaded once)
         PFrag up[C::TPW];
         {
-            const PFrag tf = MM::ld_p(&sm.t_pad[r * LDP], g);
+            PFrag tf;
+            if constexpr (TWS) tf = MM::pad(t_cur);
+            else tf = MM::ld_p(&sm.t_pad[r * LDP], g);
+            if constexpr (MAP) {
+                // publish T of this chunk for the out kernel: lane (g, r) holds T[r][4g .. 4g+3]
+                if (wave == C::NW - 1) {
+                    typedef E V4 __attribute__((__vector_size__(4 * sizeof(E))));
+                    V4 tv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tv[i] = sm.t_pad[r * LDP + 8 * g + i];
+                    *reinterpret_cast<V4*>(ws_t + ((int64_t)bh * nchunks + n) * 256 + r * 16 + 4 * g) = tv;
+                }
+            }
             PFrag qf;
             if constexpr (!MAP) qf = MM::ld_p(&sm.aqk_pad[r * LDP], g);
 #pragma unroll
@@ -476,7 +500,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * t + 4 * g + i;
                 if constexpr (MAP) {
-                    ws_mn[(((int64_t)seg * BH + bh) * D + row) * (2 * D) + 16 * jt + r] = S[jj][t][i];
+                    if (seg < nseg - 1) ws_mn[(((int64_t)seg * BH + bh) * D + row) * (2 * D) + 16 * jt + r] = S[jj][t][i];
                 } else {
                     if (S_T && seg == nseg - 1)
                         S_T[((int64_t)bh * D + row) * D + 16 * jt + r] = S[jj][t][i];
@@ -612,12 +636,13 @@ SegPlan plan_segments(int T, int requested) {
     return p;
 }
 
-size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg) {
+size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg, int nchunks) {
     if (nseg <= 1) return 0;
     const size_t bh = (size_t)B * H;
     const size_t mn = (size_t)(nseg - 1) * bh * dk * (size_t)(dv + dk);
     const size_t st = (size_t)nseg * bh * dk * dv;
-    return (mn + st) * sizeof(float);
+    const size_t tt = (size_t)nchunks * bh * CHUNK * CHUNK;   // T per chunk, sized for fp32
+    return (mn + st + tt) * sizeof(float);
 }
 
 // Wavefronts per workgroup: four, so that two workgroups share a compute unit
@@ -633,24 +658,32 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
     const int BH = B * H;
     float* ws_mn = nullptr;
     float* ws_start = nullptr;
+    E* ws_t = nullptr;
     if (p.nseg > 1) {
         ws_mn = reinterpret_cast<float*>(workspace);
         ws_start = ws_mn + (size_t)(p.nseg - 1) * BH * D * (2 * D);
-        hipLaunchKernelGGL((chunk_kernel<E, D, true, CHUNK_NW_MAP>), dim3((unsigned)(BH * (p.nseg - 1))),
+        ws_t = reinterpret_cast<E*>(ws_start + (size_t)p.nseg * BH * D * D);
+        hipLaunchKernelGGL((chunk_kernel<E, D, true, CHUNK_NW_MAP, false>), dim3((unsigned)(BH * p.nseg)),
                            dim3(64 * CHUNK_NW_MAP), 0,
                            stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k,
                            (const E*)v, theta, beta, (const float*)nullptr, (const float*)nullptr, ws_mn,
-                           (E*)nullptr, (float*)nullptr);
+                           ws_t, (E*)nullptr, (float*)nullptr);
         const int heads_per_xcd = (BH + COMBINE_XCDS - 1) / COMBINE_XCDS;
         hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(COMBINE_XCDS * heads_per_xcd * (D / 16))),
                            dim3(256), 0, stream,
                            BH, p.nseg,
                            S0, (const float*)ws_mn, ws_start);
     }
-    hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT>), dim3((unsigned)(BH * p.nseg)),
-                       dim3(64 * CHUNK_NW_OUT), 0, stream, T,
-                       H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
-                       beta, S0, (const float*)ws_start, (float*)nullptr, (E*)o, S_T);
+    if (p.nseg > 1)
+        hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT, true>), dim3((unsigned)(BH * p.nseg)),
+                           dim3(64 * CHUNK_NW_OUT), 0, stream, T,
+                           H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
+                           beta, S0, (const float*)ws_start, (float*)nullptr, ws_t, (E*)o, S_T);
+    else
+        hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT, false>), dim3((unsigned)BH),
+                           dim3(64 * CHUNK_NW_OUT), 0, stream, T,
+                           H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
+                           beta, S0, (const float*)nullptr, (float*)nullptr, (E*)nullptr, (E*)o, S_T);
     return hipGetLastError();
 }
 

@@ -108,6 +108,21 @@ __device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t sof
 __device__ __forceinline__ f32x2 buf_ld_f2(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
 }
+// Four adjacent storage elements as one load.
+template <typename E> struct BufQuad;
+template <> struct BufQuad<bf16> {
+    typedef bf16x4 T;
+    static __device__ __forceinline__ T ld(Rsrc r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+    }
+};
+template <> struct BufQuad<float> {
+    typedef f32x4 T;
+    static __device__ __forceinline__ T ld(Rsrc r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+    }
+};
+
 // Two adjacent storage elements as one load.
 template <typename E> struct BufPair;
 template <> struct BufPair<bf16> {
@@ -211,6 +226,11 @@ template <> struct Ops<bf16> {
     }
     // The padded operand of one lane, loaded once and reused by several products.
     static __device__ __forceinline__ PFrag ld_p(const bf16* row, int g) { return ld_b8(row + 8 * g); }
+    // Four k-slots held in registers, padded to an operand.
+    static __device__ __forceinline__ PFrag pad(bf16x4 x) {
+        const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+        return cat8(x, z);
+    }
     static __device__ __forceinline__ f32x4 mm16(PFrag a, PFrag b, f32x4 acc) { return mfma_k32(a, b, acc); }
 
     // mm_la and mm_al over NTL column tiles at once (tiles n < nv only): each
@@ -333,6 +353,7 @@ template <> struct Ops<float> {
     static __device__ __forceinline__ PFrag ld_p(const float* row, int g) {
         return *reinterpret_cast<const f32x4*>(row + 8 * g);
     }
+    static __device__ __forceinline__ PFrag pad(f32x4 x) { return x; }
     static __device__ __forceinline__ f32x4 mm16(PFrag a, PFrag b, f32x4 acc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = mfma_k4(a[i], b[i], acc);

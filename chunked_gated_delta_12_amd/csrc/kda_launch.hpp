@@ -18,8 +18,8 @@ struct SegPlan {
 };
 SegPlan plan_segments(int T, int requested);
 
-// Workspace bytes of a chunked prefill with `nseg` segments.
-size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg);
+// Workspace bytes of a chunked prefill with `nseg` segments of `nchunks` chunks in all.
+size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg, int nchunks);
 
 hipError_t launch_gate(int B, int T, int H, int dk, const float* theta, float* g, float* gcum,
                        hipStream_t stream);

@@ -93,9 +93,10 @@ def test_chunk_fwd_workspace_checks(lib):
 
 
 def test_workspace_formula_and_auto_segments(lib):
-    # [N | M] per segment but the last, plus a start state per segment, fp32
+    # [N | M] per segment but the last, a start state per segment, and the 16x16
+    # T = (I + A)^-1 of every chunk, all sized in fp32
     B, T, H, d, P = 1, 65536, 16, 128, 32
-    want = ((P - 1) * B * H * d * 2 * d + P * B * H * d * d) * 4
+    want = ((P - 1) * B * H * d * 2 * d + P * B * H * d * d + (T // 16) * B * H * 256) * 4
     assert kda.kda_chunk_fwd_workspace_size(B, T, H, d, d, P) == want
     assert kda.kda_chunk_fwd_auto_segments(1, 65536, 16, 128, 128) == 32
     assert kda.kda_chunk_fwd_auto_segments(64, 4096, 16, 128, 128) == 1
