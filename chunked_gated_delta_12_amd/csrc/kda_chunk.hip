@@ -79,7 +79,6 @@ struct ChunkSmem {
     alignas(16) E aqk_pad[MAP ? 8 : 16 * LDP];     // LowerIncl(Q+K-^T), padded [token][token]
     alignas(16) float akk_t[16 * 20];              // StrictLower(beta K+ K-^T)^T, fp32
     alignas(16) float gc[D];                       // Gamma_C per channel
-    alignas(16) float bt[CHUNK];                   // beta per token
 };
 
 // Store units of the o tile: SU bytes per thread and store (4, 8 or 16).
@@ -193,56 +192,64 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     }
 
     // ---- prefetch registers for one chunk (this thread's gate-stage elements).
-    // Buffer loads: the chunk's base address and the per-token offsets are
-    // scalars, the lane offset is loop invariant; the loads stay in flight until
-    // the next chunk's gate stage.  In the final, partial chunk, tokens past T
-    // read the last valid token instead (and are masked when used).  Idle lanes
-    // read a valid element and ignore it.
+    // Buffer loads with scalar bases; the loads stay in flight until the
+    // chunk's gate stage.  Idle lanes read a valid element and ignore it.
     typedef typename Pair<E>::T RawPair;
     typedef typename BufQuad<E>::T TQuad;
-    TQuad t_r;                                                   // T[r][4g .. 4g+3] (TWS)
-    f32x2 th_r[C::PPT];
-    RawPair k_r[C::PPT], q_r[C::PPT], v_r[C::PPT];
-    float b_r[C::PPT];
+    struct Pref {
+        f32x2 th[C::PPT];
+        RawPair k[C::PPT], q[C::PPT], v[C::PPT];
+    };
+    // Inputs used only after the gate stage -- T[r][4g .. 4g+3] (TWS) and beta
+    // of tokens 4g .. 4g+3 (the rows of this lane's tiles) -- have a set of
+    // their own, refilled for the next chunk as soon as the current chunk is
+    // done with them.
+    TQuad t_l;
+    float b_l[4];
+    // Prefetch distance in chunks: two register sets where registers allow it
+    // (the out kernel that reads T), one otherwise.
+    constexpr int PFD = TWS ? 2 : 1;
+    Pref pa, pb;
     const uint32_t lane_tok = (uint32_t)(pgi * C::PPT);          // first token of this lane in a chunk
     const uint32_t lane_ch = gact ? (uint32_t)ch : 0u;
     const uint32_t tstr = (uint32_t)tok_stride;                  // elements between tokens
-    const uint32_t lane_el = lane_tok * tstr + lane_ch;          // element offset in a chunk
-    auto load_chunk = [&](int n) {
+    // Per-lane element offsets of this lane's tokens inside a chunk (loop
+    // invariant).  Each load carries its full offset in the lane register, so a
+    // resource sized to the chunk's valid tokens returns zeros for the padding
+    // tokens of the final, partial chunk and every chunk runs the same loads.
+    uint32_t el_off[C::PPT], b_off[4];
+#pragma unroll
+    for (int p = 0; p < C::PPT; ++p) el_off[p] = (lane_tok + (uint32_t)p) * tstr + lane_ch;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b_off[i] = (uint32_t)(4 * g + i) * (uint32_t)H * 4u;
+    auto load_chunk = [&](int n, Pref& d) {
         const int t0 = n * CHUNK;
-        const int64_t base = head_base + (int64_t)t0 * tok_stride;   // uniform
-        const Rsrc rth = make_rsrc(theta + base);
-        const Rsrc rk = make_rsrc(k + base);
-        const Rsrc rq = make_rsrc(q + base);
-        const Rsrc rv = make_rsrc(v + base);
-        const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h);
-        if constexpr (TWS)
-            t_r = BufQuad<E>::ld(make_rsrc(ws_t + ((int64_t)bh * nchunks + n) * 256),
-                                 (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E), 0u);
-        if (t0 + CHUNK <= T) {
+        const uint32_t nvalid = (uint32_t)min(CHUNK, T - t0);             // uniform
+        const int64_t base = head_base + (int64_t)t0 * tok_stride;       // uniform
+        const uint32_t span = nvalid * tstr;                             // elements of valid tokens
+        const Rsrc rth = make_rsrc(theta + base, span * 4u);
+        const Rsrc rk = make_rsrc(k + base, span * (uint32_t)sizeof(E));
+        const Rsrc rq = make_rsrc(q + base, span * (uint32_t)sizeof(E));
+        const Rsrc rv = make_rsrc(v + base, span * (uint32_t)sizeof(E));
 #pragma unroll
-            for (int p = 0; p < C::PPT; ++p) {
-                const uint32_t so = (uint32_t)p * tstr;             // uniform
-                th_r[p] = buf_ld_f2(rth, lane_el * 4u, so * 4u);
-                k_r[p] = BufPair<E>::ld(rk, lane_el * (uint32_t)sizeof(E), so * (uint32_t)sizeof(E));
-                if constexpr (!MAP) q_r[p] = BufPair<E>::ld(rq, lane_el * (uint32_t)sizeof(E), so * (uint32_t)sizeof(E));
-                v_r[p] = BufPair<E>::ld(rv, lane_el * (uint32_t)sizeof(E), so * (uint32_t)sizeof(E));
-                b_r[p] = __builtin_bit_cast(float, buf_ld32(rb, lane_tok * (uint32_t)H * 4u, (uint32_t)(p * H) * 4u));
-            }
-        } else {
-            const uint32_t last = (uint32_t)(T - t0 - 1);
-#pragma unroll
-            for (int p = 0; p < C::PPT; ++p) {
-                const uint32_t tl = min(lane_tok + (uint32_t)p, last);
-                const uint32_t el = tl * tstr + lane_ch;
-                th_r[p] = buf_ld_f2(rth, el * 4u, 0u);
-                k_r[p] = BufPair<E>::ld(rk, el * (uint32_t)sizeof(E), 0u);
-                if constexpr (!MAP) q_r[p] = BufPair<E>::ld(rq, el * (uint32_t)sizeof(E), 0u);
-                v_r[p] = BufPair<E>::ld(rv, el * (uint32_t)sizeof(E), 0u);
-                b_r[p] = __builtin_bit_cast(float, buf_ld32(rb, tl * (uint32_t)H * 4u, 0u));
-            }
+        for (int p = 0; p < C::PPT; ++p) {
+            d.th[p] = buf_ld_f2(rth, el_off[p] * 4u, 0u);
+            d.k[p] = BufPair<E>::ld(rk, el_off[p] * (uint32_t)sizeof(E), 0u);
+            if constexpr (!MAP) d.q[p] = BufPair<E>::ld(rq, el_off[p] * (uint32_t)sizeof(E), 0u);
+            d.v[p] = BufPair<E>::ld(rv, el_off[p] * (uint32_t)sizeof(E), 0u);
         }
     };
+    auto load_late = [&](int n) {
+        const int t0 = n * CHUNK;
+        const uint32_t nvalid = (uint32_t)min(CHUNK, T - t0);             // uniform
+        const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h, nvalid * (uint32_t)H * 4u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b_l[i] = __builtin_bit_cast(float, buf_ld32(rb, b_off[i], 0u));
+        if constexpr (TWS)
+            t_l = BufQuad<E>::ld(make_rsrc(ws_t + ((int64_t)bh * nchunks + n) * 256),
+                                 (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E), 0u);
+    };
+
 
     // ---- write the o tile of chunk n (staged in LDS) with coalesced stores.
     // Every thread stores the same number of units for a full chunk, so no
@@ -274,19 +281,16 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
     // ---- one chunk.  PARTIAL: the final chunk with fewer than 16 tokens; its
     // padding tokens get g = 0, beta = k = q = v = 0, which leave the state unchanged.
-    auto chunk = [&](auto partial_tag, int n) {
+    auto chunk = [&](auto partial_tag, int n, Pref& cur) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
         const int t0 = n * CHUNK;
-        // T of this chunk is used in stage 3, after the next chunk's loads have
-        // been issued into t_r: keep this chunk's copy.
-        const TQuad t_cur = t_r;
         // ---------------- stage 1: gate, cumulative decay, scaled operand tiles
         float G0[C::PPT], G1[C::PPT];
         float run0 = 0.0f, run1 = 0.0f;
 #pragma unroll
         for (int p = 0; p < C::PPT; ++p) {
-            float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th_r[p][0]));
-            float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th_r[p][1]));
+            float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * cur.th[p][0]));
+            float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * cur.th[p][1]));
             if (PARTIAL || !ALL_ACT) {
                 const bool ok = gact && (!PARTIAL || t0 + pgi * C::PPT + p < T);
                 ga = ok ? ga : 0.0f;
@@ -313,13 +317,6 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 sm.gc[ch] = eC0;
                 sm.gc[ch + 1] = eC1;
             }
-            if (cp == 0) {
-#pragma unroll
-                for (int p = 0; p < C::PPT; ++p) {
-                    const bool ok = !PARTIAL || t0 + pgi * C::PPT + p < T;
-                    sm.bt[pgi * C::PPT + p] = ok ? b_r[p] : 0.0f;
-                }
-            }
             float kea[C::PPT], keb[C::PPT];
             RawPair vr[C::PPT];
 #pragma unroll
@@ -328,13 +325,13 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 const float Ga = G0[p] + off0, Gb = G1[p] + off1;
                 const float eGa = __builtin_amdgcn_exp2f(Ga), eGb = __builtin_amdgcn_exp2f(Gb);
                 const float emGa = __builtin_amdgcn_exp2f(-Ga), emGb = __builtin_amdgcn_exp2f(-Gb);
-                float ka = to_f(k_r[p][0]), kb = to_f(k_r[p][1]);
+                float ka = to_f(cur.k[p][0]), kb = to_f(cur.k[p][1]);
                 float qa = 0.0f, qb = 0.0f;
                 if constexpr (!MAP) {
-                    qa = to_f(q_r[p][0]);
-                    qb = to_f(q_r[p][1]);
+                    qa = to_f(cur.q[p][0]);
+                    qb = to_f(cur.q[p][1]);
                 }
-                vr[p] = v_r[p];
+                vr[p] = cur.v[p];
                 if (PARTIAL && !(t0 + pos < T)) {   // padding token: k = q = v = 0
                     ka = kb = qa = qb = 0.0f;
                     vr[p][0] = vr[p][1] = from_f<E>(0.0f);
@@ -354,14 +351,16 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         }
         if constexpr (!MAP)
             if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
-        if (n + 1 < c1) load_chunk(n + 1);        // in flight until the next chunk's gate stage
+        if (n + PFD < c1) load_chunk(n + PFD, cur);   // in flight until that chunk's gate stage
         lds_barrier();
+
+        // beta of rows 4g+i (zero past T: loads of padding tokens return zero)
+        const f32x4 btv = f32x4{b_l[0], b_l[1], b_l[2], b_l[3]};
 
         // ---------------- stage 2: diagonal tiles, then the state-side products
         // for every column tile, overlapped with the triangular solve:
         //   Y   = beta*(V - K+ S)      (so that U = T Y = Ut - W S)
         //   O1^T = S^T Q+^T
-        const f32x4 btv = *reinterpret_cast<const f32x4*>(&sm.bt[4 * g]);   // beta of rows 4g+i
         if (!TWS && wave == 0) {
             // A = StrictLower(beta K+ K-^T), kept transposed in LDS: akk_t[col][row]
             const f32x4 a = MM::template mm_ll<D>(sm.kn_row, C::LDR, sm.km_row, C::LDR,
@@ -434,7 +433,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         PFrag up[C::TPW];
         {
             PFrag tf;
-            if constexpr (TWS) tf = MM::pad(t_cur);
+            if constexpr (TWS) tf = MM::pad(t_l);
             else tf = MM::ld_p(&sm.t_pad[r * LDP], g);
             if constexpr (MAP) {
                 // publish T of this chunk for the out kernel: lane (g, r) holds T[r][4g .. 4g+3]
@@ -463,6 +462,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 }
             }
         }
+        if (n + 1 < c1) load_late(n + 1);   // T and beta are no longer needed for this chunk
 #pragma unroll
         for (int t = 0; t < C::KT; ++t) {
             const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * t + 4 * g]);
@@ -478,15 +478,28 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         lds_barrier();
     };
 
-    load_chunk(c0);
+    load_chunk(c0, pa);
+    load_late(c0);
+    if (PFD == 2 && c0 + 1 < c1) load_chunk(c0 + 1, pb);
     // Retire every load issued so far (start state, first chunk) before the
     // loop: otherwise the compiler's wait-counter analysis carries them into the
     // loop and makes uses of the state registers wait for the next chunk's
     // prefetch as well.
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();   // zero-filled padding visible to every wavefront
-    for (int n = c0; n < c_full; ++n) chunk(std::false_type{}, n);
-    if (c_full < c1) chunk(std::true_type{}, c_full);
+    // chunk m uses register set pa if (m - c0) is even, pb otherwise
+    int n = c0;
+    if constexpr (PFD == 2) {
+        for (; n + 1 < c_full; n += 2) {
+            chunk(std::false_type{}, n, pa);
+            chunk(std::false_type{}, n + 1, pb);
+        }
+    }
+    for (; n < c_full; ++n) chunk(std::false_type{}, n, pa);   // at most one left when PFD == 2
+    if (c_full < c1) {
+        if (PFD == 2 && ((c_full - c0) & 1)) chunk(std::true_type{}, c_full, pb);
+        else chunk(std::true_type{}, c_full, pa);
+    }
     if constexpr (!MAP) store_o(c1 - 1, true);
 
     // ---- write the segment's final state

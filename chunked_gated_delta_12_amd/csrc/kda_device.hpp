@@ -93,14 +93,14 @@ __device__ __forceinline__ f32x4 mfma_k4(float a, float b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- buffer loads
-// Global loads through a buffer resource: the base address and the per-chunk
-// offsets live in scalar registers, the per-lane offset is one loop-invariant
-// 32-bit register, so a load costs no vector address arithmetic.  The range is
-// left unbounded (callers only address memory they own).
+// Global loads through a buffer resource: the base address lives in scalar
+// registers and the per-lane offset is a loop-invariant 32-bit register, so a
+// load costs no vector address arithmetic.  A load whose per-lane byte offset
+// is at or past the resource's size returns zero.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes = 0xffffffffu) {
     // dword3 0x00020000: 32-bit data format, the raw-buffer setting for gfx9 parts.
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
