@@ -78,6 +78,15 @@ CHUNK_CASES = [
     ("decay_stress", dict(H=4, T=1024), None, 8),
     ("decay_stress", dict(H=2, T=512), "f32", 4),                 # fp32 re-run of the stress case
     ("prefill_64k", dict(H=2, T=2048 + 9), None, 0),
+    # several segments with a ragged tail: the map kernel publishes T for the
+    # partial chunk and the out kernel reads it
+    ("tiny", dict(T=61), None, 3),
+    ("tiny", dict(T=77), "bf16", 2),                              # bf16 at d = 16
+    ("small", dict(dk=32, dv=32, H=3, T=333), None, 3),
+    # one chunk per segment; the last segment is the partial chunk alone
+    ("tiny", dict(T=53), None, 4),
+    ("small", dict(B=3, H=2, T=16 * 9 + 3), None, 10),
+    ("prefill_64k", dict(H=2, T=49), None, 4),
 ]
 
 
