@@ -242,12 +242,14 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     auto load_late = [&](int n) {
         const int t0 = n * CHUNK;
         const uint32_t nvalid = (uint32_t)min(CHUNK, T - t0);             // uniform
-        const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h, nvalid * (uint32_t)H * 4u);
+        if constexpr (!TWS) {
+            const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h, nvalid * (uint32_t)H * 4u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b_l[i] = __builtin_bit_cast(float, buf_ld32(rb, b_off[i], 0u));
-        if constexpr (TWS)
+            for (int i = 0; i < 4; ++i) b_l[i] = __builtin_bit_cast(float, buf_ld32(rb, b_off[i], 0u));
+        } else {
             t_l = BufQuad<E>::ld(make_rsrc(ws_t + ((int64_t)bh * nchunks + n) * 256),
                                  (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E), 0u);
+        }
     };
 
 
@@ -355,7 +357,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         lds_barrier();
 
         // beta of rows 4g+i (zero past T: loads of padding tokens return zero)
-        const f32x4 btv = f32x4{b_l[0], b_l[1], b_l[2], b_l[3]};
+        f32x4 btv = f32x4{0, 0, 0, 0};
+        if constexpr (!TWS) btv = f32x4{b_l[0], b_l[1], b_l[2], b_l[3]};
 
         // ---------------- stage 2: diagonal tiles, then the state-side products
         // for every column tile, overlapped with the triangular solve:
@@ -452,8 +455,10 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 if (jj >= nv) continue;
                 const int jt = wave + C::NW * jj;
                 f32x4 yy = y[jj];
+                if constexpr (!TWS) {   // the published T' already carries diag(beta)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) yy[i] *= btv[i];
+                    for (int i = 0; i < 4; ++i) yy[i] *= btv[i];
+                }
                 up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(yy), f32x4{0, 0, 0, 0}));
                 if constexpr (!MAP) {
                     // O^T = O1^T + U^T A_qk^T: lane (g, r) holds o[token r][16jt + 4g + i]
@@ -676,11 +681,9 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
         ws_mn = reinterpret_cast<float*>(workspace);
         ws_start = ws_mn + (size_t)(p.nseg - 1) * BH * D * (2 * D);
         ws_t = reinterpret_cast<E*>(ws_start + (size_t)p.nseg * BH * D * D);
-        hipLaunchKernelGGL((chunk_kernel<E, D, true, CHUNK_NW_MAP, false>), dim3((unsigned)(BH * p.nseg)),
-                           dim3(64 * CHUNK_NW_MAP), 0,
-                           stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k,
-                           (const E*)v, theta, beta, (const float*)nullptr, (const float*)nullptr, ws_mn,
-                           ws_t, (E*)nullptr, (float*)nullptr);
+        const hipError_t e = launch_chunk_map(std::is_same<E, float>::value, B, T, H, D, p, k, v, theta,
+                                              beta, ws_mn, ws_t, stream);
+        if (e != hipSuccess) return e;
         const int heads_per_xcd = (BH + COMBINE_XCDS - 1) / COMBINE_XCDS;
         hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(COMBINE_XCDS * heads_per_xcd * (D / 16))),
                            dim3(256), 0, stream,

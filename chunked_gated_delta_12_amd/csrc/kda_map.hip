@@ -1,0 +1,410 @@
+// kda_map.hip -- segment map kernel of the chunked prefill on gfx950.
+//
+// A chunk maps the state affinely, S' = M S + N ("Kimi K3 Deep Dive...", "The
+// Problem: The Diagonal-Block Dilemma" gives the chunk form; see kda_chunk.hip
+// for the algebra).  For every segment but the last, this kernel runs the chunk
+// scan with the state widened to [N | M], started from [0 | I], and stores the
+// end state.  For every chunk of every segment it also publishes
+//     T' = (I + A)^-1 diag(beta),   A = StrictLower(diag(beta) K+ K-^T),
+// so that the out kernel forms U = T' (V - K+ S) without a triangular solve.
+//
+// Wavefront roles.  Everything a chunk needs apart from the state -- the
+// gate, the decay-scaled tiles, A and T' -- is formed by NPW producer
+// wavefronts, one chunk each, into LDS slots.  NCW consumer wavefronts hold
+// the state tiles in registers and run only the state chain
+//     Y = V - K+ S,   U = T' Y,   S <- Diag(Gamma_C) S + Kend^T U
+// over the NPW chunks the producers finished in the previous step.  The slots
+// are double buffered, so a single barrier per step of NPW chunks separates
+// the two roles, and the consumers run NPW chunks back to back between
+// barriers.  A producer lane owns one channel pair of its chunk for all its
+// tokens (all 16 when d_k = 128), so the in-chunk prefix of the log-decay stays
+// inside the lane; its next chunk's inputs are loaded while it forms A and T'.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <typename E, int D>
+struct MapCfg {
+    static constexpr int NT = D / 8;                      // 16-column tiles of [N | M]
+    // consumer wavefronts: eight for bf16; four for fp32 (the validation type),
+    // whose wider operands need two wavefronts' registers per SIMD
+    static constexpr int NCWMAX = sizeof(E) == 2 ? 8 : 4;
+    static constexpr int NCW = NT < NCWMAX ? NT : NCWMAX;
+    static constexpr int TPW = NT / NCW;                  // state tiles per consumer
+    static constexpr int NPW = sizeof(E) == 2 ? 4 : 2;    // producer wavefronts = chunks per step
+    static constexpr int NW = NCW + NPW;
+    static constexpr int KT = D / 16;                     // 16-row tiles along d_k
+    static constexpr int LDR = D + 8;                     // padded [16][D] rows
+    static constexpr int LDK = 20;                        // padded [.][16] rows
+    static constexpr int PPL = D / 2 < 64 ? D / 2 : 64;   // channel pairs of a producer
+    static constexpr int NTG = 64 / PPL;                  // token groups (lanes per pair)
+    static constexpr int TPL = CHUNK / NTG;               // tokens per producer lane
+    static_assert(NT % NCW == 0, "state tiles split evenly");
+    static_assert(PPL * 2 == D, "one producer wavefront covers all channels");
+};
+
+// What the consumers read for one chunk.
+template <typename E, int D>
+struct MapSlot {
+    typedef MapCfg<E, D> C;
+    alignas(16) E kn_row[16 * C::LDR];   // -K+ = -K*Gamma            [token][ch]
+    alignas(16) E ke_col[D * C::LDK];    // Kend^T = (K*Gamma_C/Gamma)^T [ch][token]
+    alignas(16) E v_col[D * C::LDK];     // V^T                       [ch][token]
+    alignas(16) E t_row[16 * C::LDK];    // T' = (I + A)^-1 diag(beta) [row][k]
+    alignas(16) float gc[D];             // Gamma_C per channel
+};
+// Private to one producer wavefront.
+template <typename E, int D>
+struct MapScratch {
+    alignas(16) E km_row[16 * MapCfg<E, D>::LDR];   // K- = K/Gamma     [token][ch]
+    alignas(16) float akk_t[16 * 20];               // A^T, fp32        [col][row]
+};
+template <typename E, int D>
+struct MapSmem {
+    MapSlot<E, D> slot[2 * MapCfg<E, D>::NPW];
+    MapScratch<E, D> scr[MapCfg<E, D>::NPW];
+};
+
+// Orders this wavefront's LDS writes before its following LDS reads of other
+// lanes' data.  A wavefront's LDS instructions execute in issue order, so only
+// the compiler has to be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// N elements as 8-byte stores (4-byte when the run is shorter).
+template <typename E, int N>
+__device__ __forceinline__ void store_run8(E* p, const E* x) {
+    constexpr int B = N * (int)sizeof(E);
+    constexpr int U = B >= 8 ? 8 : B;
+    constexpr int EPU = U / (int)sizeof(E);
+    typedef E V __attribute__((__vector_size__(U)));
+#pragma unroll
+    for (int u = 0; u < B / U; ++u) {
+        V w;
+#pragma unroll
+        for (int i = 0; i < EPU; ++i) w[i] = x[u * EPU + i];
+        *reinterpret_cast<V*>(p + u * EPU) = w;
+    }
+}
+
+// Four consecutive elements from LDS, in the register form Ops<E>::pad takes.
+__device__ __forceinline__ bf16x4 ld_quad(const bf16* p) { return ld_b4(p); }
+__device__ __forceinline__ f32x4 ld_quad(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Four consecutive elements to global memory through a buffer resource (a
+// store at or past the resource's size is dropped).
+__device__ __forceinline__ void buf_st_quad(bf16x4 x, Rsrc r, uint32_t voff) {
+    typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ void buf_st_quad(f32x4 x, Rsrc r, uint32_t voff) {
+    typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)voff, 0, 0);
+}
+
+template <typename E, int D>
+__global__ void __launch_bounds__((64 * MapCfg<E, D>::NW))
+map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
+           const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ theta,
+           const float* __restrict__ beta, float* __restrict__ ws_mn, E* __restrict__ ws_t) {
+    typedef MapCfg<E, D> C;
+    typedef Ops<E> MM;
+    typedef typename MM::BFrag BFrag;
+    typedef typename MM::PFrag PFrag;
+    typedef MapSlot<E, D> Slot;
+    __shared__ MapSmem<E, D> sm;
+
+    // wave index as a scalar, so that branches on it stay scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int b = bh / H, h = bh % H;
+    const int c0 = seg * seg_len;
+    const int c1 = min(nchunks, c0 + seg_len);
+    const int nsteps = (c1 - c0 + C::NPW - 1) / C::NPW;
+    const int tend = min(T, c1 * CHUNK);            // the segment's tokens end here
+    const bool last = seg == nseg - 1;              // publishes T' only
+
+    if (wave >= C::NCW) {
+        // =================================================================== producer
+        const int pw = wave - C::NCW;
+        MapScratch<E, D>& scr = sm.scr[pw];
+        const int p = lane % C::PPL, tg = lane / C::PPL;
+        const int ch = 2 * p, tok0 = tg * C::TPL;
+        const uint32_t tstr = (uint32_t)(H * D);   // elements between tokens
+        const int64_t head_base = (int64_t)b * T * H * D + (int64_t)h * D;
+        typedef typename Pair<E>::T RawPair;
+        typedef typename BufQuad<E>::T Quad;
+
+        // Inputs of one chunk, loaded a step ahead.  Resources are sized to the
+        // chunk's tokens inside the segment: loads of the rest return zeros, and
+        // a chunk past the segment's end reads as all padding.
+        f32x2 th[C::TPL];
+        RawPair kr[C::TPL], vr[C::TPL];
+        float bl[4], br;
+        auto load = [&](int m) {
+            const int t0 = m * CHUNK;
+            // uniform; kept in a scalar register so the resources below stay scalar
+            const uint32_t nv = __builtin_amdgcn_readfirstlane(max(0, min(CHUNK, tend - t0)));
+            const int64_t base = head_base + (int64_t)t0 * tstr;
+            const uint32_t span = nv * tstr;
+            const Rsrc rth = make_rsrc(theta + base, span * 4u);
+            const Rsrc rk = make_rsrc(k + base, span * (uint32_t)sizeof(E));
+            const Rsrc rv = make_rsrc(v + base, span * (uint32_t)sizeof(E));
+#pragma unroll
+            for (int t = 0; t < C::TPL; ++t) {
+                const uint32_t el = (uint32_t)(tok0 + t) * tstr + (uint32_t)ch;
+                th[t] = buf_ld_f2(rth, el * 4u, 0u);
+                kr[t] = BufPair<E>::ld(rk, el * (uint32_t)sizeof(E), 0u);
+                vr[t] = BufPair<E>::ld(rv, el * (uint32_t)sizeof(E), 0u);
+            }
+        };
+        // beta of the chunk, loaded once the current chunk's beta is used up
+        auto load_beta = [&](int m) {
+            const int t0 = m * CHUNK;
+            const uint32_t nv = __builtin_amdgcn_readfirstlane(max(0, min(CHUNK, tend - t0)));
+            const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h, nv * (uint32_t)H * 4u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bl[i] = __builtin_bit_cast(float, buf_ld32(rb, (uint32_t)(4 * g + i) * (uint32_t)H * 4u, 0u));
+            br = __builtin_bit_cast(float, buf_ld32(rb, (uint32_t)r * (uint32_t)H * 4u, 0u));
+        };
+
+        constexpr float LOG2E = 1.4426950408889634f;
+        constexpr float GMIN2 = G_MIN * LOG2E;
+
+        auto produce = [&](int m, Slot& sl) {
+            const int t0 = m * CHUNK;
+            const int nv = max(0, min(CHUNK, tend - t0));
+            // ---- log-decay in base 2 (zero for padding tokens) and its in-lane prefix
+            float Ga[C::TPL], Gb[C::TPL];
+            float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+            for (int t = 0; t < C::TPL; ++t) {
+                float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][0]));
+                float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][1]));
+                const bool ok = tok0 + t < nv;
+                sa += ok ? ga : 0.0f;
+                sb += ok ? gb : 0.0f;
+                Ga[t] = sa;
+                Gb[t] = sb;
+            }
+            // prefix across the token groups of a pair (d_k < 128 only)
+            float offa = 0.0f, offb = 0.0f, tota = sa, totb = sb;
+            if constexpr (C::NTG > 1) {
+                float ia = sa, ib = sb;
+#pragma unroll
+                for (int d = 1; d < C::NTG; d <<= 1) {
+                    const float ua = __shfl_up(ia, d * C::PPL), ub = __shfl_up(ib, d * C::PPL);
+                    if (tg >= d) { ia += ua; ib += ub; }
+                }
+                offa = ia - sa;
+                offb = ib - sb;
+                tota = __shfl(ia, (C::NTG - 1) * C::PPL + p);
+                totb = __shfl(ib, (C::NTG - 1) * C::PPL + p);
+            }
+            const float eCa = __builtin_amdgcn_exp2f(tota), eCb = __builtin_amdgcn_exp2f(totb);
+            // ---- scaled tiles: -K+ and K- rows, Kend^T and V^T columns, Gamma_C
+            E kea[C::TPL], keb[C::TPL], va[C::TPL], vb[C::TPL];
+#pragma unroll
+            for (int t = 0; t < C::TPL; ++t) {
+                const int pos = tok0 + t;
+                const float xa = Ga[t] + offa, xb = Gb[t] + offb;
+                const float eGa = __builtin_amdgcn_exp2f(xa), eGb = __builtin_amdgcn_exp2f(xb);
+                const float emGa = __builtin_amdgcn_exp2f(-xa), emGb = __builtin_amdgcn_exp2f(-xb);
+                const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);   // zero for padding tokens
+                const float kma = ka * emGa, kmb = kb * emGb;
+                store_pair(&sl.kn_row[pos * C::LDR + ch], -ka * eGa, -kb * eGb);
+                store_pair(&scr.km_row[pos * C::LDR + ch], kma, kmb);
+                kea[t] = from_f<E>(kma * eCa);   // k * exp(G_C - G) <= |k|
+                keb[t] = from_f<E>(kmb * eCb);
+                va[t] = vr[t][0];
+                vb[t] = vr[t][1];
+                if constexpr (sizeof(E) == 4) {   // fp32: column elements one at a time (registers)
+                    sl.ke_col[ch * C::LDK + pos] = kea[t];
+                    sl.ke_col[(ch + 1) * C::LDK + pos] = keb[t];
+                    sl.v_col[ch * C::LDK + pos] = va[t];
+                    sl.v_col[(ch + 1) * C::LDK + pos] = vb[t];
+                }
+            }
+            if constexpr (sizeof(E) == 2) {   // bf16: packed runs of the lane's tokens
+                store_run8<E, C::TPL>(&sl.ke_col[ch * C::LDK + tok0], kea);
+                store_run8<E, C::TPL>(&sl.ke_col[(ch + 1) * C::LDK + tok0], keb);
+                store_run8<E, C::TPL>(&sl.v_col[ch * C::LDK + tok0], va);
+                store_run8<E, C::TPL>(&sl.v_col[(ch + 1) * C::LDK + tok0], vb);
+            }
+            *reinterpret_cast<f32x2*>(&sl.gc[ch]) = f32x2{eCa, eCb};   // token groups write equal values
+            load(m + C::NPW);   // in flight while A and T' are formed
+            wave_lds_sync();
+
+            // ---- A = StrictLower(diag(beta) K+ K-^T), transposed: akk_t[col][row]
+            const f32x4 a = MM::template mm_ll<D>(sl.kn_row, C::LDR, scr.km_row, C::LDR,
+                                                  f32x4{0, 0, 0, 0}, r, g);
+            f32x4 am;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) am[i] = (r < 4 * g + i) ? -bl[i] * a[i] : 0.0f;   // beta of row 4g+i
+            *reinterpret_cast<f32x4*>(&scr.akk_t[r * 20 + 4 * g]) = am;
+            wave_lds_sync();
+
+            // ---- T = (I + A)^-1, column j = r per lane (the four lane groups hold
+            // copies), right-looking: once x[s] is final, every later row subtracts
+            // A[row][s] x[s].
+            float x[16];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == r) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                f32x4 col[4];
+#pragma unroll
+                for (int c = s / 4; c < 4; ++c)
+                    col[c] = *reinterpret_cast<const f32x4*>(&scr.akk_t[s * 20 + 4 * c]);
+                const float xs = x[s];
+#pragma unroll
+                for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
+            }
+            // T' = T diag(beta): column r scaled by beta_r
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) sl.t_row[rr * C::LDK + r] = from_f<E>(x[rr] * br);
+            load_beta(m + C::NPW);
+            wave_lds_sync();
+            // publish T' of chunks inside the segment: lane (g, r) stores T'[r][4g .. 4g+3]
+            const Quad tq = ld_quad(&sl.t_row[r * C::LDK + 4 * g]);
+            const Rsrc rt = make_rsrc(ws_t + ((int64_t)bh * nchunks + m) * 256,
+                                      m < c1 ? 256u * (uint32_t)sizeof(E) : 0u);
+            buf_st_quad(tq, rt, (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E));
+        };
+
+        load(c0 + pw);
+        load_beta(c0 + pw);
+        // Retire the first chunk's loads before the loop: the compiler's
+        // wait-counter analysis would otherwise merge them with the loop's own
+        // prefetch and wait for everything at the top of every step.
+        __builtin_amdgcn_s_waitcnt(0);
+        for (int s = 0; s < nsteps; ++s) {
+            produce(c0 + s * C::NPW + pw, sm.slot[(s & 1) * C::NPW + pw]);
+            lds_barrier();
+        }
+        lds_barrier();   // the consumers' last step
+    } else {
+        // =================================================================== consumer
+        // state tiles: S[jj][t] = rows 16t.., columns 16*(wave + NCW*jj).. of [N | M]
+        f32x4 S[C::TPW][C::KT];
+#pragma unroll
+        for (int jj = 0; jj < C::TPW; ++jj) {
+            const int jt = wave + C::NCW * jj;
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S[jj][t][i] = (jt >= D / 16 && jt - D / 16 == t && 4 * g + i == r) ? 1.0f : 0.0f;
+        }
+
+        auto chain = [&](const Slot& sl) {
+            // Y = V - K+ S   (the M part of the widened state has V = 0)
+            f32x4 y[C::TPW];
+            BFrag sb[C::TPW * C::KT];
+#pragma unroll
+            for (int jj = 0; jj < C::TPW; ++jj) {
+                const int jt = wave + C::NCW * jj;
+#pragma unroll
+                for (int t = 0; t < C::KT; ++t) sb[jj * C::KT + t] = MM::to_b(S[jj][t]);
+                f32x4 yc = f32x4{0, 0, 0, 0};
+                if (jt < D / 16) {
+                    const auto vq = ld_quad(&sl.v_col[(16 * jt + r) * C::LDK + 4 * g]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yc[i] = to_f(vq[i]);
+                }
+                y[jj] = yc;
+            }
+            MM::template mm_la_n<D, C::TPW>(sl.kn_row, C::LDR, sb, y, C::TPW, r, g);
+            // U = T' Y
+            const PFrag tf = MM::pad(ld_quad(&sl.t_row[r * C::LDK + 4 * g]));
+            PFrag up[C::TPW];
+#pragma unroll
+            for (int jj = 0; jj < C::TPW; ++jj) up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(y[jj]), f32x4{0, 0, 0, 0}));
+            // fp32 operands are the state registers themselves: keep the update
+            // below from being scheduled into the products above, which would
+            // need a second copy of the state
+            if constexpr (sizeof(E) == 4) __builtin_amdgcn_sched_barrier(0);
+            // S <- Diag(Gamma_C) S + Kend^T U
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) {
+                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sl.gc[16 * t + 4 * g]);
+                const PFrag kf = MM::pad(ld_quad(&sl.ke_col[(16 * t + r) * C::LDK + 4 * g]));
+#pragma unroll
+                for (int jj = 0; jj < C::TPW; ++jj) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[jj][t][i] *= gcv[i];
+                    S[jj][t] = MM::mm16(kf, up[jj], S[jj][t]);
+                }
+            }
+        };
+
+        for (int s = 0; s <= nsteps; ++s) {
+            if (s > 0 && !last) {
+                // unrolled: a loop back-edge between two chunks would separate the
+                // state products of one from the reads of the next, and the
+                // compiler has been seen to under-count matrix-core wait states
+                // across back-edges
+#pragma unroll
+                for (int pp = 0; pp < C::NPW; ++pp) chain(sm.slot[((s - 1) & 1) * C::NPW + pp]);
+            }
+            lds_barrier();
+        }
+
+        if (!last) {
+#pragma unroll
+            for (int jj = 0; jj < C::TPW; ++jj) {
+                const int jt = wave + C::NCW * jj;
+#pragma unroll
+                for (int t = 0; t < C::KT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * t + 4 * g + i;
+                        ws_mn[(((int64_t)seg * BH + bh) * D + row) * (2 * D) + 16 * jt + r] = S[jj][t][i];
+                    }
+            }
+        }
+    }
+}
+
+template <typename E, int D>
+static hipError_t launch_map_t(int B, int H, int T, const SegPlan& p, const void* k, const void* v,
+                               const float* theta, const float* beta, float* ws_mn, void* ws_t,
+                               hipStream_t stream) {
+    typedef MapCfg<E, D> C;
+    const int BH = B * H;
+    hipLaunchKernelGGL((map_kernel<E, D>), dim3((unsigned)(BH * p.nseg)), dim3(64 * C::NW), 0, stream,
+                       T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)k, (const E*)v, theta, beta,
+                       ws_mn, (E*)ws_t);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan& plan, const void* k,
+                            const void* v, const float* theta, const float* beta, float* ws_mn,
+                            void* ws_t, hipStream_t stream) {
+#define KDA_MAP(E, D) return launch_map_t<E, D>(B, H, T, plan, k, v, theta, beta, ws_mn, ws_t, stream)
+    if (f32) {
+        switch (d) {
+            case 16: KDA_MAP(float, 16);
+            case 32: KDA_MAP(float, 32);
+            case 64: KDA_MAP(float, 64);
+            case 128: KDA_MAP(float, 128);
+        }
+    } else {
+        switch (d) {
+            case 16: KDA_MAP(bf16, 16);
+            case 32: KDA_MAP(bf16, 32);
+            case 64: KDA_MAP(bf16, 64);
+            case 128: KDA_MAP(bf16, 128);
+        }
+    }
+#undef KDA_MAP
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

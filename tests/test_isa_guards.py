@@ -48,7 +48,7 @@ def test_no_legacy_16x16x16_bf16_mfma(assembly, src):
 def test_matrix_cores_used_where_expected(assembly, src):
     text, _ = assembly[src]
     n = len(re.findall(r"^\s*v_mfma_f32_16x16x32_bf16", text, flags=re.M))
-    if src == "kda_chunk.hip":
+    if src in ("kda_chunk.hip", "kda_map.hip"):
         assert n > 0
     else:
         assert n == 0   # gate and decode are elementwise / bandwidth kernels
@@ -80,7 +80,7 @@ def test_no_spills_inside_loops(assembly, src):
     sizes = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", remarks)]
     assert sizes and max(sizes) <= 64, f"{src}: scratch use {max(sizes)} bytes/lane"
     bodies = _loop_bodies(text)
-    if src == "kda_chunk.hip":
+    if src in ("kda_chunk.hip", "kda_map.hip"):
         assert bodies, "the per-chunk loops were not found"
     per_fn = {}
     for fn, body in bodies:
@@ -89,3 +89,110 @@ def test_no_spills_inside_loops(assembly, src):
     # instructions; anything more means the kernel's registers no longer fit.
     bad = {fn: n for fn, n in per_fn.items() if n > 2}
     assert not bad, f"{src}: spills inside loops: {bad}"
+
+
+# ----------------------------------------------------------------------------- matrix-core result hazards
+# A matrix-core result must not be read before the instruction has retired; the
+# compiler inserts the wait states, and within a basic block it uses 8 for
+# 16x16x32 bf16 and 10 for 16x16x4 fp32 before a dependent read.  Across a
+# loop back-edge it has been seen to insert fewer (two, for an fp32 state
+# tile read right at the top of the next iteration), which returned stale
+# values.  This walks every control-flow path after each MFMA and checks the
+# distance to the first read of its result.
+_WAITS = {"16x16x32_bf16": 8, "16x16x4_f32": 10, "16x16x4f32": 10}
+
+
+def _regs(tok):
+    tok = tok.strip().rstrip(",")
+    m = re.match(r"^([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"^-?\|?([va])(\d+)\|?$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def _blocks(lines):
+    blocks, order, cur = {}, [], None
+    for l in lines:
+        m = re.match(r"^(\.LBB\d+_\d+):", l) or re.match(r"^; (%bb\.\d+):", l)
+        if m:
+            cur = m.group(1)
+            blocks[cur], order = [], order + [cur]
+            continue
+        s = l.split(";")[0].strip()
+        if s and not s.startswith(".") and cur is not None:
+            blocks[cur].append(s)
+    return blocks, order
+
+
+def _successors(blocks, order, b):
+    last = blocks[b][-1] if blocks[b] else ""
+    op = last.split()[0] if last else ""
+    if op == "s_branch":
+        return [last.split()[1]]
+    out = [last.split()[1]] if op.startswith("s_cbranch") else []
+    if op == "s_endpgm":
+        return out
+    i = order.index(b)
+    return out + ([order[i + 1]] if i + 1 < len(order) else [])
+
+
+def _reads(ins):
+    op = ins.split()[0]
+    ops = ins.split(None, 1)[1].split(",") if " " in ins else []
+    if op.startswith("v_mfma"):
+        return set().union(*(_regs(t) for t in ops[1:3])), _regs(ops[3])
+    first = 0 if re.match(r"(ds_write|global_store|buffer_store|scratch_store|flat_store)", op) else 1
+    if op.startswith(("v_", "ds_", "global_", "buffer_", "scratch_", "flat_")):
+        return set().union(set(), *(_regs(t) for t in ops[first:])), set()
+    return set(), set()
+
+
+def _early_reads(text):
+    found = []
+    for part in re.split(r"\n(?=_Z\S+:)", text):
+        m = re.match(r"(_Z\S+):", part)
+        if not m:
+            continue
+        blocks, order = _blocks(part[:part.find(".Lfunc_end")].split("\n"))
+        for b in order:
+            for idx, ins in enumerate(blocks[b]):
+                if not ins.startswith("v_mfma"):
+                    continue
+                need = next((n for k, n in _WAITS.items() if k in ins), 10)
+                dst = _regs(ins.split(None, 1)[1].split(",")[0])
+                stack, seen = [(b, idx + 1, 0)], set()
+                while stack:
+                    bb, i, ws = stack.pop()
+                    if (bb, i, ws) in seen or ws >= need:
+                        continue
+                    seen.add((bb, i, ws))
+                    if i >= len(blocks[bb]):
+                        stack += [(s, 0, ws) for s in _successors(blocks, order, bb) if s in blocks]
+                        continue
+                    x = blocks[bb][i]
+                    ab, c = _reads(x)
+                    # an accumulation into exactly the same registers is forwarded
+                    if ab & dst or (c and c != dst and c & dst):
+                        found.append(f"{m.group(1)[:50]} {b}: {ins[:40]} -> {bb}: {x[:40]} after {ws}")
+                        continue
+                    n = int(x.split()[1]) + 1 if x.startswith("s_nop") else 1
+                    stack.append((bb, i + 1, ws + n))
+    return found
+
+
+@pytest.mark.parametrize("src", HIP_SOURCES)
+def test_matrix_results_not_read_early(assembly, src):
+    text, _ = assembly[src]
+    bad = _early_reads(text)
+    assert not bad, f"{src}: matrix-core results read too early: {bad[:4]}"
+
+
+def test_early_read_check_finds_a_planted_case():
+    """The check itself: a fp32 result read two instructions after its
+    producer, through a loop back-edge, is reported; with a pad it is not."""
+    asm = ("_Zk:\n; %bb.0:\n.LBB0_1:\n\tv_mov_b32 v5, 0\n"
+           "\tv_mfma_f32_16x16x4_f32 a[0:3], v23, a3, a[4:7]\n\ts_cbranch_vccz .LBB0_1\n"
+           "; %bb.2:\n\ts_endpgm\n.Lfunc_end0:\n")
+    assert _early_reads(asm)
+    assert not _early_reads(asm.replace("\ts_cbranch_vccz", "\ts_nop 9\n\ts_cbranch_vccz"))
