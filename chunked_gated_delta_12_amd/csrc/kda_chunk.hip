@@ -530,27 +530,31 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 // Start state of every segment: S_0 = S0 (or 0), S_{s+1} = M_s S_s + N_s, where
 // [N_s | M_s] is the widened end state the map kernel stored for segment s.
 // Columns of the state are independent, so one workgroup owns one 16-column
-// tile of one head; its 4 wavefronts split the 16-row tiles of the product.
-// The column tile is shared through LDS (transposed, rounded to the operand
-// type) at every step; the rows of M_s and the N_s tile each wavefront needs
-// are fetched two steps ahead into a three-slot register ring.
+// tile of one head, and each of its wavefronts one 16-row tile of it.  The
+// column tile is shared through LDS (transposed, rounded to the operand type)
+// at every step; the row of M_s and the N_s tile a wavefront needs are fetched
+// two steps ahead into a three-slot register ring.  Every step runs the same
+// loads and stores: a fetch past the last map reads zeros and a store past the
+// last start state is dropped (buffer resources of size zero), so the loop
+// holds no conditional memory access that would make the compiler wait for the
+// prefetch.
 constexpr int COMBINE_XCDS = 8;   // accelerator complex dies of an MI355X
 
 template <typename E, int D>
 struct CombineCfg {
-    static constexpr int NW = 4, NTHR = 64 * NW;
     static constexpr int KT = D / 16, NT = D / 16;
-    static constexpr int RPW = (KT + NW - 1) / NW;   // row tiles per wavefront
+    static constexpr int NW = KT;                    // one wavefront per 16-row tile
     static constexpr int LDT = D + 8;                // padded row of the transposed tile
 };
 
 template <typename E, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * (D / 16))
 combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_mn,
                float* __restrict__ ws_start) {
     typedef CombineCfg<E, D> C;
     __shared__ alignas(16) E st[16 * C::LDT];   // st[col][row]: the state column tile
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int rt = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wavefront's row tile
     const int r = lane & 15, g = lane >> 4;
     // Workgroups are dealt to the 8 XCDs round-robin by index; all column tiles
     // of one head go to the same XCD so that its L2 serves the segment maps
@@ -558,88 +562,82 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
     const int xcd = blockIdx.x % COMBINE_XCDS, i = blockIdx.x / COMBINE_XCDS;
     const int bh = xcd + COMBINE_XCDS * (i / C::NT), jt = i % C::NT;
     if (bh >= BH) return;
+    const int nsteps = nseg - 1;
 
     struct Pref {
-        f32x4 m[C::RPW][C::KT];   // M rows 16rt + r, columns 16t + 4g .. +3
-        f32x4 n[C::RPW];          // N rows 16rt + 4g + i, column 16jt + r
+        f32x4 m[C::KT];   // M row 16rt + r, columns 16t + 4g .. +3
+        float n[4];       // N rows 16rt + 4g + i, column 16jt + r
     };
     auto fetch = [&](int s, Pref& pf) {
-        const float* X = ws_mn + ((int64_t)s * BH + bh) * D * (2 * D);   // [D][2D] = [N | M]
+        const Rsrc x = make_rsrc(ws_mn + ((int64_t)s * BH + bh) * D * (2 * D),
+                                 s < nsteps ? (uint32_t)(D * 2 * D * 4) : 0u);   // [D][2D] = [N | M]
 #pragma unroll
-        for (int k = 0; k < C::RPW; ++k) {
-            const int rt = min(wave + C::NW * k, C::KT - 1);
+        for (int t = 0; t < C::KT; ++t)
+            pf.m[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                x, (int)(((16 * rt + r) * (2 * D) + D + 16 * t + 4 * g) * 4), 0, 0));
 #pragma unroll
-            for (int t = 0; t < C::KT; ++t)
-                pf.m[k][t] = *reinterpret_cast<const f32x4*>(X + (int64_t)(16 * rt + r) * (2 * D) + D + 16 * t + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pf.n[k][i] = X[(int64_t)(16 * rt + 4 * g + i) * (2 * D) + 16 * jt + r];
-        }
+        for (int q = 0; q < 4; ++q)
+            pf.n[q] = __builtin_bit_cast(float, buf_ld32(x, (uint32_t)(((16 * rt + 4 * g + q) * (2 * D) + 16 * jt + r) * 4), 0u));
     };
-    auto publish = [&](int s, const f32x4* acc) {   // acc[k]: rows 16rt + 4g + i, column 16jt + r
-        float* dst = ws_start + ((int64_t)s * BH + bh) * D * D;
+    auto publish = [&](int s, f32x4 acc) {   // acc: rows 16rt + 4g + i, column 16jt + r
+        const Rsrc dst = make_rsrc(ws_start + ((int64_t)s * BH + bh) * D * D,
+                                   s <= nsteps ? (uint32_t)(D * D * 4) : 0u);
 #pragma unroll
-        for (int k = 0; k < C::RPW; ++k) {
-            const int rt = wave + C::NW * k;
-            if (rt >= C::KT) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * rt + 4 * g + i;
-                dst[(int64_t)row * D + 16 * jt + r] = acc[k][i];
-                st[r * C::LDT + row] = from_f<E>(acc[k][i]);
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int row = 16 * rt + 4 * g + q;
+            const float val = acc[q];   // (a bit cast of the vector element itself read element 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), dst,
+                                                  (int)((row * D + 16 * jt + r) * 4), 0, 0);
+            st[r * C::LDT + row] = from_f<E>(acc[q]);
         }
     };
 
-    f32x4 acc[C::RPW];
+    f32x4 acc;
 #pragma unroll
-    for (int k = 0; k < C::RPW; ++k) {
-        const int rt = min(wave + C::NW * k, C::KT - 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[k][i] = S0 ? S0[((int64_t)bh * D + 16 * rt + 4 * g + i) * D + 16 * jt + r] : 0.0f;
-    }
-    publish(0, acc);
-    const int nsteps = nseg - 1;
+    for (int q = 0; q < 4; ++q)
+        acc[q] = S0 ? S0[((int64_t)bh * D + 16 * rt + 4 * g + q) * D + 16 * jt + r] : 0.0f;
     Pref ring0, ring1, ring2;
-    if (nsteps > 0) fetch(0, ring0);
-    if (nsteps > 1) fetch(1, ring1);
+    fetch(0, ring0);
+    fetch(1, ring1);
+    publish(0, acc);
+    // Retire the loads above before the loop, so that the wait counting inside it
+    // only sees the loop's own prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
 
     // one step: S <- M_s S + N_s, using the prefetched slot `cur`, refilling `nxt2`
     auto step = [&](int s, const Pref& cur, Pref& nxt2) {
-        if (s + 2 < nsteps) fetch(s + 2, nxt2);
+        fetch(s + 2, nxt2);
+        f32x4 a = f32x4{cur.n[0], cur.n[1], cur.n[2], cur.n[3]};
+        if constexpr (sizeof(E) == 2) {   // bf16 operands, k-map of the accumulator-as-B form
+            if constexpr (D == 16) {
+                a = mfma_k16(Ops<bf16>::to_b(cur.m[0]), ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
+            } else {
 #pragma unroll
-        for (int k = 0; k < C::RPW; ++k) {
-            f32x4 a = cur.n[k];
-            if constexpr (sizeof(E) == 2) {   // bf16 operands, k-map of the accumulator-as-B form
-                if constexpr (D == 16) {
-                    a = mfma_k16(Ops<bf16>::to_b(cur.m[k][0]), ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
-                } else {
-#pragma unroll
-                    for (int kb = 0; kb < D / 32; ++kb) {
-                        const bf16* bp = (const bf16*)&st[r * C::LDT + 32 * kb + 4 * g];
-                        a = mfma_k32(cat8(Ops<bf16>::to_b(cur.m[k][2 * kb]), Ops<bf16>::to_b(cur.m[k][2 * kb + 1])),
-                                     cat8(ld_b4(bp), ld_b4(bp + 16)), a);
-                    }
-                }
-            } else {                          // fp32 operands: step (t, i) contracts row 16t + 4g + i
-#pragma unroll
-                for (int t = 0; t < C::KT; ++t) {
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(&st[r * C::LDT + 16 * t + 4 * g]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a = mfma_k4(cur.m[k][t][i], b[i], a);
+                for (int kb = 0; kb < D / 32; ++kb) {
+                    const bf16* bp = (const bf16*)&st[r * C::LDT + 32 * kb + 4 * g];
+                    a = mfma_k32(cat8(Ops<bf16>::to_b(cur.m[2 * kb]), Ops<bf16>::to_b(cur.m[2 * kb + 1])),
+                                 cat8(ld_b4(bp), ld_b4(bp + 16)), a);
                 }
             }
-            acc[k] = a;
+        } else {                          // fp32 operands: step (t, i) contracts row 16t + 4g + i
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) {
+                const f32x4 b = *reinterpret_cast<const f32x4*>(&st[r * C::LDT + 16 * t + 4 * g]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) a = mfma_k4(cur.m[t][q], b[q], a);
+            }
         }
         lds_barrier();              // every wavefront has read the old column tile
-        publish(s + 1, acc);
+        publish(s + 1, a);
         lds_barrier();
     };
+    // Whole rounds of three steps; the at most two steps past the last map read
+    // zeros and store nothing.
     for (int s = 0; s < nsteps; s += 3) {
         step(s, ring0, ring2);
-        if (s + 1 < nsteps) step(s + 1, ring1, ring0);
-        if (s + 2 < nsteps) step(s + 2, ring2, ring1);
+        step(s + 1, ring1, ring0);
+        step(s + 2, ring2, ring1);
     }
 }
 
@@ -686,7 +684,7 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
         if (e != hipSuccess) return e;
         const int heads_per_xcd = (BH + COMBINE_XCDS - 1) / COMBINE_XCDS;
         hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(COMBINE_XCDS * heads_per_xcd * (D / 16))),
-                           dim3(256), 0, stream,
+                           dim3(64 * (D / 16)), 0, stream,
                            BH, p.nseg,
                            S0, (const float*)ws_mn, ws_start);
     }

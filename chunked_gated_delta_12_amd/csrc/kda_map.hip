@@ -91,21 +91,6 @@ __device__ __forceinline__ void store_run8(E* p, const E* x) {
     }
 }
 
-// Four consecutive elements from LDS, in the register form Ops<E>::pad takes.
-__device__ __forceinline__ bf16x4 ld_quad(const bf16* p) { return ld_b4(p); }
-__device__ __forceinline__ f32x4 ld_quad(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-// Four consecutive elements to global memory through a buffer resource (a
-// store at or past the resource's size is dropped).
-__device__ __forceinline__ void buf_st_quad(bf16x4 x, Rsrc r, uint32_t voff) {
-    typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, (int)voff, 0, 0);
-}
-__device__ __forceinline__ void buf_st_quad(f32x4 x, Rsrc r, uint32_t voff) {
-    typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)voff, 0, 0);
-}
-
 template <typename E, int D>
 __global__ void __launch_bounds__((64 * MapCfg<E, D>::NW))
 map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,

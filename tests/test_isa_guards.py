@@ -138,14 +138,17 @@ def _successors(blocks, order, b):
 
 
 def _reads(ins):
+    """(srcA/srcB or plain vector reads, srcC reads, vector registers written)."""
     op = ins.split()[0]
     ops = ins.split(None, 1)[1].split(",") if " " in ins else []
     if op.startswith("v_mfma"):
-        return set().union(*(_regs(t) for t in ops[1:3])), _regs(ops[3])
-    first = 0 if re.match(r"(ds_write|global_store|buffer_store|scratch_store|flat_store)", op) else 1
+        return set().union(*(_regs(t) for t in ops[1:3])), _regs(ops[3]), _regs(ops[0])
+    store = re.match(r"(ds_write|global_store|buffer_store|scratch_store|flat_store)", op)
     if op.startswith(("v_", "ds_", "global_", "buffer_", "scratch_", "flat_")):
-        return set().union(set(), *(_regs(t) for t in ops[first:])), set()
-    return set(), set()
+        first = 0 if store else 1
+        written = set() if store else _regs(ops[0]) if ops else set()
+        return set().union(set(), *(_regs(t) for t in ops[first:])), set(), written
+    return set(), set(), set()
 
 
 def _early_reads(text):
@@ -160,24 +163,24 @@ def _early_reads(text):
                 if not ins.startswith("v_mfma"):
                     continue
                 need = next((n for k, n in _WAITS.items() if k in ins), 10)
-                dst = _regs(ins.split(None, 1)[1].split(",")[0])
-                stack, seen = [(b, idx + 1, 0)], set()
+                dst0 = frozenset(_regs(ins.split(None, 1)[1].split(",")[0]))
+                stack, seen = [(b, idx + 1, 0, dst0)], set()
                 while stack:
-                    bb, i, ws = stack.pop()
-                    if (bb, i, ws) in seen or ws >= need:
+                    bb, i, ws, dst = stack.pop()
+                    if (bb, i, ws, dst) in seen or ws >= need or not dst:
                         continue
-                    seen.add((bb, i, ws))
+                    seen.add((bb, i, ws, dst))
                     if i >= len(blocks[bb]):
-                        stack += [(s, 0, ws) for s in _successors(blocks, order, bb) if s in blocks]
+                        stack += [(s, 0, ws, dst) for s in _successors(blocks, order, bb) if s in blocks]
                         continue
                     x = blocks[bb][i]
-                    ab, c = _reads(x)
+                    ab, c, w = _reads(x)
                     # an accumulation into exactly the same registers is forwarded
-                    if ab & dst or (c and c != dst and c & dst):
+                    if ab & dst or (c and c != dst0 and c & dst):
                         found.append(f"{m.group(1)[:50]} {b}: {ins[:40]} -> {bb}: {x[:40]} after {ws}")
                         continue
                     n = int(x.split()[1]) + 1 if x.startswith("s_nop") else 1
-                    stack.append((bb, i + 1, ws + n))
+                    stack.append((bb, i + 1, ws + n, dst - frozenset(w)))
     return found
 
 
