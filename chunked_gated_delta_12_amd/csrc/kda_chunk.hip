@@ -17,22 +17,23 @@
 // A chunk maps the state affinely, S' = M S + N (M = Diag(Gamma_C) - Kend^T W,
 // N = Kend^T Ut).  To expose parallelism beyond batch*heads, each sequence is
 // cut into segments of whole chunks:
-//   map kernel     one workgroup per (segment but the last, head): runs the
+//   map kernel     (kda_map.hip) one workgroup per (segment, head): runs the
 //                  chunk scan over its segment with the state widened to
-//                  [N | M], started from [0 | I], and stores the result;
-//   combine kernel one workgroup per head: start state of every segment,
-//                  S_{s+1} = M_s S_s + N_s (sequential over segments);
+//                  [N | M], started from [0 | I], stores the result and
+//                  publishes every chunk's T' = T diag(beta);
+//   combine kernel start state of every segment, S_{s+1} = M_s S_s + N_s
+//                  (sequential over segments);
 //   out kernel     one workgroup per (segment, head): the chunk scan from the
 //                  segment's true start state, writing o (and S_T for the
 //                  last segment).
-// With one segment only the out kernel runs, straight from S0.
+// With one segment only the out kernel runs, straight from S0, and solves for
+// T itself.
 //
-// Workgroups of 4 (out kernel, two workgroups per compute unit) or 8 (map
-// kernel, which carries the twice-as-wide state) wavefronts.  Per chunk: the gate and all
-// decay-scaled operand tiles are formed once in LDS; A, T, W are shared by the
-// workgroup; the state columns are split into 16-column tiles across the
-// wavefronts, each tile living in fp32 accumulator registers for the whole
-// segment.  The next chunk's inputs are loaded while the current one is being
+// The out kernel runs workgroups of 4 wavefronts, two per compute unit.  Per
+// chunk: the gate and all decay-scaled operand tiles are formed once in LDS;
+// A and T are shared by the workgroup; the state columns are split into
+// 16-column tiles across the wavefronts, each tile living in fp32 accumulator
+// registers for the whole segment.  The next chunk's inputs are loaded while the current one is being
 // processed, and each chunk's o tile is written out during the next chunk.  All products
 // are 16x16 matrix-core tiles (bf16 operands, fp32 accumulation; fp32
 // operands in the validation dtype).
@@ -43,11 +44,11 @@
 
 namespace kda {
 
-template <int D, bool MAP, int NW_>
+template <int D, int NW_>
 struct ChunkCfg {
     static constexpr int NW = NW_;                 // wavefronts per workgroup
     static constexpr int NTHR = 64 * NW;
-    static constexpr int NCOL = MAP ? 2 * D : D;   // state columns carried
+    static constexpr int NCOL = D;                 // state columns carried
     static constexpr int NT = NCOL / 16;           // 16-column tiles
     static constexpr int TPW = (NT + NW - 1) / NW; // tiles per wavefront (max)
     static constexpr int KT = D / 16;              // 16-row tiles along d_k
@@ -65,18 +66,18 @@ struct ChunkCfg {
     static_assert(PPT == 1 || PPT == 2 || PPT == 4, "gate stage column writes");
 };
 
-template <typename E, int D, bool MAP, int NW>
+template <typename E, int D, int NW>
 struct ChunkSmem {
-    typedef ChunkCfg<D, MAP, NW> C;
+    typedef ChunkCfg<D, NW> C;
     static constexpr int LDP = Ops<E>::PAD_ROW;    // padded K = 16 operand rows
     alignas(16) E kn_row[16 * C::LDR];             // -K+ = -K*Gamma           [token][ch]
     alignas(16) E km_row[16 * C::LDR];             // K- = K/Gamma             [token][ch]
-    alignas(16) E qp_row[MAP ? 8 : 16 * C::LDR];   // Q+ = Q*Gamma             [token][ch]
-    alignas(16) E o_tile[MAP ? 8 : 16 * C::LDR];   // o of the chunk           [token][col]
+    alignas(16) E qp_row[16 * C::LDR];             // Q+ = Q*Gamma             [token][ch]
+    alignas(16) E o_tile[16 * C::LDR];             // o of the chunk           [token][col]
     alignas(16) E ke_pad[D * LDP];                 // Kend^T, padded           [ch][token]
     alignas(16) E v_col[D * C::LDC];               // V^T                      [col][token]
     alignas(16) E t_pad[16 * LDP];                 // T = (I + A)^-1, padded   [token][token]
-    alignas(16) E aqk_pad[MAP ? 8 : 16 * LDP];     // LowerIncl(Q+K-^T), padded [token][token]
+    alignas(16) E aqk_pad[16 * LDP];               // LowerIncl(Q+K-^T), padded [token][token]
     alignas(16) float akk_t[16 * 20];              // StrictLower(beta K+ K-^T)^T, fp32
     alignas(16) float gc[D];                       // Gamma_C per channel
 };
@@ -122,20 +123,17 @@ __device__ __forceinline__ void store_pair_runs(E* pa, E* pb, const typename Pai
     *reinterpret_cast<V*>(pb) = b;
 }
 
-// MAP: the map kernel (one workgroup per segment and head; widened state; it
-// also stores every chunk's T = (I + A)^-1 to ws_t, and the last segment's
-// workgroups exist only for that).  TWS: the out kernel reads T from ws_t
-// instead of forming A and solving for T itself.
-template <typename E, int D, bool MAP, int NW, bool TWS>
+// TWS: several segments; the kernel reads each chunk's T' = T diag(beta) from
+// ws_t (published by the map kernel) instead of forming A and solving for T.
+template <typename E, int D, int NW, bool TWS>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
              const float* __restrict__ theta, const float* __restrict__ beta,
-             const float* S0, const float* __restrict__ ws_start, float* __restrict__ ws_mn,
-             E* ws_t, E* __restrict__ o, float* S_T) {
-    static_assert(!(MAP && TWS), "the map kernel forms T itself");
-    typedef ChunkCfg<D, MAP, NW> C;
-    typedef ChunkSmem<E, D, MAP, NW> SM;
+             const float* S0, const float* __restrict__ ws_start,
+             const E* ws_t, E* __restrict__ o, float* S_T) {
+    typedef ChunkCfg<D, NW> C;
+    typedef ChunkSmem<E, D, NW> SM;
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
     typedef typename MM::PFrag PFrag;
@@ -164,14 +162,14 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     for (int i = tid; i < D * LDP; i += C::NTHR) sm.ke_pad[i] = from_f<E>(0.0f);
     for (int i = tid; i < 16 * LDP; i += C::NTHR) {
         sm.t_pad[i] = from_f<E>(0.0f);
-        if constexpr (!MAP) sm.aqk_pad[i] = from_f<E>(0.0f);
+        sm.aqk_pad[i] = from_f<E>(0.0f);
     }
 
     // ---- state tiles: S[jj][t] = rows 16t.., columns 16*(wave + NW*jj)..
     f32x4 S[C::TPW][C::KT];
     const float* src = nullptr;
-    if constexpr (!MAP) src = ws_start ? ws_start + ((int64_t)seg * BH + bh) * D * D
-                                       : (S0 ? S0 + (int64_t)bh * D * D : nullptr);
+    src = ws_start ? ws_start + ((int64_t)seg * BH + bh) * D * D
+                   : (S0 ? S0 + (int64_t)bh * D * D : nullptr);
 #pragma unroll
     for (int jj = 0; jj < C::TPW; ++jj) {
         const int jt = wave + C::NW * jj;
@@ -181,11 +179,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * t + 4 * g + i;
                 float x = 0.0f;
-                if constexpr (MAP) {
-                    if (jt >= D / 16 && jt - D / 16 == t && 4 * g + i == r) x = 1.0f;
-                } else {
-                    if (src && jt < C::NT) x = src[(int64_t)row * D + 16 * jt + r];
-                }
+                if (src && jt < C::NT) x = src[(int64_t)row * D + 16 * jt + r];
                 S[jj][t][i] = x;
             }
         }
@@ -235,7 +229,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         for (int p = 0; p < C::PPT; ++p) {
             d.th[p] = buf_ld_f2(rth, el_off[p] * 4u, 0u);
             d.k[p] = BufPair<E>::ld(rk, el_off[p] * (uint32_t)sizeof(E), 0u);
-            if constexpr (!MAP) d.q[p] = BufPair<E>::ld(rq, el_off[p] * (uint32_t)sizeof(E), 0u);
+            d.q[p] = BufPair<E>::ld(rq, el_off[p] * (uint32_t)sizeof(E), 0u);
             d.v[p] = BufPair<E>::ld(rv, el_off[p] * (uint32_t)sizeof(E), 0u);
         }
     };
@@ -328,11 +322,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 const float eGa = __builtin_amdgcn_exp2f(Ga), eGb = __builtin_amdgcn_exp2f(Gb);
                 const float emGa = __builtin_amdgcn_exp2f(-Ga), emGb = __builtin_amdgcn_exp2f(-Gb);
                 float ka = to_f(cur.k[p][0]), kb = to_f(cur.k[p][1]);
-                float qa = 0.0f, qb = 0.0f;
-                if constexpr (!MAP) {
-                    qa = to_f(cur.q[p][0]);
-                    qb = to_f(cur.q[p][1]);
-                }
+                float qa = to_f(cur.q[p][0]), qb = to_f(cur.q[p][1]);
                 vr[p] = cur.v[p];
                 if (PARTIAL && !(t0 + pos < T)) {   // padding token: k = q = v = 0
                     ka = kb = qa = qb = 0.0f;
@@ -343,7 +333,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 keb[p] = kmb * eC1;
                 store_pair(&sm.kn_row[pos * C::LDR + ch], -ka * eGa, -kb * eGb);
                 store_pair(&sm.km_row[pos * C::LDR + ch], kma, kmb);
-                if constexpr (!MAP) store_pair(&sm.qp_row[pos * C::LDR + ch], qa * eGa, qb * eGb);
+                store_pair(&sm.qp_row[pos * C::LDR + ch], qa * eGa, qb * eGb);
             }
             const int pos0 = pgi * C::PPT;
             const int kp = 8 * (pos0 >> 2) + (pos0 & 3);   // padded slot of token pos0
@@ -351,8 +341,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             store_run<E, C::PPT>(&sm.ke_pad[(ch + 1) * LDP + kp], keb);
             store_pair_runs<E, C::PPT>(&sm.v_col[ch * C::LDC + pos0], &sm.v_col[(ch + 1) * C::LDC + pos0], vr);
         }
-        if constexpr (!MAP)
-            if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
+        if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
         if (n + PFD < c1) load_chunk(n + PFD, cur);   // in flight until that chunk's gate stage
         lds_barrier();
 
@@ -372,7 +361,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 #pragma unroll
             for (int i = 0; i < 4; ++i) m[i] = (r < 4 * g + i) ? -btv[i] * a[i] : 0.0f;   // mask by select
             *reinterpret_cast<f32x4*>(&sm.akk_t[r * 20 + 4 * g]) = m;
-        } else if (!MAP && wave == (TWS ? 0 : 1)) {
+        } else if (wave == (TWS ? 0 : 1)) {
             // A_qk^T = K- Q+^T; lane (g, r) holds A_qk[r][4g+i], i.e. four
             // consecutive k-slots of row r of the padded tile
             const f32x4 a = MM::template mm_ll<D>(sm.km_row, C::LDR, sm.qp_row, C::LDR,
@@ -401,7 +390,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             o1[jj] = f32x4{0, 0, 0, 0};
         }
         MM::template mm_la_n<D, C::TPW>(sm.kn_row, C::LDR, sb, y, nv, r, g);
-        if constexpr (!MAP) MM::template mm_al_n<D, C::TPW>(sb, sm.qp_row, C::LDR, o1, nv, r, g);
+        MM::template mm_al_n<D, C::TPW>(sb, sm.qp_row, C::LDR, o1, nv, r, g);
         // The products above are issued before the solve starts (matrix cores
         // run them while the solve proceeds); keeping the two apart in the
         // instruction stream also keeps their registers from being live at once.
@@ -438,18 +427,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             PFrag tf;
             if constexpr (TWS) tf = MM::pad(t_l);
             else tf = MM::ld_p(&sm.t_pad[r * LDP], g);
-            if constexpr (MAP) {
-                // publish T of this chunk for the out kernel: lane (g, r) holds T[r][4g .. 4g+3]
-                if (wave == C::NW - 1) {
-                    typedef E V4 __attribute__((__vector_size__(4 * sizeof(E))));
-                    V4 tv;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) tv[i] = sm.t_pad[r * LDP + 8 * g + i];
-                    *reinterpret_cast<V4*>(ws_t + ((int64_t)bh * nchunks + n) * 256 + r * 16 + 4 * g) = tv;
-                }
-            }
             PFrag qf;
-            if constexpr (!MAP) qf = MM::ld_p(&sm.aqk_pad[r * LDP], g);
+            qf = MM::ld_p(&sm.aqk_pad[r * LDP], g);
 #pragma unroll
             for (int jj = 0; jj < C::TPW; ++jj) {
                 if (jj >= nv) continue;
@@ -460,11 +439,9 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                     for (int i = 0; i < 4; ++i) yy[i] *= btv[i];
                 }
                 up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(yy), f32x4{0, 0, 0, 0}));
-                if constexpr (!MAP) {
-                    // O^T = O1^T + U^T A_qk^T: lane (g, r) holds o[token r][16jt + 4g + i]
-                    const f32x4 ot = MM::mm16(up[jj], qf, o1[jj]);
-                    store4<E>(&sm.o_tile[r * C::LDR + 16 * jt + 4 * g], ot);
-                }
+                // O^T = O1^T + U^T A_qk^T: lane (g, r) holds o[token r][16jt + 4g + i]
+                const f32x4 ot = MM::mm16(up[jj], qf, o1[jj]);
+                store4<E>(&sm.o_tile[r * C::LDR + 16 * jt + 4 * g], ot);
             }
         }
         if (n + 1 < c1) load_late(n + 1);   // T and beta are no longer needed for this chunk
@@ -505,7 +482,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         if (PFD == 2 && ((c_full - c0) & 1)) chunk(std::true_type{}, c_full, pb);
         else chunk(std::true_type{}, c_full, pa);
     }
-    if constexpr (!MAP) store_o(c1 - 1, true);
+    store_o(c1 - 1, true);
 
     // ---- write the segment's final state
 #pragma unroll
@@ -517,18 +494,16 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * t + 4 * g + i;
-                if constexpr (MAP) {
-                    if (seg < nseg - 1) ws_mn[(((int64_t)seg * BH + bh) * D + row) * (2 * D) + 16 * jt + r] = S[jj][t][i];
-                } else {
-                    if (S_T && seg == nseg - 1)
-                        S_T[((int64_t)bh * D + row) * D + 16 * jt + r] = S[jj][t][i];
-                }
+                if (S_T && seg == nseg - 1)
+                    S_T[((int64_t)bh * D + row) * D + 16 * jt + r] = S[jj][t][i];
             }
     }
 }
 
 // Start state of every segment: S_0 = S0 (or 0), S_{s+1} = M_s S_s + N_s, where
-// [N_s | M_s] is the widened end state the map kernel stored for segment s.
+// [N_s | M_s] is the widened end state the map kernel stored for segment s (N_s
+// in fp32, M_s in the operand type: every step streams all of M_s through the
+// compute unit, so its size sets the pace).
 // Columns of the state are independent, so one workgroup owns one 16-column
 // tile of one head, and each of its wavefronts one 16-row tile of it.  The
 // column tile is shared through LDS (transposed, rounded to the operand type)
@@ -549,8 +524,8 @@ struct CombineCfg {
 
 template <typename E, int D>
 __global__ void __launch_bounds__(64 * (D / 16))
-combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_mn,
-               float* __restrict__ ws_start) {
+combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_n,
+               const E* __restrict__ ws_m, float* __restrict__ ws_start) {
     typedef CombineCfg<E, D> C;
     __shared__ alignas(16) E st[16 * C::LDT];   // st[col][row]: the state column tile
     const int tid = threadIdx.x, lane = tid & 63;
@@ -564,20 +539,40 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
     if (bh >= BH) return;
     const int nsteps = nseg - 1;
 
+    // M row 16rt + r as operand fragments: bf16, per 32-column block kb, columns
+    // 32kb + 4g .. +3 and 32kb + 16 + 4g .. +3 (the k-map of Ops<bf16>::mm_la);
+    // fp32, per 16-column tile t, columns 16t + 4g .. +3
+    constexpr bool BF = sizeof(E) == 2;
+    constexpr int NMF = BF ? (D >= 32 ? D / 32 : 1) : C::KT;
+    typedef typename std::conditional<BF, bf16x8, f32x4>::type MFrag;
     struct Pref {
-        f32x4 m[C::KT];   // M row 16rt + r, columns 16t + 4g .. +3
+        MFrag m[NMF];
         float n[4];       // N rows 16rt + 4g + i, column 16jt + r
     };
     auto fetch = [&](int s, Pref& pf) {
-        const Rsrc x = make_rsrc(ws_mn + ((int64_t)s * BH + bh) * D * (2 * D),
-                                 s < nsteps ? (uint32_t)(D * 2 * D * 4) : 0u);   // [D][2D] = [N | M]
+        const bool in = s < nsteps;
+        const Rsrc xn = make_rsrc(ws_n + ((int64_t)s * BH + bh) * D * D, in ? (uint32_t)(D * D * 4) : 0u);
+        const Rsrc xm = make_rsrc(ws_m + ((int64_t)s * BH + bh) * D * D, in ? (uint32_t)(D * D * sizeof(E)) : 0u);
+        const uint32_t row = (uint32_t)(16 * rt + r) * D;
+        if constexpr (BF) {
+            if constexpr (D == 16) {
+                const bf16x4 lo = BufQuad<bf16>::ld(xm, (row + 4 * g) * 2u, 0u);
+                pf.m[0] = cat8(lo, lo);   // upper half unused (K = 16)
+            } else {
 #pragma unroll
-        for (int t = 0; t < C::KT; ++t)
-            pf.m[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                x, (int)(((16 * rt + r) * (2 * D) + D + 16 * t + 4 * g) * 4), 0, 0));
+                for (int kb = 0; kb < D / 32; ++kb)
+                    pf.m[kb] = cat8(BufQuad<bf16>::ld(xm, (row + 32 * kb + 4 * g) * 2u, 0u),
+                                    BufQuad<bf16>::ld(xm, (row + 32 * kb + 16 + 4 * g) * 2u, 0u));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t)
+                pf.m[t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    xm, (int)((row + 16 * t + 4 * g) * 4), 0, 0));
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            pf.n[q] = __builtin_bit_cast(float, buf_ld32(x, (uint32_t)(((16 * rt + 4 * g + q) * (2 * D) + 16 * jt + r) * 4), 0u));
+            pf.n[q] = __builtin_bit_cast(float, buf_ld32(xn, (uint32_t)(((16 * rt + 4 * g + q) * D + 16 * jt + r) * 4), 0u));
     };
     auto publish = [&](int s, f32x4 acc) {   // acc: rows 16rt + 4g + i, column 16jt + r
         const Rsrc dst = make_rsrc(ws_start + ((int64_t)s * BH + bh) * D * D,
@@ -607,17 +602,21 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
 
     // one step: S <- M_s S + N_s, using the prefetched slot `cur`, refilling `nxt2`
     auto step = [&](int s, const Pref& cur, Pref& nxt2) {
+        // Keep each step's instructions in its own step: converting the next
+        // step's rows early would wait for a fetch issued only one step before.
+        __builtin_amdgcn_sched_barrier(0);
         fetch(s + 2, nxt2);
         f32x4 a = f32x4{cur.n[0], cur.n[1], cur.n[2], cur.n[3]};
-        if constexpr (sizeof(E) == 2) {   // bf16 operands, k-map of the accumulator-as-B form
+        if constexpr (BF) {   // bf16 operands, k-map of the accumulator-as-B form
             if constexpr (D == 16) {
-                a = mfma_k16(Ops<bf16>::to_b(cur.m[0]), ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
+                const bf16x8 mf = cur.m[0];
+                a = mfma_k16(__builtin_shufflevector(mf, mf, 0, 1, 2, 3),
+                             ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
             } else {
 #pragma unroll
                 for (int kb = 0; kb < D / 32; ++kb) {
                     const bf16* bp = (const bf16*)&st[r * C::LDT + 32 * kb + 4 * g];
-                    a = mfma_k32(cat8(Ops<bf16>::to_b(cur.m[2 * kb]), Ops<bf16>::to_b(cur.m[2 * kb + 1])),
-                                 cat8(ld_b4(bp), ld_b4(bp + 16)), a);
+                    a = mfma_k32(cur.m[kb], cat8(ld_b4(bp), ld_b4(bp + 16)), a);
                 }
             }
         } else {                          // fp32 operands: step (t, i) contracts row 16t + 4g + i
@@ -631,6 +630,7 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_m
         lds_barrier();              // every wavefront has read the old column tile
         publish(s + 1, a);
         lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
     };
     // Whole rounds of three steps; the at most two steps past the last map read
     // zeros and store nothing.
@@ -664,7 +664,6 @@ size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg, int nchunks
 // Wavefronts per workgroup: four, so that two workgroups share a compute unit
 // and one's gate/solve phases overlap the other's matrix-core phases.
 constexpr int CHUNK_NW_OUT = 4;
-constexpr int CHUNK_NW_MAP = 8;
 
 template <typename E, int D>
 static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const void* q,
@@ -672,32 +671,33 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
                                  const float* beta, const float* S0, void* o, float* S_T,
                                  void* workspace, hipStream_t stream) {
     const int BH = B * H;
-    float* ws_mn = nullptr;
     float* ws_start = nullptr;
     E* ws_t = nullptr;
     if (p.nseg > 1) {
-        ws_mn = reinterpret_cast<float*>(workspace);
-        ws_start = ws_mn + (size_t)(p.nseg - 1) * BH * D * (2 * D);
+        // segment maps: N (fp32) then M (input type, in a region sized for fp32)
+        float* ws_n = reinterpret_cast<float*>(workspace);
+        E* ws_m = reinterpret_cast<E*>(ws_n + (size_t)(p.nseg - 1) * BH * D * D);
+        ws_start = ws_n + (size_t)(p.nseg - 1) * BH * D * (2 * D);
         ws_t = reinterpret_cast<E*>(ws_start + (size_t)p.nseg * BH * D * D);
         const hipError_t e = launch_chunk_map(std::is_same<E, float>::value, B, T, H, D, p, k, v, theta,
-                                              beta, ws_mn, ws_t, stream);
+                                              beta, ws_n, ws_m, ws_t, stream);
         if (e != hipSuccess) return e;
         const int heads_per_xcd = (BH + COMBINE_XCDS - 1) / COMBINE_XCDS;
         hipLaunchKernelGGL((combine_kernel<E, D>), dim3((unsigned)(COMBINE_XCDS * heads_per_xcd * (D / 16))),
                            dim3(64 * (D / 16)), 0, stream,
                            BH, p.nseg,
-                           S0, (const float*)ws_mn, ws_start);
+                           S0, (const float*)ws_n, (const E*)ws_m, ws_start);
     }
     if (p.nseg > 1)
-        hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT, true>), dim3((unsigned)(BH * p.nseg)),
+        hipLaunchKernelGGL((chunk_kernel<E, D, CHUNK_NW_OUT, true>), dim3((unsigned)(BH * p.nseg)),
                            dim3(64 * CHUNK_NW_OUT), 0, stream, T,
                            H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
-                           beta, S0, (const float*)ws_start, (float*)nullptr, ws_t, (E*)o, S_T);
+                           beta, S0, (const float*)ws_start, (const E*)ws_t, (E*)o, S_T);
     else
-        hipLaunchKernelGGL((chunk_kernel<E, D, false, CHUNK_NW_OUT, false>), dim3((unsigned)BH),
+        hipLaunchKernelGGL((chunk_kernel<E, D, CHUNK_NW_OUT, false>), dim3((unsigned)BH),
                            dim3(64 * CHUNK_NW_OUT), 0, stream, T,
                            H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
-                           beta, S0, (const float*)nullptr, (float*)nullptr, (E*)nullptr, (E*)o, S_T);
+                           beta, S0, (const float*)nullptr, (const E*)nullptr, (E*)o, S_T);
     return hipGetLastError();
 }
 

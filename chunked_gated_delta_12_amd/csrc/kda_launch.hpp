@@ -29,11 +29,11 @@ hipError_t launch_decode(bool f32, int B, int H, int d, const void* q, const voi
                          hipStream_t stream);
 
 // Segment map kernel of the chunked prefill: the widened end state [N | M] of
-// every segment but the last into ws_mn, T' = (I + A)^-1 diag(beta) of every
-// chunk into ws_t.
+// every segment but the last (N fp32 into ws_n, M in the input type into ws_m,
+// both [segment][head][d_k][d]), T' = (I + A)^-1 diag(beta) of every chunk into ws_t.
 hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan& plan, const void* k,
-                            const void* v, const float* theta, const float* beta, float* ws_mn,
-                            void* ws_t, hipStream_t stream);
+                            const void* v, const float* theta, const float* beta, float* ws_n,
+                            void* ws_m, void* ws_t, hipStream_t stream);
 
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,

@@ -4,7 +4,8 @@
 // Problem: The Diagonal-Block Dilemma" gives the chunk form; see kda_chunk.hip
 // for the algebra).  For every segment but the last, this kernel runs the chunk
 // scan with the state widened to [N | M], started from [0 | I], and stores the
-// end state.  For every chunk of every segment it also publishes
+// end state (N in fp32, M in the operand type).  For every chunk of every
+// segment it also publishes
 //     T' = (I + A)^-1 diag(beta),   A = StrictLower(diag(beta) K+ K-^T),
 // so that the out kernel forms U = T' (V - K+ S) without a triangular solve.
 //
@@ -95,7 +96,8 @@ template <typename E, int D>
 __global__ void __launch_bounds__((64 * MapCfg<E, D>::NW))
 map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
            const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ theta,
-           const float* __restrict__ beta, float* __restrict__ ws_mn, E* __restrict__ ws_t) {
+           const float* __restrict__ beta, float* __restrict__ ws_n, E* __restrict__ ws_m,
+           E* __restrict__ ws_t) {
     typedef MapCfg<E, D> C;
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
@@ -350,7 +352,10 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = 16 * t + 4 * g + i;
-                        ws_mn[(((int64_t)seg * BH + bh) * D + row) * (2 * D) + 16 * jt + r] = S[jj][t][i];
+                        const int64_t rb = (((int64_t)seg * BH + bh) * D + row) * D;
+                        // N in fp32; M already in the operand type the combine kernel uses
+                        if (jt < D / 16) ws_n[rb + 16 * jt + r] = S[jj][t][i];
+                        else ws_m[rb + 16 * (jt - D / 16) + r] = from_f<E>(S[jj][t][i]);
                     }
             }
         }
@@ -359,20 +364,20 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
 template <typename E, int D>
 static hipError_t launch_map_t(int B, int H, int T, const SegPlan& p, const void* k, const void* v,
-                               const float* theta, const float* beta, float* ws_mn, void* ws_t,
+                               const float* theta, const float* beta, float* ws_n, void* ws_m, void* ws_t,
                                hipStream_t stream) {
     typedef MapCfg<E, D> C;
     const int BH = B * H;
     hipLaunchKernelGGL((map_kernel<E, D>), dim3((unsigned)(BH * p.nseg)), dim3(64 * C::NW), 0, stream,
                        T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)k, (const E*)v, theta, beta,
-                       ws_mn, (E*)ws_t);
+                       ws_n, (E*)ws_m, (E*)ws_t);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan& plan, const void* k,
-                            const void* v, const float* theta, const float* beta, float* ws_mn,
+                            const void* v, const float* theta, const float* beta, float* ws_n, void* ws_m,
                             void* ws_t, hipStream_t stream) {
-#define KDA_MAP(E, D) return launch_map_t<E, D>(B, H, T, plan, k, v, theta, beta, ws_mn, ws_t, stream)
+#define KDA_MAP(E, D) return launch_map_t<E, D>(B, H, T, plan, k, v, theta, beta, ws_n, ws_m, ws_t, stream)
     if (f32) {
         switch (d) {
             case 16: KDA_MAP(float, 16);
