@@ -520,6 +520,12 @@ struct CombineCfg {
     static constexpr int KT = D / 16, NT = D / 16;
     static constexpr int NW = KT;                    // one wavefront per 16-row tile
     static constexpr int LDT = D + 8;                // padded row of the transposed tile
+    // bf16: a wavefront's 16 rows of M_s are one contiguous block of 32D bytes,
+    // fetched with whole-wavefront 16-byte loads and laid out as operand
+    // fragments through the wavefront's own LDS rows
+    static constexpr int MB = 16 * D * 2;            // bytes of the block
+    static constexpr int NML = MB >= 1024 ? MB / 1024 : 1;   // 16-byte loads per lane
+    static constexpr int LDM = D + 8;                // padded LDS row of the block
 };
 
 template <typename E, int D>
@@ -528,6 +534,8 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_n
                const E* __restrict__ ws_m, float* __restrict__ ws_start) {
     typedef CombineCfg<E, D> C;
     __shared__ alignas(16) E st[16 * C::LDT];   // st[col][row]: the state column tile
+    // each wavefront's rows of M_s (bf16 only)
+    __shared__ alignas(16) E mw[sizeof(E) == 2 ? C::NW * 16 * C::LDM : 8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int rt = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wavefront's row tile
     const int r = lane & 15, g = lane >> 4;
@@ -545,8 +553,10 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_n
     constexpr bool BF = sizeof(E) == 2;
     constexpr int NMF = BF ? (D >= 32 ? D / 32 : 1) : C::KT;
     typedef typename std::conditional<BF, bf16x8, f32x4>::type MFrag;
+    typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
     struct Pref {
-        MFrag m[NMF];
+        // bf16: the raw block, 16 bytes per lane per load; fp32: operand fragments
+        typename std::conditional<BF, u32x4, MFrag>::type m[BF ? C::NML : NMF];
         float n[4];       // N rows 16rt + 4g + i, column 16jt + r
     };
     auto fetch = [&](int s, Pref& pf) {
@@ -555,15 +565,11 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_n
         const Rsrc xm = make_rsrc(ws_m + ((int64_t)s * BH + bh) * D * D, in ? (uint32_t)(D * D * sizeof(E)) : 0u);
         const uint32_t row = (uint32_t)(16 * rt + r) * D;
         if constexpr (BF) {
-            if constexpr (D == 16) {
-                const bf16x4 lo = BufQuad<bf16>::ld(xm, (row + 4 * g) * 2u, 0u);
-                pf.m[0] = cat8(lo, lo);   // upper half unused (K = 16)
-            } else {
+            const uint32_t blk = (uint32_t)(16 * rt) * D * 2u;   // this wavefront's rows
 #pragma unroll
-                for (int kb = 0; kb < D / 32; ++kb)
-                    pf.m[kb] = cat8(BufQuad<bf16>::ld(xm, (row + 32 * kb + 4 * g) * 2u, 0u),
-                                    BufQuad<bf16>::ld(xm, (row + 32 * kb + 16 + 4 * g) * 2u, 0u));
-            }
+            for (int i = 0; i < C::NML; ++i)
+                pf.m[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    xm, (int)(blk + (uint32_t)(i * 64 + lane) * 16u), 0, 0));
         } else {
 #pragma unroll
             for (int t = 0; t < C::KT; ++t)
@@ -608,15 +614,23 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_n
         fetch(s + 2, nxt2);
         f32x4 a = f32x4{cur.n[0], cur.n[1], cur.n[2], cur.n[3]};
         if constexpr (BF) {   // bf16 operands, k-map of the accumulator-as-B form
+            // the raw block into this wavefront's LDS rows, then row r as fragments
+            bf16* mwv = (bf16*)&mw[rt * 16 * C::LDM];
+#pragma unroll
+            for (int i = 0; i < C::NML; ++i) {
+                const int e = (i * 64 + lane) * 8;        // element offset in the block
+                if (C::MB >= 1024 || e < 16 * D)
+                    *reinterpret_cast<u32x4*>(&mwv[(e / D) * C::LDM + e % D]) = cur.m[i];
+            }
+            wave_lds_sync();
             if constexpr (D == 16) {
-                const bf16x8 mf = cur.m[0];
-                a = mfma_k16(__builtin_shufflevector(mf, mf, 0, 1, 2, 3),
-                             ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
+                a = mfma_k16(ld_b4(&mwv[r * C::LDM + 4 * g]), ld_b4((const bf16*)&st[r * C::LDT + 4 * g]), a);
             } else {
 #pragma unroll
                 for (int kb = 0; kb < D / 32; ++kb) {
+                    const bf16* mp = &mwv[r * C::LDM + 32 * kb + 4 * g];
                     const bf16* bp = (const bf16*)&st[r * C::LDT + 32 * kb + 4 * g];
-                    a = mfma_k32(cur.m[kb], cat8(ld_b4(bp), ld_b4(bp + 16)), a);
+                    a = mfma_k32(cat8(ld_b4(mp), ld_b4(mp + 16)), cat8(ld_b4(bp), ld_b4(bp + 16)), a);
                 }
             }
         } else {                          // fp32 operands: step (t, i) contracts row 16t + 4g + i

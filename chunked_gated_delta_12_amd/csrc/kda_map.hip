@@ -67,15 +67,6 @@ struct MapSmem {
     MapScratch<E, D> scr[MapCfg<E, D>::NPW];
 };
 
-// Orders this wavefront's LDS writes before its following LDS reads of other
-// lanes' data.  A wavefront's LDS instructions execute in issue order, so only
-// the compiler has to be kept from moving accesses across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // N elements as 8-byte stores (4-byte when the run is shorter).
 template <typename E, int N>
 __device__ __forceinline__ void store_run8(E* p, const E* x) {
