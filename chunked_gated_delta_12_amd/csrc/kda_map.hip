@@ -83,6 +83,14 @@ __device__ __forceinline__ void store_run8(E* p, const E* x) {
     }
 }
 
+// The LDS-side operand of a K = 16 product, row [.][16] at p (k = 4g .. 4g+3 at
+// p).  bf16: the upper four k-slots of the 16x16x32 operand take the next four
+// stored elements instead of zeros, saving the register copies that padding
+// would cost.  They are finite (data, or row padding zeroed at the start) and
+// meet the zero slots of the register-side operand, so they add exact zeros.
+__device__ __forceinline__ bf16x8 ld_k16(const bf16* p) { return cat8(ld_b4(p), ld_b4(p + 4)); }
+__device__ __forceinline__ f32x4 ld_k16(const float* p) { return ld_quad(p); }
+
 template <typename E, int D>
 __global__ void __launch_bounds__((64 * MapCfg<E, D>::NW))
 map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
@@ -107,9 +115,21 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     const int tend = min(T, c1 * CHUNK);            // the segment's tokens end here
     const bool last = seg == nseg - 1;              // publishes T' only
 
+    // zero the padding columns 16 .. LDK-1 of the [.][16] tiles read by ld_k16
+    for (int i = tid; i < 2 * C::NPW * (D + 16); i += 64 * C::NW) {
+        Slot& sl = sm.slot[i / (D + 16)];
+        const int row = i % (D + 16);
+        E* pad = row < D ? &sl.ke_col[row * C::LDK + 16] : &sl.t_row[(row - D) * C::LDK + 16];
+#pragma unroll
+        for (int j = 0; j < C::LDK - 16; ++j) pad[j] = from_f<E>(0.0f);
+    }
+
     if (wave >= C::NCW) {
         // =================================================================== producer
         const int pw = wave - C::NCW;
+        // The producers' chunk is the critical path of every step: let the SIMD
+        // issue their instructions first and the consumers' in the gaps.
+        __builtin_amdgcn_s_setprio(3);
         MapScratch<E, D>& scr = sm.scr[pw];
         const int p = lane % C::PPL, tg = lane / C::PPL;
         const int ch = 2 * p, tok0 = tg * C::TPL;
@@ -300,7 +320,7 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             }
             MM::template mm_la_n<D, C::TPW>(sl.kn_row, C::LDR, sb, y, C::TPW, r, g);
             // U = T' Y
-            const PFrag tf = MM::pad(ld_quad(&sl.t_row[r * C::LDK + 4 * g]));
+            const PFrag tf = ld_k16(&sl.t_row[r * C::LDK + 4 * g]);
             PFrag up[C::TPW];
 #pragma unroll
             for (int jj = 0; jj < C::TPW; ++jj) up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(y[jj]), f32x4{0, 0, 0, 0}));
@@ -312,7 +332,7 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 #pragma unroll
             for (int t = 0; t < C::KT; ++t) {
                 const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sl.gc[16 * t + 4 * g]);
-                const PFrag kf = MM::pad(ld_quad(&sl.ke_col[(16 * t + r) * C::LDK + 4 * g]));
+                const PFrag kf = ld_k16(&sl.ke_col[(16 * t + r) * C::LDK + 4 * g]);
 #pragma unroll
                 for (int jj = 0; jj < C::TPW; ++jj) {
 #pragma unroll
