@@ -49,6 +49,8 @@ def _load():
         ip = ctypes.POINTER(ctypes.c_int)
         lib.kda_oracle_gate.argtypes = [ctypes.c_long, dp, dp]
         lib.kda_oracle_gate.restype = None
+        lib.kda_oracle_output_gate.argtypes = [ctypes.c_long, dp, dp, dp]
+        lib.kda_oracle_output_gate.restype = None
         lib.kda_oracle_gate_cumsum.argtypes = [ctypes.c_int] * 4 + [dp, dp]
         lib.kda_oracle_gate_cumsum.restype = None
         lib.kda_oracle_recurrence.argtypes = (
@@ -88,6 +90,15 @@ def gate(theta):
     g = np.empty_like(th)
     _load().kda_oracle_gate(th.size, _p(th), _p(g))
     return g
+
+
+def output_gate(o, z):
+    """o * sigmoid(z), elementwise, float64 (o and z of the same shape)."""
+    o, z = _d(o), _d(z)
+    assert o.shape == z.shape
+    out = np.empty_like(o)
+    _load().kda_oracle_output_gate(o.size, _p(o), _p(z), _p(out))
+    return out
 
 
 def gate_cumsum(g):

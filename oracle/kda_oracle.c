@@ -31,6 +31,13 @@
  *        o_t  = S^T q_t                                 (output read)
  *    The decode step is this body for one token with S updated in place.
  *
+ *  - Output gate ("Kimi K3" explainer, "Across the sequence": the output of
+ *    each attention layer is scaled per channel and per token by a learned,
+ *    input-dependent sigmoid gate before it rejoins the residual stream).
+ *    Read as o'_t[j] = o_t[j] * sigmoid(z_t[j]), where z (the gate's
+ *    pre-activation, same shape as o) is an input.  The gate acts on the
+ *    output only; the state recurrence above does not see it.
+ *
  * Plain loops in double precision, no blocking or reordering beyond the
  * definition.  Threads only split independent (batch, head) sequences.
  * Column j of S evolves independently of the other columns (every operation
@@ -57,6 +64,11 @@ static double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 /* g = g_min * sigmoid(theta), elementwise over n values. */
 void kda_oracle_gate(long n, const double* theta, double* g) {
     for (long i = 0; i < n; ++i) g[i] = ORACLE_G_MIN * oracle_sigmoid(theta[i]);
+}
+
+/* Output gate: out = o * sigmoid(z), elementwise over n values (out may be o). */
+void kda_oracle_output_gate(long n, const double* o, const double* z, double* out) {
+    for (long i = 0; i < n; ++i) out[i] = o[i] * oracle_sigmoid(z[i]);
 }
 
 /* Inclusive prefix sum of g along T, restarted at every 16-token chunk start

@@ -75,6 +75,48 @@ def test_gate_range_and_monotone(oracle_mod):
     np.testing.assert_allclose(g + g[::-1], -5.0, rtol=0, atol=1e-14)
 
 
+# ----------------------------------------------------------------------------- output gate
+# "Kimi K3" explainer, "Across the sequence": each attention output is scaled per
+# channel and token by a sigmoid gate, o' = o * sigmoid(z).
+def test_output_gate_special_values(oracle_mod):
+    # sigmoid(0) = 1/2 and sigmoid(+-ln 3) = 3/4, 1/4; the far tails give o and 0
+    o = np.array([2.0, -4.0, 8.0, 3.0, -7.0])
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), 800.0, -800.0])
+    out = oracle_mod.output_gate(o, z)
+    np.testing.assert_allclose(out, [1.0, -3.0, 2.0, 3.0, 0.0], rtol=0, atol=1e-14)
+    assert out[0] == 1.0 and out[3] == 3.0 and out[4] == 0.0
+
+
+def test_output_gate_symmetry_and_monotone(oracle_mod):
+    rng = np.random.default_rng(21)
+    o = rng.standard_normal((3, 5, 2, 8))
+    z = rng.standard_normal((3, 5, 2, 8)) * 4.0
+    # sigmoid(z) + sigmoid(-z) = 1, so the two gated outputs add back to o
+    np.testing.assert_allclose(oracle_mod.output_gate(o, z) + oracle_mod.output_gate(o, -z), o,
+                               rtol=0, atol=1e-14)
+    # for a fixed positive output the gated value rises with z and stays in (0, o)
+    zs = np.linspace(-30, 30, 601)
+    g = oracle_mod.output_gate(np.full_like(zs, 2.5), zs)
+    assert np.all(np.diff(g) > 0) and np.all(g > 0) and np.all(g < 2.5)
+
+
+def test_output_gate_after_one_token_by_hand(oracle_mod):
+    # One token, d_k = d_v = 2, S0 = I, g = 0, beta = 1, k = (1, 0), v = (3, 5),
+    # q = (1, 1):  u = v - S^T k = (2, 5);  S = I + k u^T = [[3, 5], [0, 1]];
+    # o = S^T q = (3, 6).  With z = (0, ln 3) the gated output is (1.5, 4.5); the
+    # state is the gate-free one.
+    q = np.array([1.0, 1.0]).reshape(1, 1, 1, 2)
+    k = np.array([1.0, 0.0]).reshape(1, 1, 1, 2)
+    v = np.array([3.0, 5.0]).reshape(1, 1, 1, 2)
+    g = np.zeros((1, 1, 1, 2))
+    beta = np.ones((1, 1, 1))
+    S0 = np.eye(2).reshape(1, 1, 2, 2)
+    o, S_T = oracle_mod.recurrence(q, k, v, g, beta, S0)
+    z = np.array([0.0, math.log(3.0)]).reshape(1, 1, 1, 2)
+    np.testing.assert_allclose(oracle_mod.output_gate(o, z)[0, 0, 0], [1.5, 4.5], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S_T[0, 0], [[3.0, 5.0], [0.0, 1.0]], rtol=0, atol=1e-15)
+
+
 def test_gate_cumsum_restarts_every_16(oracle_mod):
     B, T, H, dk = 2, 40, 3, 4          # 2.5 chunks: ragged tail
     g = -np.ones((B, T, H, dk))
