@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the timing of the calls with the output gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -194,6 +196,24 @@ def main():
                  "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": flops},
     }
 
+    if not args.no_gated:
+        # the same prefill with the output gate o * sigmoid(z): z is read once more
+        z = kin.output_gate_preact((B, T, H, dv), w.dtype, w.seed, device=dev)
+        og = torch.empty_like(o)
+
+        def gstep():
+            kda.kda_chunk_fwd_gated(x["q"], x["k"], x["v"], x["theta"], x["beta"], z, x["S0"],
+                                    segments=seg, o=og, S_T=S_T, workspace=ws, stream=stream)
+
+        gms, _ = time_calls(gstep, args.steps, args.warmup, stream)
+        gbytes = nbytes + B * T * H * dv * es
+        ggbs = gbytes / (gms * 1e-3) / 1e9
+        out["output_gate"] = {"workload": w.name, "call": "kda_chunk_fwd_gated", "ms_per_step": gms,
+                              "tokens_per_s": B * T / (gms * 1e-3), "achieved": ggbs,
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ggbs / HBM_PEAK_GBS,
+                              "algorithmic_bytes": gbytes, "time_vs_ungated": gms / ms}
+        del z, og
+
     if not args.no_decode:
         dw = kin.DECODE_WORKLOADS["decode_b256"]
         S, gen = kin.decode_state(dw, device=dev)
@@ -215,6 +235,21 @@ def main():
                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "tokens_per_s": dw.B / (dms * 1e-3), "algorithmic_bytes": dby,
                          "steps_timed": args.decode_steps}
+        if not args.no_gated:
+            zd = kin.output_gate_preact((nt, dw.B, dw.H, dw.dv), dw.dtype, dw.seed, device=dev)
+
+            def gdstep():
+                i = it[0] % nt
+                it[0] += 1
+                kda.kda_decode_step_gated(tok["q"][i], tok["k"][i], tok["v"][i], tok["theta"][i],
+                                          tok["beta"][i], S, zd[i], o=od, stream=stream)
+
+            gdms, _ = time_calls(gdstep, args.decode_steps, 3, stream)
+            gdby = dby + dw.B * dw.H * dw.dv * 2
+            out["decode"]["output_gate"] = {"ms_per_step": gdms, "achieved": gdby / (gdms * 1e-3) / 1e9,
+                                            "frac": gdby / (gdms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                            "algorithmic_bytes": gdby}
+            del zd
         del S, tok
 
     if args.copy_calibration > 0:

@@ -9,6 +9,8 @@ has not been built, every call raises.
 
     o, S_T = kda_chunk_fwd(q, k, v, theta, beta, S0=None)
     o      = kda_decode_step(q, k, v, theta, beta, S)        # S updated in place
+    o, S_T = kda_chunk_fwd_gated(q, k, v, theta, beta, z)    # o * sigmoid(z)
+    o      = kda_decode_step_gated(q, k, v, theta, beta, S, z)
     g, gc  = kda_gate(theta)
 """
 from __future__ import annotations
@@ -54,6 +56,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_auto_segments.restype = c_int
     lib.kda_decode_step.argtypes = [c_int] * 5 + [vp] * 3 + [fp] * 3 + [vp, vp]
     lib.kda_decode_step.restype = c_int
+    lib.kda_chunk_fwd_gated.argtypes = [c_int] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, fp, vp, c_size, vp]
+    lib.kda_chunk_fwd_gated.restype = c_int
+    lib.kda_decode_step_gated.argtypes = [c_int] * 5 + [vp] * 3 + [fp] * 3 + [vp, vp, vp]
+    lib.kda_decode_step_gated.restype = c_int
     lib.kda_gate.argtypes = [c_int] * 4 + [fp, fp, fp, vp]
     lib.kda_gate.restype = c_int
     lib.kda_status_string.argtypes = [c_int]
@@ -126,6 +132,16 @@ def kda_chunk_fwd(q, k, v, theta, beta, S0=None, *, segments=0, o=None, S_T=None
     """Chunked prefill.  q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32), theta
     [B,T,H,dk] fp32, beta [B,T,H] fp32, S0 [B,H,dk,dv] fp32 or None.
     Returns (o, S_T); S_T is None when want_state is False."""
+    return _chunk_fwd(q, k, v, theta, beta, S0, None, segments, o, S_T, want_state, workspace, stream)
+
+
+def kda_chunk_fwd_gated(q, k, v, theta, beta, z, S0=None, *, segments=0, o=None, S_T=None,
+                        want_state=True, workspace=None, stream=None):
+    """kda_chunk_fwd with the output gate: o * sigmoid(z), z [B,T,H,dv] of q's dtype."""
+    return _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream)
+
+
+def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream):
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -138,6 +154,8 @@ def kda_chunk_fwd(q, k, v, theta, beta, S0=None, *, segments=0, o=None, S_T=None
     _need(beta, "beta", torch.float32, (B, T, H), dev)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if z is not None:
+        _need(z, "z", dt, (B, T, H, dv), dev)
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
     _need(o, "o", dt, (B, T, H, dv), dev)
@@ -149,16 +167,31 @@ def kda_chunk_fwd(q, k, v, theta, beta, S0=None, *, segments=0, o=None, S_T=None
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.kda_chunk_fwd(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
-                           _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
-                           _stream(q, stream))
-    _check("kda_chunk_fwd", st)
+    if z is None:
+        st = lib.kda_chunk_fwd(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
+                               _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
+                               _stream(q, stream))
+        _check("kda_chunk_fwd", st)
+    else:
+        st = lib.kda_chunk_fwd_gated(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(theta), _ptr(beta), _ptr(S0), _ptr(z), _ptr(o), _ptr(S_T),
+                                     _ptr(workspace), ws_bytes, _stream(q, stream))
+        _check("kda_chunk_fwd_gated", st)
     return o, S_T
 
 
 def kda_decode_step(q, k, v, theta, beta, S, *, o=None, stream=None):
     """One decode step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), theta [B,H,dk]
     fp32, beta [B,H] fp32, S [B,H,dk,dv] fp32 (updated in place).  Returns o."""
+    return _decode_step(q, k, v, theta, beta, S, None, o, stream)
+
+
+def kda_decode_step_gated(q, k, v, theta, beta, S, z, *, o=None, stream=None):
+    """kda_decode_step with the output gate: o * sigmoid(z), z [B,H,dv] of q's dtype."""
+    return _decode_step(q, k, v, theta, beta, S, z, o, stream)
+
+
+def _decode_step(q, k, v, theta, beta, S, z, o, stream):
     lib = load_library()
     B, H, dk = q.shape
     dv = v.shape[-1]
@@ -170,12 +203,19 @@ def kda_decode_step(q, k, v, theta, beta, S, *, o=None, stream=None):
     _need(theta, "theta", torch.float32, (B, H, dk), dev)
     _need(beta, "beta", torch.float32, (B, H), dev)
     _need(S, "S", torch.float32, (B, H, dk, dv), dev)
+    if z is not None:
+        _need(z, "z", dt, (B, H, dv), dev)
     if o is None:
         o = torch.empty((B, H, dv), dtype=dt, device=dev)
     _need(o, "o", dt, (B, H, dv), dev)
-    st = lib.kda_decode_step(code, B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(beta),
-                             _ptr(S), _ptr(o), _stream(q, stream))
-    _check("kda_decode_step", st)
+    if z is None:
+        st = lib.kda_decode_step(code, B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(beta),
+                                 _ptr(S), _ptr(o), _stream(q, stream))
+        _check("kda_decode_step", st)
+    else:
+        st = lib.kda_decode_step_gated(code, B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
+                                       _ptr(beta), _ptr(S), _ptr(z), _ptr(o), _stream(q, stream))
+        _check("kda_decode_step_gated", st)
     return o
 
 

@@ -113,10 +113,12 @@ int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segmen
     return ok();
 }
 
-int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
-                  const void* k, const void* v, const float* theta, const float* beta,
-                  const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+// kda_chunk_fwd and kda_chunk_fwd_gated; z (the output gate's pre-activation)
+// is NULL for the former.
+static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
+                          const void* k, const void* v, const float* theta, const float* beta,
+                          const float* S0, const void* z, void* o, float* S_T, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     int st = check_common(dtype, B, H, dk, dv);
     if (st) return st;
     if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
@@ -128,9 +130,9 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, 
         return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);
     if (!q || !k || !v || !theta || !beta || !o)
         return fail(KDA_ERR_NULL, "q, k, v, theta, beta and o must be non-NULL");
-    const void* all[] = {q, k, v, theta, beta, S0, o, S_T, workspace};
-    const char* names[] = {"q", "k", "v", "theta", "beta", "S0", "o", "S_T", "workspace"};
-    for (int i = 0; i < 9; ++i)
+    const void* all[] = {q, k, v, theta, beta, S0, o, S_T, workspace, z};
+    const char* names[] = {"q", "k", "v", "theta", "beta", "S0", "o", "S_T", "workspace", "z"};
+    for (int i = 0; i < 10; ++i)
         if (all[i] && !aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
 
     const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
@@ -145,7 +147,7 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, 
     const size_t st_bytes = (size_t)B * H * dk * dv * 4;
     const Range in[] = {rng("q", q, tok * dk * es), rng("k", k, tok * dk * es), rng("v", v, tok * dv * es),
                         rng("theta", theta, tok * dk * 4), rng("beta", beta, tok * 4),
-                        rng("S0", S0, S0 ? st_bytes : 0)};
+                        rng("S0", S0, S0 ? st_bytes : 0), rng("z", z, z ? tok * dv * es : 0)};
     const Range r_o = rng("o", o, tok * dv * es);
     const Range r_st = rng("S_T", S_T, S_T ? st_bytes : 0);
     const Range r_ws = rng("workspace", workspace, need);
@@ -160,29 +162,48 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, 
     if (overlap(r_st, r_ws)) return fail(KDA_ERR_ALIAS, "S_T overlaps workspace");
 
     hipError_t e = kda::launch_chunk_fwd(dtype == KDA_F32, B, T, H, dk, plan, q, k, v, theta, beta, S0,
-                                         o, S_T, need ? workspace : nullptr,
+                                         z, o, S_T, need ? workspace : nullptr,
                                          reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 
-int kda_decode_step(int dtype, int B, int H, int dk, int dv, const void* q, const void* k,
-                    const void* v, const float* theta, const float* beta, float* S, void* o,
-                    void* stream) {
+int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
+                  const void* k, const void* v, const float* theta, const float* beta,
+                  const float* S0, void* o, float* S_T, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return chunk_fwd_impl(dtype, B, T, H, dk, dv, segments, q, k, v, theta, beta, S0, nullptr, o, S_T,
+                          workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_gated(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
+                        const void* k, const void* v, const float* theta, const float* beta,
+                        const float* S0, const void* z, void* o, float* S_T, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (!z) return fail(KDA_ERR_NULL, "z must be non-NULL");
+    return chunk_fwd_impl(dtype, B, T, H, dk, dv, segments, q, k, v, theta, beta, S0, z, o, S_T,
+                          workspace, workspace_bytes, stream);
+}
+
+// kda_decode_step and kda_decode_step_gated; z is NULL for the former.
+static int decode_step_impl(int dtype, int B, int H, int dk, int dv, const void* q, const void* k,
+                            const void* v, const float* theta, const float* beta, float* S,
+                            const void* z, void* o, void* stream) {
     int st = check_common(dtype, B, H, dk, dv);
     if (st) return st;
     if (!sizes_fit(B, H, dk, dv) || (int64_t)B * H > 0x7fffffffLL)
         return fail(KDA_ERR_SHAPE, "B*H too large");
     if (!q || !k || !v || !theta || !beta || !S || !o)
         return fail(KDA_ERR_NULL, "q, k, v, theta, beta, S and o must be non-NULL");
-    const void* all[] = {q, k, v, theta, beta, S, o};
-    const char* names[] = {"q", "k", "v", "theta", "beta", "S", "o"};
-    for (int i = 0; i < 7; ++i)
-        if (!aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const void* all[] = {q, k, v, theta, beta, S, o, z};
+    const char* names[] = {"q", "k", "v", "theta", "beta", "S", "o", "z"};
+    for (int i = 0; i < 8; ++i)
+        if (all[i] && !aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     const size_t es = dtype == KDA_BF16 ? 2 : 4;
     const size_t bh = (size_t)B * H;
     const Range in[] = {rng("q", q, bh * dk * es), rng("k", k, bh * dk * es), rng("v", v, bh * dv * es),
-                        rng("theta", theta, bh * dk * 4), rng("beta", beta, bh * 4)};
+                        rng("theta", theta, bh * dk * 4), rng("beta", beta, bh * 4),
+                        rng("z", z, z ? bh * dv * es : 0)};
     const Range r_s = rng("S", S, bh * dk * dv * 4);
     const Range r_o = rng("o", o, bh * dv * es);
     for (const Range& x : in) {
@@ -191,10 +212,23 @@ int kda_decode_step(int dtype, int B, int H, int dk, int dv, const void* q, cons
     }
     if (overlap(r_o, r_s)) return fail(KDA_ERR_ALIAS, "o overlaps S");
 
-    hipError_t e = kda::launch_decode(dtype == KDA_F32, B, H, dk, q, k, v, theta, beta, S, o,
+    hipError_t e = kda::launch_decode(dtype == KDA_F32, B, H, dk, q, k, v, theta, beta, S, z, o,
                                       reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+int kda_decode_step(int dtype, int B, int H, int dk, int dv, const void* q, const void* k,
+                    const void* v, const float* theta, const float* beta, float* S, void* o,
+                    void* stream) {
+    return decode_step_impl(dtype, B, H, dk, dv, q, k, v, theta, beta, S, nullptr, o, stream);
+}
+
+int kda_decode_step_gated(int dtype, int B, int H, int dk, int dv, const void* q, const void* k,
+                          const void* v, const float* theta, const float* beta, float* S,
+                          const void* z, void* o, void* stream) {
+    if (!z) return fail(KDA_ERR_NULL, "z must be non-NULL");
+    return decode_step_impl(dtype, B, H, dk, dv, q, k, v, theta, beta, S, z, o, stream);
 }
 
 int kda_gate(int B, int T, int H, int dk, const float* theta, float* g, float* g_cum, void* stream) {

@@ -88,6 +88,34 @@ template <> struct StoreUnit<4> { typedef uint32_t T; };
 template <> struct StoreUnit<8> { typedef uint64_t T; };
 template <> struct StoreUnit<16> { typedef f32x4 T; };
 
+// One store unit by buffer load (zero outside the resource).
+template <int SU> __device__ __forceinline__ typename StoreUnit<SU>::T ld_unit(Rsrc r, uint32_t voff);
+template <> __device__ __forceinline__ uint32_t ld_unit<4>(Rsrc r, uint32_t voff) {
+    return buf_ld32(r, voff, 0u);
+}
+template <> __device__ __forceinline__ uint64_t ld_unit<8>(Rsrc r, uint32_t voff) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0));
+}
+template <> __device__ __forceinline__ f32x4 ld_unit<16>(Rsrc r, uint32_t voff) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// The output gate on one store unit of o: every element times sigmoid of the
+// matching element of z, in fp32, rounded once to the storage type.
+template <typename E, typename U>
+__device__ __forceinline__ U gate_unit(U ou, U zu) {
+    constexpr int N = (int)(sizeof(U) / sizeof(E));
+    typedef E V __attribute__((__vector_size__(sizeof(U))));
+    const V ov = __builtin_bit_cast(V, ou), zv = __builtin_bit_cast(V, zu);
+    V r;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const E oe = ov[i], ze = zv[i];
+        r[i] = from_f<E>(to_f(oe) * out_sigmoid(to_f(ze)));
+    }
+    return __builtin_bit_cast(U, r);
+}
+
 // N consecutive values as one store of the storage type.
 template <typename E, int N>
 __device__ __forceinline__ void store_run(E* p, const float* x) {
@@ -125,13 +153,15 @@ __device__ __forceinline__ void store_pair_runs(E* pa, E* pb, const typename Pai
 
 // TWS: several segments; the kernel reads each chunk's T' = T diag(beta) from
 // ws_t (published by the map kernel) instead of forming A and solving for T.
-template <typename E, int D, int NW, bool TWS>
+// GATE: o is scaled by the output gate sigmoid(z) ("Kimi K3" explainer,
+// "Across the sequence"); z has o's layout.
+template <typename E, int D, int NW, bool TWS, bool GATE>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
              const float* __restrict__ theta, const float* __restrict__ beta,
              const float* S0, const float* __restrict__ ws_start,
-             const E* ws_t, E* __restrict__ o, float* S_T) {
+             const E* ws_t, const E* __restrict__ z, E* __restrict__ o, float* S_T) {
     typedef ChunkCfg<D, NW> C;
     typedef ChunkSmem<E, D, NW> SM;
     typedef Ops<E> MM;
@@ -257,6 +287,23 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     constexpr int NU = OB / SU;                             // units per tile
     constexpr int UPT = (NU + C::NTHR - 1) / C::NTHR;       // units per thread
     typedef typename StoreUnit<SU>::T Unit;
+    // With the output gate, z of the units a thread stores for chunk n is loaded
+    // during chunk n's update (load_z) and used when that tile is stored during
+    // the next chunk; a thread without a unit reads offset 0 and ignores it.
+    Unit z_l[UPT];
+    auto load_z = [&](int n) {
+        const int t0 = n * CHUNK;
+        const uint32_t nvalid = (uint32_t)min(CHUNK, T - t0);
+        const Rsrc rz = make_rsrc(z + head_base + (int64_t)t0 * tok_stride,
+                                  nvalid * (uint32_t)tok_stride * (uint32_t)sizeof(E));
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int u = tid + C::NTHR * j;
+            const int row = u / UPR, ce = (u % UPR) * (SU / (int)sizeof(E));
+            const bool has = NU % C::NTHR == 0 || u < NU;
+            z_l[j] = ld_unit<SU>(rz, has ? ((uint32_t)row * (uint32_t)tok_stride + (uint32_t)ce) * (uint32_t)sizeof(E) : 0u);
+        }
+    };
     auto store_o = [&](int n, bool masked) {
         const int t0 = n * CHUNK;
 #pragma unroll
@@ -264,7 +311,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             const int u = tid + C::NTHR * j;
             const int row = u / UPR, ce = (u % UPR) * (SU / (int)sizeof(E));
             if ((NU % C::NTHR == 0 || u < NU) && (!masked || t0 + row < T)) {
-                const Unit val = *reinterpret_cast<const Unit*>(&sm.o_tile[row * C::LDR + ce]);
+                Unit val = *reinterpret_cast<const Unit*>(&sm.o_tile[row * C::LDR + ce]);
+                if constexpr (GATE) val = gate_unit<E>(val, z_l[j]);
                 *reinterpret_cast<Unit*>(o + head_base + (int64_t)(t0 + row) * tok_stride + ce) = val;
             }
         }
@@ -445,6 +493,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             }
         }
         if (n + 1 < c1) load_late(n + 1);   // T and beta are no longer needed for this chunk
+        if constexpr (GATE) load_z(n);      // stored with this chunk's o tile, during the next chunk
 #pragma unroll
         for (int t = 0; t < C::KT; ++t) {
             const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * t + 4 * g]);
@@ -682,8 +731,8 @@ constexpr int CHUNK_NW_OUT = 4;
 template <typename E, int D>
 static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const void* q,
                                  const void* k, const void* v, const float* theta,
-                                 const float* beta, const float* S0, void* o, float* S_T,
-                                 void* workspace, hipStream_t stream) {
+                                 const float* beta, const float* S0, const void* z, void* o,
+                                 float* S_T, void* workspace, hipStream_t stream) {
     const int BH = B * H;
     float* ws_start = nullptr;
     E* ws_t = nullptr;
@@ -702,25 +751,29 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
                            BH, p.nseg,
                            S0, (const float*)ws_n, (const E*)ws_m, ws_start);
     }
-    if (p.nseg > 1)
-        hipLaunchKernelGGL((chunk_kernel<E, D, CHUNK_NW_OUT, true>), dim3((unsigned)(BH * p.nseg)),
-                           dim3(64 * CHUNK_NW_OUT), 0, stream, T,
-                           H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
-                           beta, S0, (const float*)ws_start, (const E*)ws_t, (E*)o, S_T);
-    else
-        hipLaunchKernelGGL((chunk_kernel<E, D, CHUNK_NW_OUT, false>), dim3((unsigned)BH),
-                           dim3(64 * CHUNK_NW_OUT), 0, stream, T,
-                           H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)q, (const E*)k, (const E*)v, theta,
-                           beta, S0, (const float*)nullptr, (const E*)nullptr, (E*)o, S_T);
+    const bool gate = z != nullptr;
+#define KDA_OUT(TWS_, GATE_, GRID, WS_START, WS_T)                                                        \
+    hipLaunchKernelGGL((chunk_kernel<E, D, CHUNK_NW_OUT, TWS_, GATE_>), dim3((unsigned)(GRID)),           \
+                       dim3(64 * CHUNK_NW_OUT), 0, stream, T, H, BH, p.nchunks, p.seg_len, p.nseg,         \
+                       (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const float*)(WS_START),   \
+                       (const E*)(WS_T), (const E*)z, (E*)o, S_T)
+    if (p.nseg > 1) {
+        if (gate) KDA_OUT(true, true, BH * p.nseg, ws_start, ws_t);
+        else KDA_OUT(true, false, BH * p.nseg, ws_start, ws_t);
+    } else {
+        if (gate) KDA_OUT(false, true, BH, nullptr, nullptr);
+        else KDA_OUT(false, false, BH, nullptr, nullptr);
+    }
+#undef KDA_OUT
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,
-                            const float* beta, const float* S0, void* o, float* S_T,
+                            const float* beta, const float* S0, const void* z, void* o, float* S_T,
                             void* workspace, hipStream_t stream) {
 #define KDA_CH(E, D) \
-    return launch_chunk_t<E, D>(B, T, H, plan, q, k, v, theta, beta, S0, o, S_T, workspace, stream)
+    return launch_chunk_t<E, D>(B, T, H, plan, q, k, v, theta, beta, S0, z, o, S_T, workspace, stream)
     if (f32) {
         switch (d) {
             case 16: KDA_CH(float, 16);

@@ -10,7 +10,9 @@
 // 8*dk*dv bytes per head (plus ~1.5 KB of token data).  One workgroup owns
 // one head; each thread keeps a [RPT x 4] slab of S in registers between the
 // read and the write, and every load/store is a 16-byte vector access with a
-// wavefront covering contiguous rows.
+// wavefront covering contiguous rows.  With the output gate ("Kimi K3"
+// explainer, "Across the sequence") o is multiplied by sigmoid(z) in fp32
+// before it is rounded.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -28,7 +30,7 @@ template <typename E, int D>
 __global__ void __launch_bounds__(DecodeCfg<D>::NTHR)
 decode_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
               const float* __restrict__ theta, const float* __restrict__ beta,
-              float* __restrict__ S, E* __restrict__ o) {
+              float* __restrict__ S, const E* __restrict__ z, E* __restrict__ o) {
     typedef DecodeCfg<D> C;
     __shared__ alignas(16) float s_alpha[D];
     __shared__ alignas(16) float s_ak[D];
@@ -100,7 +102,9 @@ decode_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __restr
         }
         const float u = beta[bh] * (to_f(v[bh * D + tid]) - a);
         s_u[tid] = u;
-        o[bh * D + tid] = from_f<E>(b + s_dot * u);
+        float ov = b + s_dot * u;
+        if (z) ov *= out_sigmoid(to_f(z[bh * D + tid]));   // output gate, if given
+        o[bh * D + tid] = from_f<E>(ov);
     }
     __syncthreads();
 
@@ -119,17 +123,18 @@ decode_kernel(const E* __restrict__ q, const E* __restrict__ k, const E* __restr
 
 template <typename E, int D>
 static hipError_t launch_decode_t(int B, int H, const void* q, const void* k, const void* v,
-                                  const float* theta, const float* beta, float* S, void* o,
-                                  hipStream_t stream) {
+                                  const float* theta, const float* beta, float* S, const void* z,
+                                  void* o, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<E, D>), dim3((unsigned)(B * H)), dim3(DecodeCfg<D>::NTHR), 0,
-                       stream, (const E*)q, (const E*)k, (const E*)v, theta, beta, S, (E*)o);
+                       stream, (const E*)q, (const E*)k, (const E*)v, theta, beta, S, (const E*)z,
+                       (E*)o);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(bool f32, int B, int H, int d, const void* q, const void* k,
-                         const void* v, const float* theta, const float* beta, float* S, void* o,
-                         hipStream_t stream) {
-#define KDA_DEC(E, D) return launch_decode_t<E, D>(B, H, q, k, v, theta, beta, S, o, stream)
+                         const void* v, const float* theta, const float* beta, float* S,
+                         const void* z, void* o, hipStream_t stream) {
+#define KDA_DEC(E, D) return launch_decode_t<E, D>(B, H, q, k, v, theta, beta, S, z, o, stream)
     if (f32) {
         switch (d) {
             case 16: KDA_DEC(float, 16);

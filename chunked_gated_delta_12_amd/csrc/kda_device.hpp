@@ -37,6 +37,14 @@ __device__ __forceinline__ float gate_logdecay(float theta) {
     return G_MIN * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Output gate sigmoid(z) = 1 / (1 + e^-z) ("Kimi K3" explainer, "Across the
+// sequence": a per-channel sigmoid gate on the attention output), from the
+// hardware base-2 exponential and reciprocal.  It saturates to exactly 0 and
+// 1 in the tails (e^-z overflowing to inf gives 0), never NaN for finite z.
+__device__ __forceinline__ float out_sigmoid(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
 // ---------------------------------------------------------------- synchronisation
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // orders global memory, for which the compiler waits until every outstanding

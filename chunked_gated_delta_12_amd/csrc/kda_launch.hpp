@@ -24,9 +24,10 @@ size_t chunk_workspace_bytes(int B, int H, int dk, int dv, int nseg, int nchunks
 hipError_t launch_gate(int B, int T, int H, int dk, const float* theta, float* g, float* gcum,
                        hipStream_t stream);
 
+// z: pre-activation of the output gate (o's layout and type), or NULL for none.
 hipError_t launch_decode(bool f32, int B, int H, int d, const void* q, const void* k,
-                         const void* v, const float* theta, const float* beta, float* S, void* o,
-                         hipStream_t stream);
+                         const void* v, const float* theta, const float* beta, float* S,
+                         const void* z, void* o, hipStream_t stream);
 
 // Segment map kernel of the chunked prefill: the widened end state [N | M] of
 // every segment but the last (N fp32 into ws_n, M in the input type into ws_m,
@@ -35,9 +36,10 @@ hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan&
                             const void* v, const float* theta, const float* beta, float* ws_n,
                             void* ws_m, void* ws_t, hipStream_t stream);
 
+// z: pre-activation of the output gate (o's layout and type), or NULL for none.
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,
-                            const float* beta, const float* S0, void* o, float* S_T,
+                            const float* beta, const float* S0, const void* z, void* o, float* S_T,
                             void* workspace, hipStream_t stream);
 
 }  // namespace kda

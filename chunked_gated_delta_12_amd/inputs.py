@@ -18,6 +18,11 @@ Distributions (the second parameter of N is the standard deviation):
 Draw order: q, k, v, theta, beta, S0, all from one torch.Generator seeded with
 the workload's seed on the device the tensors are made on.  q, k, v are
 rounded to bf16 (round-to-nearest-even) unless the workload is fp32.
+
+The output gate's pre-activation z ~ N(0, 2), in the storage dtype, comes from
+a generator of its own (seed + 1000), so adding it leaves the draws above
+unchanged.  With a standard deviation of 2 the gate sigmoid(z) spans about
+0.02 .. 0.98 over the central 95% of draws.
 """
 from __future__ import annotations
 
@@ -129,3 +134,11 @@ def decode_token(w: DecodeWorkload, gen, device="cpu", steps: int = 1):
     theta = _normal((steps, B, H, dk), gen, device, w.theta_mu, w.theta_sigma)
     beta = torch.sigmoid(_normal((steps, B, H), gen, device))
     return dict(q=q, k=k, v=v, theta=theta, beta=beta)
+
+
+def output_gate_preact(shape, dtype: str, seed: int, device="cpu", sigma: float = 2.0):
+    """Pre-activation z of the output gate: N(0, sigma) of the given shape, rounded
+    to the storage dtype, drawn from a generator seeded with seed + 1000."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 1000)
+    return _normal(tuple(shape), gen, device, 0.0, sigma).to(torch_dtype(dtype))

@@ -101,6 +101,27 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments,
                   void* o, float* S_T,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * kda_chunk_fwd_gated: kda_chunk_fwd with the output gate applied to o
+ * ("Kimi K3" explainer, "Across the sequence": in the model, the attention
+ * output is multiplied channel by channel, token by token, by a sigmoid of a
+ * pre-activation computed from the layer's input):
+ *     o_t[j] = sigmoid(z_t[j]) * (S_t^T q_t)[j]
+ * The gate acts on the output only; S_T is the same as kda_chunk_fwd's.
+ *
+ *   z            [B, T, H, dv]   dtype, the gate's pre-activation; must be
+ *                non-NULL and 16-byte aligned, and must not overlap o, S_T or
+ *                the workspace.
+ *   Every other argument, the workspace size and the errors are those of
+ *   kda_chunk_fwd.  The ungated output is rounded to dtype, multiplied by the
+ *   gate in fp32 and rounded again.
+ * ------------------------------------------------------------------------- */
+int kda_chunk_fwd_gated(int dtype, int B, int T, int H, int dk, int dv, int segments,
+                        const void* q, const void* k, const void* v,
+                        const float* theta, const float* beta, const float* S0,
+                        const void* z, void* o, float* S_T,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace kda_chunk_fwd needs for these sizes and this segment
  * count (0 = automatic).  Writes *bytes; returns a kda_status. */
 int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments,
@@ -130,6 +151,21 @@ int kda_decode_step(int dtype, int B, int H, int dk, int dv,
                     const void* q, const void* k, const void* v,
                     const float* theta, const float* beta,
                     float* S, void* o, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kda_decode_step_gated: kda_decode_step with the output gate of
+ * kda_chunk_fwd_gated, o[j] = sigmoid(z[j]) * (S'^T q)[j], formed in fp32 and
+ * rounded once to dtype.
+ *
+ *   z            [B, H, dv]      dtype; non-NULL, 16-byte aligned, and not
+ *                overlapping o or S.
+ *   Every other argument and the errors are those of kda_decode_step; the
+ *   state update is the same.
+ * ------------------------------------------------------------------------- */
+int kda_decode_step_gated(int dtype, int B, int H, int dk, int dv,
+                          const void* q, const void* k, const void* v,
+                          const float* theta, const float* beta,
+                          float* S, const void* z, void* o, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kda_gate: the bounded gate on its own ("Architecture Deep Dive", section 3.2,

@@ -83,6 +83,27 @@ def test_chunk_fwd_rejects_null_misaligned_alias(lib):
     assert b.call(lib, ws=b.addr["v"], segments=2) == ALIAS
 
 
+def test_chunk_fwd_gated_validation(lib):
+    b = Bufs()
+    z = (1 << 43)
+    vp = ctypes.c_void_p
+
+    def call(zaddr, **over):
+        a = dict(b.addr)
+        a.update(over)
+        p = lambda n: vp(a[n]) if a[n] is not None else None
+        return lib.kda_chunk_fwd_gated(0, b.B, b.T, b.H, b.d, b.d, 1, p("q"), p("k"), p("v"), p("theta"),
+                                       p("beta"), p("S0"), vp(zaddr) if zaddr is not None else None,
+                                       p("o"), p("S_T"), p("ws"), 64 * MB, None)
+
+    assert call(None) == NULL
+    assert "z" in lib.kda_last_error().decode()
+    assert call(z + 8) == ALIGN
+    assert call(b.addr["o"]) == ALIAS                 # o may not be written over z
+    assert call(z, q=None) == NULL                    # the ungated checks still apply
+    assert call(z, o=b.addr["q"]) == ALIAS
+
+
 def test_chunk_fwd_workspace_checks(lib):
     b = Bufs(T=1024, H=2, d=64)
     need = kda.kda_chunk_fwd_workspace_size(1, 1024, 2, 64, 64, 4)
@@ -128,6 +149,22 @@ def test_decode_step_validation(lib):
     assert call(o=addr["o"] + 2) == ALIGN
     assert call(o=addr["S"]) == ALIAS
     assert call(S=addr["q"]) == ALIAS
+
+    z = base
+
+    def gated(zaddr, **over):
+        a = dict(addr)
+        a.update(over)
+        p = lambda n: ctypes.c_void_p(a[n]) if a[n] is not None else None
+        return lib.kda_decode_step_gated(0, B, H, d, d, p("q"), p("k"), p("v"), p("theta"), p("beta"),
+                                         p("S"), ctypes.c_void_p(zaddr) if zaddr is not None else None,
+                                         p("o"), None)
+
+    assert gated(None) == NULL
+    assert gated(z + 4) == ALIGN
+    assert gated(addr["o"]) == ALIAS                  # o over z
+    assert gated(addr["S"]) == ALIAS                  # the state over z
+    assert gated(z, S=None) == NULL                   # the ungated checks still apply
 
 
 def test_gate_validation(lib):

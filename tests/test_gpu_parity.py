@@ -175,6 +175,61 @@ def test_chunk_fwd_equals_decode_chain():
     assert rel_err(S, s.double().cpu().numpy()) <= 2e-2
 
 
+# ----------------------------------------------------------------------------- output gate
+GATED_CASES = [
+    ("tiny", {}, None, 1),                                        # fp32, d = 16, one segment
+    ("tiny", dict(T=5), None, 0),                                 # shorter than one chunk
+    ("small", dict(T=1000 + 7), None, 5),                         # bf16, ragged tail, segments
+    ("small", {}, None, 1),                                       # the single-segment kernel
+    ("small", {}, "f32", 4),
+    ("small", dict(dk=32, dv=32, H=3, T=333), None, 3),
+    ("prefill_64k", dict(H=2, T=2048 + 9), None, 0),
+]
+
+
+@pytest.mark.parametrize("name,over,dt,segments", GATED_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}-seg{c[3]}" for c in GATED_CASES])
+def test_chunk_fwd_gated_matches_oracle(oracle_mod, name, over, dt, segments):
+    w = _chunk_case(name, over, dt)
+    note(f"chunk_fwd_gated {w} segments={segments}")
+    x = kin.chunk_inputs(w)
+    z = kin.output_gate_preact((w.B, w.T, w.H, w.dv), w.dtype, w.seed)
+    d = to_dev(x)
+    zd = z.to(DEV)
+    o = torch.full((w.B, w.T, w.H, w.dv), float("nan"), device=DEV, dtype=d["q"].dtype)
+    S_T = torch.full((w.B, w.H, w.dk, w.dv), float("nan"), device=DEV)
+    kda.kda_chunk_fwd_gated(d["q"], d["k"], d["v"], d["theta"], d["beta"], zd, d["S0"],
+                            segments=segments, o=o, S_T=S_T)
+    o_u, S_u = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], d["S0"], segments=segments)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_mod.chunk_fwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], x["S0"])
+    og_ref = oracle_mod.output_gate(o_ref, z)
+    eo, es = rel_err(o, og_ref), rel_err(S_T, s_ref)
+    note(f"  err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+    # the gate touches only o: the state is the ungated call's, bit for bit
+    assert torch.equal(S_T, S_u)
+
+
+@pytest.mark.parametrize("B,H,d,dt,steps", [(3, 2, 16, "f32", 4), (8, 16, 128, "bf16", 3), (2, 2, 32, "bf16", 3)])
+def test_decode_step_gated_matches_oracle(oracle_mod, B, H, d, dt, steps):
+    note(f"decode_gated B={B} H={H} d={d} {dt} steps={steps}")
+    w = kin.DecodeWorkload("t", B, H, d, d, steps, dt, 0.0, 2.0, 0.1, 12)
+    S, gen = kin.decode_state(w)
+    tok = kin.decode_token(w, gen, steps=steps)
+    z = kin.output_gate_preact((steps, B, H, d), dt, w.seed)
+    S_dev = S.to(DEV)
+    S_ref = S.double().numpy()
+    for t in range(steps):
+        args = [tok[n][t] for n in ("q", "k", "v", "theta", "beta")]
+        o = torch.full((B, H, d), float("nan"), device=DEV, dtype=kin.torch_dtype(dt))
+        kda.kda_decode_step_gated(*[a.to(DEV) for a in args], S_dev, z[t].to(DEV), o=o)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle_mod.decode_step(*args, S_ref)
+        assert rel_err(o, oracle_mod.output_gate(o_ref, z[t])) <= TOL[dt], f"step {t}"
+    assert rel_err(S_dev, S_ref) <= TOL[dt]
+
+
 # ----------------------------------------------------------------------------- decode
 DECODE_CASES = [(3, 2, 16, "f32", 6), (4, 4, 64, "bf16", 6), (8, 16, 128, "bf16", 4), (5, 3, 128, "f32", 3),
                 (2, 2, 32, "bf16", 5)]
