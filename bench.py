@@ -7,10 +7,12 @@ inter-chunk scan) over the 64K-token training-shaped prefill: B=1, H=16,
 T=65536, d_k=d_v=128, bf16 q/k/v, fp32 theta ~ N(0, 2), beta, S0 = 0, seeded
 synthetic data already resident in HBM.  The timed region is exactly K steps
 between two device synchronisations, measured with HIP events on the stream the
-kernels run on.  The decode step (B=256, H=16 fp32 state, in place) is timed
-the same way and reported in the "decode" object.  The fp64 oracle is timed on
-the host cores on a bounded sample of the same prefill ("cpu_baseline").
-Prints one JSON line.
+kernels run on, after W untimed warm-up calls (the clocks settle after about
+60 calls).  The same prefill with the output gate (kda_chunk_fwd_gated) is
+timed the same way and reported in the "output_gate" object.  The decode step
+(B=256, H=16 fp32 state, in place) is timed the same way and reported in the
+"decode" object.  The fp64 oracle is timed on the host cores on a bounded
+sample of the same prefill ("cpu_baseline").  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -123,8 +125,11 @@ def cpu_baseline(x, T_sample, threads):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    # The GPU's clocks rise over the first ~50 ms of sustained work (a prefill call
+    # takes ~1.2 ms cold and ~0.77 ms after about 60 calls), so the default warm-up
+    # runs 100 calls before the timed ones.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=64)
@@ -228,7 +233,7 @@ def main():
             kda.kda_decode_step(tok["q"][i], tok["k"][i], tok["v"][i], tok["theta"][i], tok["beta"][i], S,
                                 o=od, stream=stream)
 
-        dms, _ = time_calls(dstep, args.decode_steps, 3, stream)
+        dms, _ = time_calls(dstep, args.decode_steps, args.warmup, stream)
         dfl, dby = decode_work(dw.B, dw.H, dw.dk, dw.dv)
         gbs = dby / (dms * 1e-3) / 1e9
         out["decode"] = {"workload": dw.name, "B": dw.B, "H": dw.H, "d": dw.dk, "ms_per_step": dms,
@@ -244,7 +249,7 @@ def main():
                 kda.kda_decode_step_gated(tok["q"][i], tok["k"][i], tok["v"][i], tok["theta"][i],
                                           tok["beta"][i], S, zd[i], o=od, stream=stream)
 
-            gdms, _ = time_calls(gdstep, args.decode_steps, 3, stream)
+            gdms, _ = time_calls(gdstep, args.decode_steps, args.warmup, stream)
             gdby = dby + dw.B * dw.H * dw.dv * 2
             out["decode"]["output_gate"] = {"ms_per_step": gdms, "achieved": gdby / (gdms * 1e-3) / 1e9,
                                             "frac": gdby / (gdms * 1e-3) / 1e9 / HBM_PEAK_GBS,
