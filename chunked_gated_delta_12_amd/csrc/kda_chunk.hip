@@ -70,9 +70,13 @@ template <typename E, int D, int NW>
 struct ChunkSmem {
     typedef ChunkCfg<D, NW> C;
     static constexpr int LDP = Ops<E>::PAD_ROW;    // padded K = 16 operand rows
-    alignas(16) E kn_row[16 * C::LDR];             // -K+ = -K*Gamma           [token][ch]
-    alignas(16) E km_row[16 * C::LDR];             // K- = K/Gamma             [token][ch]
-    alignas(16) E qp_row[16 * C::LDR];             // Q+ = Q*Gamma             [token][ch]
+    // operand rows [16][D]: bf16 D + 4 elements (a stride of 2 (mod 4) dwords keeps
+    // the pairs of 8-byte operand reads free of bank conflicts); o_tile keeps
+    // C::LDR, whose rows are 16-byte aligned for the o stores
+    static constexpr int LDQ = sizeof(E) == 2 ? D + 4 : D + 8;
+    alignas(16) E kn_row[16 * LDQ];                // -K+ = -K*Gamma           [token][ch]
+    alignas(16) E km_row[16 * LDQ];                // K- = K/Gamma             [token][ch]
+    alignas(16) E qp_row[16 * LDQ];                // Q+ = Q*Gamma             [token][ch]
     alignas(16) E o_tile[16 * C::LDR];             // o of the chunk           [token][col]
     alignas(16) E ke_pad[D * LDP];                 // Kend^T, padded           [ch][token]
     alignas(16) E v_col[D * C::LDC];               // V^T                      [col][token]
@@ -379,9 +383,9 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 const float kma = ka * emGa, kmb = kb * emGb;
                 kea[p] = kma * eC0;                 // k * exp(G_C - G), every factor <= 1 in range
                 keb[p] = kmb * eC1;
-                store_pair(&sm.kn_row[pos * C::LDR + ch], -ka * eGa, -kb * eGb);
-                store_pair(&sm.km_row[pos * C::LDR + ch], kma, kmb);
-                store_pair(&sm.qp_row[pos * C::LDR + ch], qa * eGa, qb * eGb);
+                store_pair(&sm.kn_row[pos * SM::LDQ + ch], -ka * eGa, -kb * eGb);
+                store_pair(&sm.km_row[pos * SM::LDQ + ch], kma, kmb);
+                store_pair(&sm.qp_row[pos * SM::LDQ + ch], qa * eGa, qb * eGb);
             }
             const int pos0 = pgi * C::PPT;
             const int kp = 8 * (pos0 >> 2) + (pos0 & 3);   // padded slot of token pos0
@@ -403,7 +407,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         //   O1^T = S^T Q+^T
         if (!TWS && wave == 0) {
             // A = StrictLower(beta K+ K-^T), kept transposed in LDS: akk_t[col][row]
-            const f32x4 a = MM::template mm_ll<D>(sm.kn_row, C::LDR, sm.km_row, C::LDR,
+            const f32x4 a = MM::template mm_ll<D>(sm.kn_row, SM::LDQ, sm.km_row, SM::LDQ,
                                                   f32x4{0, 0, 0, 0}, r, g);
             f32x4 m;
 #pragma unroll
@@ -412,7 +416,7 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         } else if (wave == (TWS ? 0 : 1)) {
             // A_qk^T = K- Q+^T; lane (g, r) holds A_qk[r][4g+i], i.e. four
             // consecutive k-slots of row r of the padded tile
-            const f32x4 a = MM::template mm_ll<D>(sm.km_row, C::LDR, sm.qp_row, C::LDR,
+            const f32x4 a = MM::template mm_ll<D>(sm.km_row, SM::LDQ, sm.qp_row, SM::LDQ,
                                                   f32x4{0, 0, 0, 0}, r, g);
             f32x4 m;
 #pragma unroll
@@ -437,8 +441,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             y[jj] = yc;
             o1[jj] = f32x4{0, 0, 0, 0};
         }
-        MM::template mm_la_n<D, C::TPW>(sm.kn_row, C::LDR, sb, y, nv, r, g);
-        MM::template mm_al_n<D, C::TPW>(sb, sm.qp_row, C::LDR, o1, nv, r, g);
+        MM::template mm_la_n<D, C::TPW>(sm.kn_row, SM::LDQ, sb, y, nv, r, g);
+        MM::template mm_al_n<D, C::TPW>(sb, sm.qp_row, SM::LDQ, o1, nv, r, g);
         // The products above are issued before the solve starts (matrix cores
         // run them while the solve proceeds); keeping the two apart in the
         // instruction stream also keeps their registers from being live at once.

@@ -199,9 +199,11 @@ template <> struct Ops<bf16> {
             acc = mfma_k16(ld_b4(A + r * lda + 4 * g), ld_b4(Bt + r * ldb + 4 * g), acc);
         } else {
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb)
-                acc = mfma_k32(ld_b8(A + r * lda + 32 * kb + 8 * g),
-                               ld_b8(Bt + r * ldb + 32 * kb + 8 * g), acc);
+            for (int kb = 0; kb < K / 32; ++kb) {   // 8-byte halves: rows need only 8-byte alignment
+                const bf16* a = A + r * lda + 32 * kb + 8 * g;
+                const bf16* b = Bt + r * ldb + 32 * kb + 8 * g;
+                acc = mfma_k32(cat8(ld_b4(a), ld_b4(a + 4)), cat8(ld_b4(b), ld_b4(b + 4)), acc);
+            }
         }
         return acc;
     }
@@ -244,7 +246,10 @@ template <> struct Ops<bf16> {
     // is stored as 4 groups of 8 elements, group g holding k = 4g .. 4g+3 and
     // four zeros, so one 16-byte load yields a complete 16x16x32 operand.
     typedef bf16x8 PFrag;   // a register operand in the same padded form
-    static constexpr int PAD_ROW = 40;   // elements per padded row (32 + 8 against bank conflicts)
+    // elements per padded row: 32 + 8.  (A 24-dword stride would free the 16-byte
+    // reads of these rows from their bank conflicts, about four per read, but the
+    // larger tiles measured slower in the kernel that uses them.)
+    static constexpr int PAD_ROW = 40;
     static __device__ __forceinline__ PFrag to_p(f32x4 x) {
         const bf16x4 z = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
         return cat8(to_b(x), z);

@@ -36,7 +36,10 @@ struct MapCfg {
     static constexpr int NPW = sizeof(E) == 2 ? 4 : 2;    // producer wavefronts = chunks per step
     static constexpr int NW = NCW + NPW;
     static constexpr int KT = D / 16;                     // 16-row tiles along d_k
-    static constexpr int LDR = D + 8;                     // padded [16][D] rows
+    // padded [16][D] rows.  bf16: D + 4 elements, a row stride of 2 (mod 4) dwords,
+    // for which the pairs of 8-byte operand reads (k = 4g.., 16 + 4g..) of 16 rows
+    // meet no bank conflict; with D + 8 they meet about eight per read on gfx950
+    static constexpr int LDR = sizeof(E) == 2 ? D + 4 : D + 8;
     static constexpr int LDK = 20;                        // padded [.][16] rows
     static constexpr int PPL = D / 2 < 64 ? D / 2 : 64;   // channel pairs of a producer
     static constexpr int NTG = 64 / PPL;                  // token groups (lanes per pair)
