@@ -181,55 +181,109 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         auto produce = [&](int m, Slot& sl) {
             const int t0 = m * CHUNK;
             const int nv = max(0, min(CHUNK, tend - t0));
-            // ---- log-decay in base 2 (zero for padding tokens) and its in-lane prefix
-            float Ga[C::TPL], Gb[C::TPL];
-            float sa = 0.0f, sb = 0.0f;
-#pragma unroll
-            for (int t = 0; t < C::TPL; ++t) {
-                float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][0]));
-                float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][1]));
-                const bool ok = tok0 + t < nv;
-                sa += ok ? ga : 0.0f;
-                sb += ok ? gb : 0.0f;
-                Ga[t] = sa;
-                Gb[t] = sb;
-            }
-            // prefix across the token groups of a pair (d_k < 128 only)
-            float offa = 0.0f, offb = 0.0f, tota = sa, totb = sb;
-            if constexpr (C::NTG > 1) {
-                float ia = sa, ib = sb;
-#pragma unroll
-                for (int d = 1; d < C::NTG; d <<= 1) {
-                    const float ua = __shfl_up(ia, d * C::PPL), ub = __shfl_up(ib, d * C::PPL);
-                    if (tg >= d) { ia += ua; ib += ub; }
-                }
-                offa = ia - sa;
-                offb = ib - sb;
-                tota = __shfl(ia, (C::NTG - 1) * C::PPL + p);
-                totb = __shfl(ib, (C::NTG - 1) * C::PPL + p);
-            }
-            const float eCa = __builtin_amdgcn_exp2f(tota), eCb = __builtin_amdgcn_exp2f(totb);
-            // ---- scaled tiles: -K+ and K- rows, Kend^T and V^T columns, Gamma_C
             E kea[C::TPL], keb[C::TPL], va[C::TPL], vb[C::TPL];
+            float eCa, eCb;
+            if constexpr (C::NTG == 1) {
+                // The lane holds all 16 tokens of its channel pair, so the decay is
+                // formed as products: per-token factor gamma = 2^(g2) (1 for padding
+                // tokens), Gamma_t = prefix product, Kend = k * (suffix product after
+                // t) = k Gamma_C / Gamma_t, and K- = Kend / Gamma_C.  Three
+                // transcendentals per element instead of four.
+                float gma[C::TPL], gmb[C::TPL];
 #pragma unroll
-            for (int t = 0; t < C::TPL; ++t) {
-                const int pos = tok0 + t;
-                const float xa = Ga[t] + offa, xb = Gb[t] + offb;
-                const float eGa = __builtin_amdgcn_exp2f(xa), eGb = __builtin_amdgcn_exp2f(xb);
-                const float emGa = __builtin_amdgcn_exp2f(-xa), emGb = __builtin_amdgcn_exp2f(-xb);
-                const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);   // zero for padding tokens
-                const float kma = ka * emGa, kmb = kb * emGb;
-                store_pair(&sl.kn_row[pos * C::LDR + ch], -ka * eGa, -kb * eGb);
-                store_pair(&scr.km_row[pos * C::LDR + ch], kma, kmb);
-                kea[t] = from_f<E>(kma * eCa);   // k * exp(G_C - G) <= |k|
-                keb[t] = from_f<E>(kmb * eCb);
-                va[t] = vr[t][0];
-                vb[t] = vr[t][1];
-                if constexpr (sizeof(E) == 4) {   // fp32: column elements one at a time (registers)
-                    sl.ke_col[ch * C::LDK + pos] = kea[t];
-                    sl.ke_col[(ch + 1) * C::LDK + pos] = keb[t];
-                    sl.v_col[ch * C::LDK + pos] = va[t];
-                    sl.v_col[(ch + 1) * C::LDK + pos] = vb[t];
+                for (int t = 0; t < C::TPL; ++t) {
+                    gma[t] = __builtin_amdgcn_exp2f(GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][0])));
+                    gmb[t] = __builtin_amdgcn_exp2f(GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][1])));
+                }
+                if (nv < CHUNK) {   // the segment's partial last chunk: padding tokens do not decay
+#pragma unroll
+                    for (int t = 0; t < C::TPL; ++t) {
+                        gma[t] = t < nv ? gma[t] : 1.0f;
+                        gmb[t] = t < nv ? gmb[t] : 1.0f;
+                    }
+                }
+                float Pa = 1.0f, Pb = 1.0f;   // Gamma_t
+#pragma unroll
+                for (int t = 0; t < C::TPL; ++t) {
+                    Pa *= gma[t];
+                    Pb *= gmb[t];
+                    const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);   // zero for padding tokens
+                    store_pair(&sl.kn_row[t * C::LDR + ch], -ka * Pa, -kb * Pb);
+                }
+                eCa = Pa;
+                eCb = Pb;
+                // 1 / Gamma_C <= e^80: the bound keeps it finite in fp32
+                const float ia = __builtin_amdgcn_rcpf(eCa), ib = __builtin_amdgcn_rcpf(eCb);
+                float Qa = 1.0f, Qb = 1.0f;   // product of gamma over the tokens after t
+#pragma unroll
+                for (int t = C::TPL - 1; t >= 0; --t) {
+                    const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);
+                    const float xa = ka * Qa, xb = kb * Qb;   // Kend, |Kend| <= |k|
+                    store_pair(&scr.km_row[t * C::LDR + ch], xa * ia, xb * ib);
+                    kea[t] = from_f<E>(xa);
+                    keb[t] = from_f<E>(xb);
+                    va[t] = vr[t][0];
+                    vb[t] = vr[t][1];
+                    if constexpr (sizeof(E) == 4) {   // fp32: column elements one at a time (registers)
+                        sl.ke_col[ch * C::LDK + t] = kea[t];
+                        sl.ke_col[(ch + 1) * C::LDK + t] = keb[t];
+                        sl.v_col[ch * C::LDK + t] = va[t];
+                        sl.v_col[(ch + 1) * C::LDK + t] = vb[t];
+                    }
+                    Qa *= gma[t];
+                    Qb *= gmb[t];
+                }
+            } else {
+                // ---- log-decay in base 2 (zero for padding tokens) and its in-lane prefix
+                float Ga[C::TPL], Gb[C::TPL];
+                float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+                for (int t = 0; t < C::TPL; ++t) {
+                    float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][0]));
+                    float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th[t][1]));
+                    const bool ok = tok0 + t < nv;
+                    sa += ok ? ga : 0.0f;
+                    sb += ok ? gb : 0.0f;
+                    Ga[t] = sa;
+                    Gb[t] = sb;
+                }
+                // prefix across the token groups of a pair (d_k < 128 only)
+                float offa = 0.0f, offb = 0.0f, tota = sa, totb = sb;
+                if constexpr (C::NTG > 1) {
+                    float ia = sa, ib = sb;
+#pragma unroll
+                    for (int d = 1; d < C::NTG; d <<= 1) {
+                        const float ua = __shfl_up(ia, d * C::PPL), ub = __shfl_up(ib, d * C::PPL);
+                        if (tg >= d) { ia += ua; ib += ub; }
+                    }
+                    offa = ia - sa;
+                    offb = ib - sb;
+                    tota = __shfl(ia, (C::NTG - 1) * C::PPL + p);
+                    totb = __shfl(ib, (C::NTG - 1) * C::PPL + p);
+                }
+                eCa = __builtin_amdgcn_exp2f(tota);
+                eCb = __builtin_amdgcn_exp2f(totb);
+                // ---- scaled tiles: -K+ and K- rows, Kend^T and V^T columns, Gamma_C
+#pragma unroll
+                for (int t = 0; t < C::TPL; ++t) {
+                    const int pos = tok0 + t;
+                    const float xa = Ga[t] + offa, xb = Gb[t] + offb;
+                    const float eGa = __builtin_amdgcn_exp2f(xa), eGb = __builtin_amdgcn_exp2f(xb);
+                    const float emGa = __builtin_amdgcn_exp2f(-xa), emGb = __builtin_amdgcn_exp2f(-xb);
+                    const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);   // zero for padding tokens
+                    const float kma = ka * emGa, kmb = kb * emGb;
+                    store_pair(&sl.kn_row[pos * C::LDR + ch], -ka * eGa, -kb * eGb);
+                    store_pair(&scr.km_row[pos * C::LDR + ch], kma, kmb);
+                    kea[t] = from_f<E>(kma * eCa);   // k * exp(G_C - G) <= |k|
+                    keb[t] = from_f<E>(kmb * eCb);
+                    va[t] = vr[t][0];
+                    vb[t] = vr[t][1];
+                    if constexpr (sizeof(E) == 4) {   // fp32: column elements one at a time (registers)
+                        sl.ke_col[ch * C::LDK + pos] = kea[t];
+                        sl.ke_col[(ch + 1) * C::LDK + pos] = keb[t];
+                        sl.v_col[ch * C::LDK + pos] = va[t];
+                        sl.v_col[(ch + 1) * C::LDK + pos] = vb[t];
+                    }
                 }
             }
             if constexpr (sizeof(E) == 2) {   // bf16: packed runs of the lane's tokens
