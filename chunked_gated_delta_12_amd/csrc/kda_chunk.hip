@@ -292,8 +292,8 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     constexpr int UPT = (NU + C::NTHR - 1) / C::NTHR;       // units per thread
     typedef typename StoreUnit<SU>::T Unit;
     // With the output gate, z of the units a thread stores for chunk n is loaded
-    // during chunk n's update (load_z) and used when that tile is stored during
-    // the next chunk; a thread without a unit reads offset 0 and ignores it.
+    // during chunk n's gate stage (load_z) and used when that tile is stored
+    // during the next chunk; a thread without a unit reads offset 0 and ignores it.
     Unit z_l[UPT];
     auto load_z = [&](int n) {
         const int t0 = n * CHUNK;
@@ -394,6 +394,10 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             store_pair_runs<E, C::PPT>(&sm.v_col[ch * C::LDC + pos0], &sm.v_col[(ch + 1) * C::LDC + pos0], vr);
         }
         if (n > c0) store_o(n - 1, false);   // the previous chunk is always a full one
+        // z of this chunk (used when its o tile is stored, during the next chunk) is
+        // issued before the prefetch: loads retire in order, and waiting for z must
+        // not mean waiting for the prefetch as well
+        if constexpr (GATE) load_z(n);
         if (n + PFD < c1) load_chunk(n + PFD, cur);   // in flight until that chunk's gate stage
         lds_barrier();
 
@@ -497,7 +501,6 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             }
         }
         if (n + 1 < c1) load_late(n + 1);   // T and beta are no longer needed for this chunk
-        if constexpr (GATE) load_z(n);      // stored with this chunk's o tile, during the next chunk
 #pragma unroll
         for (int t = 0; t < C::KT; ++t) {
             const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * t + 4 * g]);
