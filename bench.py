@@ -65,7 +65,7 @@ def time_calls(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall / steps * 1e3
 
 
-CHUNK_SOURCES = ("kda_chunk.hip", "kda_map.hip", "kda_device.hpp", "kda_launch.hpp")
+CHUNK_SOURCES = ("kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_device.hpp", "kda_launch.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 

@@ -764,6 +764,10 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
                        dim3(64 * CHUNK_NW_OUT), 0, stream, T, H, BH, p.nchunks, p.seg_len, p.nseg,         \
                        (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const float*)(WS_START),   \
                        (const E*)(WS_T), (const E*)z, (E*)o, S_T)
+    if (p.nseg > 1 && std::is_same<E, bf16>::value && chunk_out_supported(D)) {
+        // bf16: the output pass with producer and consumer wavefronts (kda_out.hip)
+        return launch_chunk_out(B, T, H, D, p, q, k, v, theta, ws_t, ws_start, z, o, S_T, stream);
+    }
     if (p.nseg > 1) {
         if (gate) KDA_OUT(true, true, BH * p.nseg, ws_start, ws_t);
         else KDA_OUT(true, false, BH * p.nseg, ws_start, ws_t);

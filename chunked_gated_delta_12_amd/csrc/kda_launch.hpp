@@ -36,6 +36,15 @@ hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan&
                             const void* v, const float* theta, const float* beta, float* ws_n,
                             void* ws_m, void* ws_t, hipStream_t stream);
 
+// Output pass of a segmented bf16 prefill with producer and consumer
+// wavefronts (d = 32, 64 or 128: chunk_out_supported): o from each segment's
+// start state in ws_start and each chunk's T' in ws_t, scaled by the output gate
+// sigmoid(z) when z is not NULL; S_T (nullable) from the last segment.
+bool chunk_out_supported(int d);
+hipError_t launch_chunk_out(int B, int T, int H, int d, const SegPlan& plan, const void* q, const void* k,
+                            const void* v, const float* theta, const void* ws_t, const float* ws_start,
+                            const void* z, void* o, float* S_T, hipStream_t stream);
+
 // z: pre-activation of the output gate (o's layout and type), or NULL for none.
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,

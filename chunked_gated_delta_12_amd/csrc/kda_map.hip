@@ -110,7 +110,9 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     // wave index as a scalar, so that branches on it stay scalar branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int bh = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    // segment-major: the workgroups resident at once cover every head of a run of
+    // segments, so that concurrent reads of a token row (all heads of it) meet in DRAM
+    const int bh = blockIdx.x % BH, seg = blockIdx.x / BH;
     const int b = bh / H, h = bh % H;
     const int c0 = seg * seg_len;
     const int c1 = min(nchunks, c0 + seg_len);
