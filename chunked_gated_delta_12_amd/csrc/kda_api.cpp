@@ -87,12 +87,16 @@ int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 int kda_chunk_fwd_auto_segments(int B, int T, int H, int dk, int dv) {
     if (B < 1 || T < 1 || H < 1 || !supported_d(dk) || dk != dv) return 0;
-    // Aim for >= 512 workgroups in the output pass (two per compute unit on a
-    // 256-CU part) while keeping every segment at least 16 chunks long.
+    // The map and output passes run one workgroup per compute unit: aim for one
+    // resident round of 256 workgroups (every head of a run of segments at once;
+    // at least two segments below 512 sequences, where the single-segment kernel,
+    // two workgroups per compute unit, would leave the chip half empty), keeping
+    // every segment at least 16 chunks long.
     const int64_t bh = (int64_t)B * H;
     const int64_t nchunks = ((int64_t)T + KDA_CHUNK - 1) / KDA_CHUNK;
     if (bh >= 512) return 1;
-    int64_t want = (512 + bh - 1) / bh;
+    int64_t want = (256 + bh - 1) / bh;
+    if (want < 2) want = 2;
     int64_t cap = nchunks / 16;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;

@@ -119,7 +119,8 @@ def test_workspace_formula_and_auto_segments(lib):
     B, T, H, d, P = 1, 65536, 16, 128, 32
     want = ((P - 1) * B * H * d * 2 * d + P * B * H * d * d + (T // 16) * B * H * 256) * 4
     assert kda.kda_chunk_fwd_workspace_size(B, T, H, d, d, P) == want
-    assert kda.kda_chunk_fwd_auto_segments(1, 65536, 16, 128, 128) == 32
+    assert kda.kda_chunk_fwd_auto_segments(1, 65536, 16, 128, 128) == 16
+    assert kda.kda_chunk_fwd_auto_segments(2, 65536, 128, 128, 128) == 2
     assert kda.kda_chunk_fwd_auto_segments(64, 4096, 16, 128, 128) == 1
     assert kda.kda_chunk_fwd_auto_segments(1, 64, 1, 16, 16) == 1       # too short to split
     assert kda.kda_chunk_fwd_auto_segments(1, 64, 1, 24, 24) <= 0       # unsupported size
