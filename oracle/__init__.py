@@ -50,6 +50,8 @@ def _load():
         lib.kda_oracle_gate.argtypes = [ctypes.c_long, dp, dp]
         lib.kda_oracle_gate.restype = None
         lib.kda_oracle_output_gate.argtypes = [ctypes.c_long, dp, dp, dp]
+        lib.kda_oracle_gate_softplus.argtypes = [ctypes.c_long, dp, dp]
+        lib.kda_oracle_gate_softplus.restype = None
         lib.kda_oracle_output_gate.restype = None
         lib.kda_oracle_gate_cumsum.argtypes = [ctypes.c_int] * 4 + [dp, dp]
         lib.kda_oracle_gate_cumsum.restype = None
@@ -90,6 +92,20 @@ def gate(theta):
     g = np.empty_like(th)
     _load().kda_oracle_gate(th.size, _p(th), _p(g))
     return g
+
+
+def gate_softplus(theta):
+    """g = -softplus(theta) = -ln(1 + e^theta), elementwise, float64: the
+    unbounded log-decay the bounded gate replaces (ablation of the bound)."""
+    th = _d(theta)
+    g = np.empty_like(th)
+    _load().kda_oracle_gate_softplus(th.size, _p(th), _p(g))
+    return g
+
+
+def chunk_fwd_unbounded(q, k, v, theta, beta, S0=None, cols=None, nthreads=None):
+    """The recurrence with the unbounded gate g = -softplus(theta)."""
+    return recurrence(q, k, v, gate_softplus(theta), beta, S0, cols=cols, nthreads=nthreads)
 
 
 def output_gate(o, z):

@@ -31,6 +31,13 @@
  *        o_t  = S^T q_t                                 (output read)
  *    The decode step is this body for one token with S updated in place.
  *
+ *  - Unbounded gate, for the ablation of the bound ("Kimi K3 Deep Dive...",
+ *    "The Design: Putting a Lower Bound on Log-Decay", which names the
+ *    conventional log-decay it replaces as the negative softplus of the gate
+ *    input; "Architecture Deep Dive: Kimi K3...", section 3.1):
+ *        g_t = -softplus(theta_t) = -ln(1 + e^{theta_t}),
+ *    with range (-inf, 0).  It enters the same recurrence below.
+ *
  *  - Output gate ("Kimi K3" explainer, "Across the sequence": the output of
  *    each attention layer is scaled per channel and per token by a learned,
  *    input-dependent sigmoid gate before it rejoins the residual stream).
@@ -64,6 +71,16 @@ static double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 /* g = g_min * sigmoid(theta), elementwise over n values. */
 void kda_oracle_gate(long n, const double* theta, double* g) {
     for (long i = 0; i < n; ++i) g[i] = ORACLE_G_MIN * oracle_sigmoid(theta[i]);
+}
+
+/* g = -softplus(theta) = -ln(1 + e^theta), elementwise over n values.  Written
+ * as max(theta, 0) + ln(1 + e^{-|theta|}), which is the same quantity and stays
+ * finite for every finite theta. */
+void kda_oracle_gate_softplus(long n, const double* theta, double* g) {
+    for (long i = 0; i < n; ++i) {
+        const double x = theta[i];
+        g[i] = -((x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))));
+    }
 }
 
 /* Output gate: out = o * sigmoid(z), elementwise over n values (out may be o). */

@@ -75,6 +75,59 @@ def test_gate_range_and_monotone(oracle_mod):
     np.testing.assert_allclose(g + g[::-1], -5.0, rtol=0, atol=1e-14)
 
 
+# ----------------------------------------------------------------------------- unbounded gate
+# The ablation of the bound: the conventional log-decay -softplus(theta) ("Kimi K3 Deep
+# Dive...", "The Design: Putting a Lower Bound on Log-Decay").
+def test_softplus_gate_special_values(oracle_mod):
+    # 1 + e^theta = 2, e, 4, 4/3 at theta = 0, ln(e - 1), ln 3, -ln 3
+    th = np.array([0.0, math.log(math.e - 1.0), math.log(3.0), -math.log(3.0), 800.0, -800.0])
+    g = oracle_mod.gate_softplus(th)
+    np.testing.assert_allclose(g[:4], [-math.log(2.0), -1.0, -math.log(4.0), -math.log(4.0 / 3.0)],
+                               rtol=0, atol=1e-15)
+    assert g[4] == -800.0                   # no overflow of e^theta, and no lower bound
+    assert -1e-300 < g[5] <= 0.0            # vanishing forgetting for very negative theta
+
+
+def test_softplus_gate_identity_and_unbounded(oracle_mod):
+    th = np.linspace(-40, 40, 1601)
+    g = oracle_mod.gate_softplus(th)
+    # softplus(x) - softplus(-x) = x
+    np.testing.assert_allclose(g - g[::-1], -th, rtol=0, atol=1e-13)
+    assert np.all(g <= 0.0) and np.all(np.diff(g) < 0)
+    # below every bound: g <= -theta for theta > 0, and equal to -theta up to e^-theta
+    pos = th > 0
+    assert np.all(g[pos] <= -th[pos])
+    np.testing.assert_allclose(g[th >= 35], -th[th >= 35], rtol=0, atol=1e-14)
+    # agrees with an independent library softplus, ln(e^0 + e^theta)
+    np.testing.assert_allclose(g, -np.logaddexp(0.0, th), rtol=1e-15, atol=1e-15)
+
+
+def test_unbounded_gate_breaks_the_bf16_bound(oracle_mod):
+    """With the unbounded gate a 16-token inverse decay exceeds bf16 on the decay-stress
+    workload's gate inputs (theta ~ N(8, 1), g ~ -8 per token), which is why its diagonal
+    tiles need the position-wise path; the bounded gate keeps the same inputs within e^80."""
+    w = kin.scaled(kin.WORKLOADS["decay_stress"], T=512, H=4)
+    th = kin.chunk_inputs(w)["theta"]
+    G = oracle_mod.gate_cumsum(oracle_mod.gate_softplus(th))
+    assert -G.min() > math.log(torch.finfo(torch.bfloat16).max)
+    assert oracle_mod.gate_cumsum(oracle_mod.gate(th)).min() >= -80.0
+
+
+def test_unbounded_beta_zero_is_pure_decay(oracle_mod):
+    # beta = 0: o_t = S0^T (exp(Ghat_t) * q_t), Ghat the sum of -softplus(theta) from the
+    # sequence start (numpy's logaddexp as the softplus)
+    rng = np.random.default_rng(33)
+    B, T, H, d = 1, 40, 2, 6
+    q, k = rng.standard_normal((B, T, H, d)), rng.standard_normal((B, T, H, d))
+    v, th = rng.standard_normal((B, T, H, d)), rng.standard_normal((B, T, H, d))
+    S0 = rng.standard_normal((B, H, d, d))
+    o, S_T = oracle_mod.chunk_fwd_unbounded(q, k, v, th, np.zeros((B, T, H)), S0)
+    Gh = np.cumsum(-np.logaddexp(0.0, th), axis=1)
+    ref = np.einsum("bhcj,bthc->bthj", S0, np.exp(Gh) * q)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S_T, np.exp(Gh[:, -1])[..., None] * S0, rtol=1e-12, atol=1e-14)
+
+
 # ----------------------------------------------------------------------------- output gate
 # "Kimi K3" explainer, "Across the sequence": each attention output is scaled per
 # channel and token by a sigmoid gate, o' = o * sigmoid(z).
