@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the timing of the calls with the output gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the timing of the unbounded-gate ablation (kda_chunk_fwd_unbounded)")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, run one elementwise copy of MIB MiB (for counter scaling)")
@@ -256,6 +258,35 @@ def main():
                                             "algorithmic_bytes": gdby}
             del zd
         del S, tok
+
+    if not args.no_ablation:
+        # What the bound buys: the same batch-parallel prefill (one segment, 512 sequences
+        # filling the chip) with the bounded gate (dense matrix-core diagonal tiles) and with
+        # the unbounded -softplus gate (position-wise fp32 diagonal tiles).
+        aw = kin.scaled(w, B=32, T=4096)
+        ax = kin.chunk_inputs(aw, device=dev)
+        ao = torch.empty((aw.B, aw.T, aw.H, aw.dv), device=dev, dtype=ax["q"].dtype)
+        aS = torch.empty((aw.B, aw.H, aw.dk, aw.dv), device=dev, dtype=torch.float32)
+        aseg = kda.kda_chunk_fwd_auto_segments(aw.B, aw.T, aw.H, aw.dk, aw.dv)
+
+        def bstep():
+            kda.kda_chunk_fwd(ax["q"], ax["k"], ax["v"], ax["theta"], ax["beta"], ax["S0"], segments=aseg,
+                              o=ao, S_T=aS, stream=stream)
+
+        def ustep():
+            kda.kda_chunk_fwd_unbounded(ax["q"], ax["k"], ax["v"], ax["theta"], ax["beta"], ax["S0"],
+                                        o=ao, S_T=aS, stream=stream)
+
+        bms, _ = time_calls(bstep, 20, 20, stream)
+        ums, _ = time_calls(ustep, 20, 20, stream)
+        ntok = aw.B * aw.T
+        out["ablation"] = {"workload": f"B={aw.B} H={aw.H} T={aw.T} d={aw.dk} {aw.dtype}, "
+                                       f"theta N({aw.theta_mu},{aw.theta_sigma}), {aseg} segment(s)",
+                           "bounded_call": "kda_chunk_fwd", "unbounded_call": "kda_chunk_fwd_unbounded",
+                           "bounded_ms": bms, "unbounded_ms": ums, "unbounded_vs_bounded": ums / bms,
+                           "bounded_tokens_per_s": ntok / (bms * 1e-3),
+                           "unbounded_tokens_per_s": ntok / (ums * 1e-3)}
+        del ax, ao, aS
 
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration, dev)

@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step.restype = c_int
     lib.kda_chunk_fwd_gated.argtypes = [c_int] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, fp, vp, c_size, vp]
     lib.kda_chunk_fwd_gated.restype = c_int
+    lib.kda_chunk_fwd_unbounded.argtypes = [c_int] * 6 + [vp] * 3 + [fp] * 3 + [vp, fp, vp]
+    lib.kda_chunk_fwd_unbounded.restype = c_int
     lib.kda_decode_step_gated.argtypes = [c_int] * 5 + [vp] * 3 + [fp] * 3 + [vp, vp, vp]
     lib.kda_decode_step_gated.restype = c_int
     lib.kda_gate.argtypes = [c_int] * 4 + [fp, fp, fp, vp]
@@ -141,7 +143,15 @@ def kda_chunk_fwd_gated(q, k, v, theta, beta, z, S0=None, *, segments=0, o=None,
     return _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream)
 
 
-def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream):
+def kda_chunk_fwd_unbounded(q, k, v, theta, beta, S0=None, *, o=None, S_T=None, want_state=True,
+                            stream=None):
+    """The ablation of the bound: the recurrence with the unbounded gate
+    g = -softplus(theta) and position-wise fp32 diagonal tiles (one segment)."""
+    return _chunk_fwd(q, k, v, theta, beta, S0, None, 1, o, S_T, want_state, None, stream, unbounded=True)
+
+
+def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream,
+               unbounded=False):
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -163,11 +173,15 @@ def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, worksp
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     if S_T is not None:
         _need(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
-    nbytes = kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments)
+    nbytes = 0 if unbounded else kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if z is None:
+    if unbounded:
+        st = lib.kda_chunk_fwd_unbounded(code, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
+                                         _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _stream(q, stream))
+        _check("kda_chunk_fwd_unbounded", st)
+    elif z is None:
         st = lib.kda_chunk_fwd(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
                                _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
                                _stream(q, stream))
@@ -240,6 +254,7 @@ def kda_gate(theta, *, g=True, g_cum=True, stream=None):
     return g, g_cum
 
 
-__all__ = ["kda_chunk_fwd", "kda_decode_step", "kda_gate", "kda_chunk_fwd_workspace_size",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_unbounded", "kda_decode_step",
+           "kda_decode_step_gated", "kda_gate", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_auto_segments", "load_library", "header_functions", "KdaError",
            "KDA_BF16", "KDA_F32", "KDA_CHUNK", "KDA_G_MIN"]

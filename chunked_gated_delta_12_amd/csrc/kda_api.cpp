@@ -117,12 +117,12 @@ int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segmen
     return ok();
 }
 
-// kda_chunk_fwd and kda_chunk_fwd_gated; z (the output gate's pre-activation)
-// is NULL for the former.
+// kda_chunk_fwd, kda_chunk_fwd_gated and kda_chunk_fwd_unbounded; z (the output
+// gate's pre-activation) is NULL for the first and the last.
 static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
                           const void* k, const void* v, const float* theta, const float* beta,
                           const float* S0, const void* z, void* o, float* S_T, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          size_t workspace_bytes, void* stream, bool unbounded = false) {
     int st = check_common(dtype, B, H, dk, dv);
     if (st) return st;
     if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
@@ -167,7 +167,7 @@ static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int se
 
     hipError_t e = kda::launch_chunk_fwd(dtype == KDA_F32, B, T, H, dk, plan, q, k, v, theta, beta, S0,
                                          z, o, S_T, need ? workspace : nullptr,
-                                         reinterpret_cast<hipStream_t>(stream));
+                                         reinterpret_cast<hipStream_t>(stream), unbounded);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }
@@ -187,6 +187,13 @@ int kda_chunk_fwd_gated(int dtype, int B, int T, int H, int dk, int dv, int segm
     if (!z) return fail(KDA_ERR_NULL, "z must be non-NULL");
     return chunk_fwd_impl(dtype, B, T, H, dk, dv, segments, q, k, v, theta, beta, S0, z, o, S_T,
                           workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_unbounded(int dtype, int B, int T, int H, int dk, int dv, const void* q, const void* k,
+                            const void* v, const float* theta, const float* beta, const float* S0,
+                            void* o, float* S_T, void* stream) {
+    return chunk_fwd_impl(dtype, B, T, H, dk, dv, 1, q, k, v, theta, beta, S0, nullptr, o, S_T, nullptr, 0,
+                          stream, true);
 }
 
 // kda_decode_step and kda_decode_step_gated; z is NULL for the former.

@@ -66,7 +66,9 @@ struct ChunkCfg {
     static_assert(PPT == 1 || PPT == 2 || PPT == 4, "gate stage column writes");
 };
 
-template <typename E, int D, int NW>
+// UNB: the ablation with the unbounded gate, which also keeps the raw q tile and
+// the in-chunk cumulative log-decay (base 2) for the position-wise diagonal tiles.
+template <typename E, int D, int NW, bool UNB = false>
 struct ChunkSmem {
     typedef ChunkCfg<D, NW> C;
     static constexpr int LDP = Ops<E>::PAD_ROW;    // padded K = 16 operand rows
@@ -75,7 +77,7 @@ struct ChunkSmem {
     // C::LDR, whose rows are 16-byte aligned for the o stores
     static constexpr int LDQ = sizeof(E) == 2 ? D + 4 : D + 8;
     alignas(16) E kn_row[16 * LDQ];                // -K+ = -K*Gamma           [token][ch]
-    alignas(16) E km_row[16 * LDQ];                // K- = K/Gamma             [token][ch]
+    alignas(16) E km_row[16 * LDQ];                // K- = K/Gamma (UNB: raw K) [token][ch]
     alignas(16) E qp_row[16 * LDQ];                // Q+ = Q*Gamma             [token][ch]
     alignas(16) E o_tile[16 * C::LDR];             // o of the chunk           [token][col]
     alignas(16) E ke_pad[D * LDP];                 // Kend^T, padded           [ch][token]
@@ -84,6 +86,8 @@ struct ChunkSmem {
     alignas(16) E aqk_pad[16 * LDP];               // LowerIncl(Q+K-^T), padded [token][token]
     alignas(16) float akk_t[16 * 20];              // StrictLower(beta K+ K-^T)^T, fp32
     alignas(16) float gc[D];                       // Gamma_C per channel
+    alignas(16) E q_row[UNB ? 16 * LDQ : 8];       // UNB: raw Q               [token][ch]
+    alignas(16) float g_row[UNB ? 16 * (D + 4) : 4];   // UNB: G2 = log2 Gamma  [token][ch]
 };
 
 // Store units of the o tile: SU bytes per thread and store (4, 8 or 16).
@@ -159,7 +163,14 @@ __device__ __forceinline__ void store_pair_runs(E* pa, E* pb, const typename Pai
 // ws_t (published by the map kernel) instead of forming A and solving for T.
 // GATE: o is scaled by the output gate sigmoid(z) ("Kimi K3" explainer,
 // "Across the sequence"); z has o's layout.
-template <typename E, int D, int NW, bool TWS, bool GATE>
+// UNB: the ablation of the bound -- the conventional unbounded log-decay
+// g = -softplus(theta) ("Kimi K3 Deep Dive...", "The Design: Putting a Lower
+// Bound on Log-Decay").  K- = K/Gamma is then unbounded and may overflow, so
+// the two diagonal tiles are formed position by position in fp32 from the raw
+// K, Q and the cumulative log-decay ("Architecture Deep Dive: Kimi K3...",
+// section 3.1): A[t][s] = sum_c x_t[c] k_s[c] 2^(G2_t[c] - G2_s[c]), s <= t, whose
+// exponents are never positive.  Every other factor stays <= 1.
+template <typename E, int D, int NW, bool TWS, bool GATE, bool UNB = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(8 / NW)))
 chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
@@ -167,8 +178,9 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
              const float* S0, const float* __restrict__ ws_start,
              const E* ws_t, const E* __restrict__ z, E* __restrict__ o, float* S_T) {
     typedef ChunkCfg<D, NW> C;
-    typedef ChunkSmem<E, D, NW> SM;
+    typedef ChunkSmem<E, D, NW, UNB> SM;
     typedef Ops<E> MM;
+    static_assert(!UNB || (!TWS && !GATE && C::NTHR == 256), "the ablation runs one segment, one thread per tile entry");
     typedef typename MM::BFrag BFrag;
     typedef typename MM::PFrag PFrag;
     constexpr int LDP = SM::LDP;
@@ -337,8 +349,15 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         float run0 = 0.0f, run1 = 0.0f;
 #pragma unroll
         for (int p = 0; p < C::PPT; ++p) {
-            float ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * cur.th[p][0]));
-            float gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * cur.th[p][1]));
+            float ga, gb;
+            if constexpr (UNB) {   // -softplus(theta) log2(e) = -(max(theta, 0) log2(e) + log2(1 + 2^(-|theta| log2(e))))
+                const float x0 = cur.th[p][0], x1 = cur.th[p][1];
+                ga = -(fmaxf(x0, 0.0f) * LOG2E + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * fabsf(x0))));
+                gb = -(fmaxf(x1, 0.0f) * LOG2E + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * fabsf(x1))));
+            } else {
+                ga = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * cur.th[p][0]));
+                gb = GMIN2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * cur.th[p][1]));
+            }
             if (PARTIAL || !ALL_ACT) {
                 const bool ok = gact && (!PARTIAL || t0 + pgi * C::PPT + p < T);
                 ga = ok ? ga : 0.0f;
@@ -372,7 +391,6 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 const int pos = pgi * C::PPT + p;
                 const float Ga = G0[p] + off0, Gb = G1[p] + off1;
                 const float eGa = __builtin_amdgcn_exp2f(Ga), eGb = __builtin_amdgcn_exp2f(Gb);
-                const float emGa = __builtin_amdgcn_exp2f(-Ga), emGb = __builtin_amdgcn_exp2f(-Gb);
                 float ka = to_f(cur.k[p][0]), kb = to_f(cur.k[p][1]);
                 float qa = to_f(cur.q[p][0]), qb = to_f(cur.q[p][1]);
                 vr[p] = cur.v[p];
@@ -380,11 +398,22 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                     ka = kb = qa = qb = 0.0f;
                     vr[p][0] = vr[p][1] = from_f<E>(0.0f);
                 }
-                const float kma = ka * emGa, kmb = kb * emGb;
-                kea[p] = kma * eC0;                 // k * exp(G_C - G), every factor <= 1 in range
-                keb[p] = kmb * eC1;
+                if constexpr (UNB) {
+                    // Kend = k 2^(G_C - G) directly (1/Gamma may overflow); raw k, q and G2
+                    // for the position-wise diagonal tiles
+                    kea[p] = ka * __builtin_amdgcn_exp2f(tot0 - Ga);
+                    keb[p] = kb * __builtin_amdgcn_exp2f(tot1 - Gb);
+                    store_pair(&sm.km_row[pos * SM::LDQ + ch], ka, kb);
+                    store_pair(&sm.q_row[pos * SM::LDQ + ch], qa, qb);
+                    *reinterpret_cast<f32x2*>(&sm.g_row[pos * (D + 4) + ch]) = f32x2{Ga, Gb};
+                } else {
+                    const float emGa = __builtin_amdgcn_exp2f(-Ga), emGb = __builtin_amdgcn_exp2f(-Gb);
+                    const float kma = ka * emGa, kmb = kb * emGb;
+                    kea[p] = kma * eC0;                 // k * exp(G_C - G), every factor <= 1 in range
+                    keb[p] = kmb * eC1;
+                    store_pair(&sm.km_row[pos * SM::LDQ + ch], kma, kmb);
+                }
                 store_pair(&sm.kn_row[pos * SM::LDQ + ch], -ka * eGa, -kb * eGb);
-                store_pair(&sm.km_row[pos * SM::LDQ + ch], kma, kmb);
                 store_pair(&sm.qp_row[pos * SM::LDQ + ch], qa * eGa, qb * eGb);
             }
             const int pos0 = pgi * C::PPT;
@@ -409,7 +438,40 @@ chunk_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         // for every column tile, overlapped with the triangular solve:
         //   Y   = beta*(V - K+ S)      (so that U = T Y = Ut - W S)
         //   O1^T = S^T Q+^T
-        if (!TWS && wave == 0) {
+        if constexpr (UNB) {
+            // Position-wise diagonal tiles in fp32: thread (t, s) forms A[t][s] and
+            // A_qk[t][s] for s <= t; both share the decay weight of every channel.
+            const int tt = tid >> 4, ss = tid & 15;
+            float dkk = 0.0f, dqk = 0.0f;
+            if (ss <= tt) {
+                const float* Gt = &sm.g_row[tt * (D + 4)];
+                const float* Gs = &sm.g_row[ss * (D + 4)];
+                const E* kt = &sm.km_row[tt * SM::LDQ];
+                const E* ks = &sm.km_row[ss * SM::LDQ];
+                const E* qt = &sm.q_row[tt * SM::LDQ];
+                for (int c = 0; c < D; c += 4) {
+                    const f32x4 gt = *reinterpret_cast<const f32x4*>(Gt + c);
+                    const f32x4 gs = *reinterpret_cast<const f32x4*>(Gs + c);
+                    const auto k4t = ld_quad(kt + c), k4s = ld_quad(ks + c), q4t = ld_quad(qt + c);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float kw = to_f(k4s[i]) * __builtin_amdgcn_exp2f(gt[i] - gs[i]);   // weight <= 1
+                        dkk = fmaf(to_f(k4t[i]), kw, dkk);
+                        dqk = fmaf(to_f(q4t[i]), kw, dqk);
+                    }
+                }
+            }
+            // beta of row tt: lanes 16*wave .. hold beta of rows 4*wave + i in b_l[i]
+            float bt = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = __shfl(b_l[i], 16 * wave);
+                bt = (tt - 4 * wave == i) ? x : bt;
+            }
+            sm.akk_t[ss * 20 + tt] = ss < tt ? bt * dkk : 0.0f;
+            sm.aqk_pad[tt * LDP + 8 * (ss >> 2) + (ss & 3)] = from_f<E>(ss <= tt ? dqk : 0.0f);
+            lds_barrier();
+        } else if (!TWS && wave == 0) {
             // A = StrictLower(beta K+ K-^T), kept transposed in LDS: akk_t[col][row]
             const f32x4 a = MM::template mm_ll<D>(sm.kn_row, SM::LDQ, sm.km_row, SM::LDQ,
                                                   f32x4{0, 0, 0, 0}, r, g);
@@ -739,8 +801,15 @@ template <typename E, int D>
 static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const void* q,
                                  const void* k, const void* v, const float* theta,
                                  const float* beta, const float* S0, const void* z, void* o,
-                                 float* S_T, void* workspace, hipStream_t stream) {
+                                 float* S_T, void* workspace, hipStream_t stream, bool unbounded) {
     const int BH = B * H;
+    if (unbounded) {   // the ablation: one segment, no output gate
+        hipLaunchKernelGGL((chunk_kernel<E, D, CHUNK_NW_OUT, false, false, true>), dim3((unsigned)BH),
+                           dim3(64 * CHUNK_NW_OUT), 0, stream, T, H, BH, p.nchunks, p.nchunks, 1,
+                           (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const float*)nullptr,
+                           (const E*)nullptr, (const E*)nullptr, (E*)o, S_T);
+        return hipGetLastError();
+    }
     float* ws_start = nullptr;
     E* ws_t = nullptr;
     if (p.nseg > 1) {
@@ -782,9 +851,9 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,
                             const float* beta, const float* S0, const void* z, void* o, float* S_T,
-                            void* workspace, hipStream_t stream) {
+                            void* workspace, hipStream_t stream, bool unbounded) {
 #define KDA_CH(E, D) \
-    return launch_chunk_t<E, D>(B, T, H, plan, q, k, v, theta, beta, S0, z, o, S_T, workspace, stream)
+    return launch_chunk_t<E, D>(B, T, H, plan, q, k, v, theta, beta, S0, z, o, S_T, workspace, stream, unbounded)
     if (f32) {
         switch (d) {
             case 16: KDA_CH(float, 16);

@@ -46,9 +46,11 @@ hipError_t launch_chunk_out(int B, int T, int H, int d, const SegPlan& plan, con
                             const void* z, void* o, float* S_T, hipStream_t stream);
 
 // z: pre-activation of the output gate (o's layout and type), or NULL for none.
+// unbounded: the ablation with the gate -softplus(theta) and position-wise fp32
+// diagonal tiles (one segment, z NULL).
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,
                             const float* beta, const float* S0, const void* z, void* o, float* S_T,
-                            void* workspace, hipStream_t stream);
+                            void* workspace, hipStream_t stream, bool unbounded = false);
 
 }  // namespace kda

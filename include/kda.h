@@ -122,6 +122,27 @@ int kda_chunk_fwd_gated(int dtype, int B, int T, int H, int dk, int dv, int segm
                         const void* z, void* o, float* S_T,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * kda_chunk_fwd_unbounded: the ablation of the bound.  The same recurrence
+ * with the conventional unbounded log-decay that the bounded gate replaces
+ * ("Kimi K3 Deep Dive...", "The Design: Putting a Lower Bound on Log-Decay"):
+ *     g = -softplus(theta) = -ln(1 + e^theta),   range (-inf, 0)
+ * instead of KDA_G_MIN*sigmoid(theta).  The inverse cumulative decay inside a
+ * chunk is then unbounded and can overflow any floating-point type, so the two
+ * diagonal tiles are formed position by position in fp32 ("Architecture Deep
+ * Dive...", section 3.1) instead of as matrix products; everything else is the
+ * chunked evaluation of kda_chunk_fwd.  It exists to measure what the bound
+ * buys, not for use in a model.
+ *
+ *   Arguments as kda_chunk_fwd, without segments (always one: no workspace),
+ *   with the same validation and errors.  Where the unbounded gate drives a
+ *   decay below fp32's range the result is the limit (the state forgets).
+ * ------------------------------------------------------------------------- */
+int kda_chunk_fwd_unbounded(int dtype, int B, int T, int H, int dk, int dv,
+                            const void* q, const void* k, const void* v,
+                            const float* theta, const float* beta, const float* S0,
+                            void* o, float* S_T, void* stream);
+
 /* Bytes of workspace kda_chunk_fwd needs for these sizes and this segment
  * count (0 = automatic).  Writes *bytes; returns a kda_status. */
 int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments,

@@ -104,6 +104,29 @@ def test_chunk_fwd_gated_validation(lib):
     assert call(z, o=b.addr["q"]) == ALIAS
 
 
+def test_chunk_fwd_unbounded_validation(lib):
+    """The ablation entry point runs the same host checks as kda_chunk_fwd (before any
+    HIP call) and takes no workspace."""
+    b = Bufs()
+    vp = ctypes.c_void_p
+
+    def call(dtype=0, dk=None, **over):
+        a = dict(b.addr)
+        a.update(over)
+        p = lambda n: vp(a[n]) if a[n] is not None else None
+        d = dk or b.d
+        return lib.kda_chunk_fwd_unbounded(dtype, b.B, b.T, b.H, d, d, p("q"), p("k"), p("v"),
+                                           p("theta"), p("beta"), p("S0"), p("o"), p("S_T"), None)
+
+    assert call(dtype=2) == DTYPE
+    assert call(dk=48) == SHAPE
+    for name in ("q", "k", "v", "theta", "beta", "o"):
+        assert call(**{name: None}) == NULL, name
+    assert call(theta=b.addr["theta"] + 4) == ALIGN
+    assert call(o=b.addr["v"]) == ALIAS
+    assert call(S_T=b.addr["beta"]) == ALIAS
+
+
 def test_chunk_fwd_workspace_checks(lib):
     b = Bufs(T=1024, H=2, d=64)
     need = kda.kda_chunk_fwd_workspace_size(1, 1024, 2, 64, 64, 4)
