@@ -52,6 +52,10 @@ def _load():
         lib.kda_oracle_output_gate.argtypes = [ctypes.c_long, dp, dp, dp]
         lib.kda_oracle_gate_softplus.argtypes = [ctypes.c_long, dp, dp]
         lib.kda_oracle_gate_softplus.restype = None
+        lib.kda_oracle_backward.argtypes = [ctypes.c_int] * 5 + [dp] * 14
+        lib.kda_oracle_backward.restype = ctypes.c_int
+        lib.kda_oracle_gate_backward.argtypes = [ctypes.c_long, dp, dp, dp]
+        lib.kda_oracle_gate_backward.restype = None
         lib.kda_oracle_output_gate.restype = None
         lib.kda_oracle_gate_cumsum.argtypes = [ctypes.c_int] * 4 + [dp, dp]
         lib.kda_oracle_gate_cumsum.restype = None
@@ -106,6 +110,35 @@ def gate_softplus(theta):
 def chunk_fwd_unbounded(q, k, v, theta, beta, S0=None, cols=None, nthreads=None):
     """The recurrence with the unbounded gate g = -softplus(theta)."""
     return recurrence(q, k, v, gate_softplus(theta), beta, S0, cols=cols, nthreads=nthreads)
+
+
+def backward(q, k, v, g, beta, S0, do, dS_T=None):
+    """Gradients of L = sum_t <do_t, o_t> + <dS_T, S_T> for the recurrence with log-decay
+    g given directly: dict of dq, dk, dv, dg [as the inputs], dbeta [B,T,H], dS0 [B,H,dk,dv]."""
+    q, k, v, g, beta, do = _d(q), _d(k), _d(v), _d(g), _d(beta), _d(do)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and g.shape == q.shape and v.shape == (B, T, H, dv)
+    assert beta.shape == (B, T, H) and do.shape == (B, T, H, dv)
+    S0, dS_T = _d(S0), _d(dS_T)
+    out = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(v), "dg": np.empty_like(g),
+           "dbeta": np.empty_like(beta), "dS0": np.empty((B, H, dk, dv))}
+    st = _load().kda_oracle_backward(B, T, H, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), _p(S0),
+                                     _p(do), _p(dS_T), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]),
+                                     _p(out["dg"]), _p(out["dbeta"]), _p(out["dS0"]))
+    if st:
+        raise RuntimeError(f"kda_oracle_backward failed ({st})")
+    return out
+
+
+def chunk_bwd(q, k, v, theta, beta, S0, do, dS_T=None):
+    """backward() with the bounded gate g = g_min sigmoid(theta): adds dtheta."""
+    th = _d(theta)
+    out = backward(q, k, v, gate(th), beta, S0, do, dS_T)
+    dth = np.empty_like(th)
+    _load().kda_oracle_gate_backward(th.size, _p(th), _p(out["dg"]), _p(dth))
+    out["dtheta"] = dth
+    return out
 
 
 def output_gate(o, z):

@@ -38,6 +38,20 @@
  *        g_t = -softplus(theta_t) = -ln(1 + e^{theta_t}),
  *    with range (-inf, 0).  It enters the same recurrence below.
  *
+ *  - Gradients (the backward pass a training step needs; the pages' gain is
+ *    training throughput, "Architecture Deep Dive: Kimi K3...", section 3.2).
+ *    For the scalar L = sum_t <do_t, o_t> + <dS_T, S_T>, the derivatives of L
+ *    with respect to q, k, v, g, beta and S0 follow by the chain rule through
+ *    the four steps of the recurrence below, taken in reverse token order
+ *    (P_t = Diag(exp(g_t)) S_{t-1} is the decayed state):
+ *        dS += q_t do_t^T;  dq_t = S_t do_t
+ *        du  = dS^T k_t;    dk_t = dS u_t;          dP = dS
+ *        dv_t = beta_t du;  dbeta_t = du . (v_t - P_t^T k_t)
+ *        dP -= beta_t k_t du^T;  dk_t -= beta_t P_t du
+ *        dg_t[i] = sum_j dP[i][j] P_t[i][j];  dS = Diag(exp(g_t)) dP
+ *    and dS0 is the dS left after the first token.  Through the gate,
+ *    dtheta = dg * (-5) sigmoid(theta) (1 - sigmoid(theta)).
+ *
  *  - Output gate ("Kimi K3" explainer, "Across the sequence": the output of
  *    each attention layer is scaled per channel and per token by a learned,
  *    input-dependent sigmoid gate before it rejoins the residual stream).
@@ -247,4 +261,118 @@ int kda_oracle_decode_step(int B, int H, int dk, int dv,
     free(g);
     free(S_new);
     return st;
+}
+
+/* Backward of the recurrence for one (batch, head) sequence; every state S_t is
+ * kept from a forward sweep (T*dk*dv doubles).  Layouts as the forward; do
+ * [B,T,H,dv], dS_T [B,H,dk,dv] or NULL (zero); outputs dq, dk [B,T,H,dk], dv
+ * [B,T,H,dv], dg [B,T,H,dk], dbeta [B,T,H], dS0 [B,H,dk,dv] (may be NULL). */
+int kda_oracle_backward(int B, int T, int H, int dk, int dv,
+                        const double* q, const double* k, const double* v,
+                        const double* g, const double* beta, const double* S0,
+                        const double* dout, const double* dS_T,
+                        double* dq, double* dkk, double* dvv, double* dg, double* dbeta,
+                        double* dS0) {
+    if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return 2;
+    if (!q || !k || !v || !g || !beta || !dout || !dq || !dkk || !dvv || !dg || !dbeta) return 2;
+    const size_t SS = (size_t)dk * dv;
+    double* St = (double*)malloc(sizeof(double) * SS * (size_t)(T + 1));   /* S_0 .. S_T */
+    double* U = (double*)malloc(sizeof(double) * (size_t)dv * (size_t)(T > 0 ? T : 1));
+    double* R = (double*)malloc(sizeof(double) * (size_t)dv * (size_t)(T > 0 ? T : 1));   /* P_t^T k_t */
+    double* dS = (double*)malloc(sizeof(double) * SS);
+    double* dP = (double*)malloc(sizeof(double) * SS);
+    double* P = (double*)malloc(sizeof(double) * SS);
+    double* du = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!St || !U || !R || !dS || !dP || !P || !du) {
+        free(St); free(U); free(R); free(dS); free(dP); free(P); free(du);
+        return 1;
+    }
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const size_t sh = ((size_t)b * H + h) * SS;
+            /* forward sweep, keeping S_t, u_t and P_t^T k_t */
+            for (size_t x = 0; x < SS; ++x) St[x] = S0 ? S0[sh + x] : 0.0;
+            for (int t = 0; t < T; ++t) {
+                const size_t row = ((size_t)b * T + t) * H + h;
+                const double *kt = k + row * dk, *vt = v + row * dv, *gt = g + row * dk;
+                const double* Sp = St + SS * t;
+                double* Sn = St + SS * (t + 1);
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) P[(size_t)i * dv + j] = exp(gt[i]) * Sp[(size_t)i * dv + j];
+                for (int j = 0; j < dv; ++j) {
+                    double r = 0.0;
+                    for (int i = 0; i < dk; ++i) r += P[(size_t)i * dv + j] * kt[i];
+                    R[(size_t)t * dv + j] = r;
+                    U[(size_t)t * dv + j] = beta[row] * (vt[j] - r);
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        Sn[(size_t)i * dv + j] = P[(size_t)i * dv + j] + kt[i] * U[(size_t)t * dv + j];
+            }
+            /* reverse sweep */
+            for (size_t x = 0; x < SS; ++x) dS[x] = dS_T ? dS_T[sh + x] : 0.0;
+            for (int t = T - 1; t >= 0; --t) {
+                const size_t row = ((size_t)b * T + t) * H + h;
+                const double *qt = q + row * dk, *kt = k + row * dk, *vt = v + row * dv, *gt = g + row * dk;
+                const double* dot = dout + row * dv;
+                const double* Sn = St + SS * (t + 1);
+                const double* Sp = St + SS * t;
+                const double* ut = U + (size_t)t * dv;
+                const double* rt = R + (size_t)t * dv;
+                const double bt = beta[row];
+                /* o_t = S_t^T q_t */
+                for (int i = 0; i < dk; ++i) {
+                    double a = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        dS[(size_t)i * dv + j] += qt[i] * dot[j];
+                        a += Sn[(size_t)i * dv + j] * dot[j];
+                    }
+                    dq[row * dk + i] = a;
+                }
+                /* S_t = P_t + k_t u_t^T */
+                for (int j = 0; j < dv; ++j) {
+                    double a = 0.0;
+                    for (int i = 0; i < dk; ++i) a += dS[(size_t)i * dv + j] * kt[i];
+                    du[j] = a;
+                }
+                for (int i = 0; i < dk; ++i) {
+                    double a = 0.0;
+                    for (int j = 0; j < dv; ++j) a += dS[(size_t)i * dv + j] * ut[j];
+                    dkk[row * dk + i] = a;
+                }
+                /* u_t = beta_t (v_t - P_t^T k_t) */
+                double db = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    dvv[row * dv + j] = bt * du[j];
+                    db += du[j] * (vt[j] - rt[j]);
+                }
+                dbeta[row] = db;
+                for (int i = 0; i < dk; ++i) {
+                    const double e = exp(gt[i]);
+                    double a = 0.0, dgi = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        const double Pij = e * Sp[(size_t)i * dv + j];
+                        const double dPij = dS[(size_t)i * dv + j] - bt * kt[i] * du[j];
+                        a += Pij * du[j];
+                        dgi += dPij * Pij;
+                        dP[(size_t)i * dv + j] = dPij;
+                    }
+                    dkk[row * dk + i] -= bt * a;
+                    /* P_t = Diag(exp(g_t)) S_{t-1} */
+                    dg[row * dk + i] = dgi;
+                    for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] = e * dP[(size_t)i * dv + j];
+                }
+            }
+            if (dS0) memcpy(dS0 + sh, dS, sizeof(double) * SS);
+        }
+    free(St); free(U); free(R); free(dS); free(dP); free(P); free(du);
+    return 0;
+}
+
+/* Through the gate g = g_min * sigmoid(theta): dtheta = dg * g_min sigmoid (1 - sigmoid). */
+void kda_oracle_gate_backward(long n, const double* theta, const double* dg, double* dtheta) {
+    for (long i = 0; i < n; ++i) {
+        const double s = oracle_sigmoid(theta[i]);
+        dtheta[i] = dg[i] * ORACLE_G_MIN * s * (1.0 - s);
+    }
 }
