@@ -87,6 +87,11 @@ CHUNK_CASES = [
     ("tiny", dict(T=53), None, 4),
     ("small", dict(B=3, H=2, T=16 * 9 + 3), None, 10),
     ("prefill_64k", dict(H=2, T=49), None, 4),
+    # more (segment, head) workgroups than one resident round: with an even segment
+    # count the output pass merges pairs of segments, with an odd one it runs two rounds
+    ("prefill_64k", dict(T=8192 - 11), None, 32),
+    ("prefill_64k", dict(T=4096 + 16), None, 17),
+    ("small", dict(B=8, H=8, T=2048 + 3, dk=32, dv=32), None, 6),
 ]
 
 
