@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the timing of the calls with the output gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-1m", action="store_true",
+                    help="skip the timing of the 1M-token prefill (B=1, H=16, T=2^20)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the timing of the unbounded-gate ablation (kda_chunk_fwd_unbounded)")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -258,6 +260,29 @@ def main():
                                             "algorithmic_bytes": gdby}
             del zd
         del S, tok
+
+    if not args.no_1m and w.name == "prefill_64k":
+        # The 1M-context shape: B=1, H=16, T=2^20, d=128, same distributions (16 GiB of inputs).
+        mw = kin.WORKLOADS["prefill_1m"]
+        mx = kin.chunk_inputs(mw, device=dev)
+        mseg = kda.kda_chunk_fwd_auto_segments(mw.B, mw.T, mw.H, mw.dk, mw.dv)
+        mo = torch.empty((mw.B, mw.T, mw.H, mw.dv), device=dev, dtype=mx["q"].dtype)
+        mS = torch.empty((mw.B, mw.H, mw.dk, mw.dv), device=dev, dtype=torch.float32)
+        mws = torch.empty(max(16, kda.kda_chunk_fwd_workspace_size(mw.B, mw.T, mw.H, mw.dk, mw.dv, mseg)),
+                          device=dev, dtype=torch.uint8)
+
+        def mstep():
+            kda.kda_chunk_fwd(mx["q"], mx["k"], mx["v"], mx["theta"], mx["beta"], mx["S0"], segments=mseg,
+                              o=mo, S_T=mS, workspace=mws, stream=stream)
+
+        mms, _ = time_calls(mstep, 5, 3, stream)
+        mfl, mby = prefill_work(mw.B, mw.T, mw.H, mw.dk, mw.dv, es=2, s0=mx["S0"] is not None)
+        out["prefill_1m"] = {"workload": mw.name, "B": mw.B, "H": mw.H, "T": mw.T, "d": mw.dk,
+                             "segments": mseg, "ms_per_call": mms, "tokens_per_s": mw.B * mw.T / (mms * 1e-3),
+                             "achieved": mby / (mms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": mby / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": mby,
+                             "calls_timed": 5}
+        del mx, mo, mS, mws
 
     if not args.no_ablation:
         # What the bound buys: the same batch-parallel prefill (one segment, 512 sequences
