@@ -8,7 +8,7 @@
 // each chunk's T' = (I + A)^-1 diag(beta) (ws_t).  One workgroup per (segment,
 // head) walks the segment's chunks and writes o (and S_T for the last segment).
 //
-// Wavefront roles.  Per step of NPW chunks:
+// Wavefront roles.  Per step of NPW = 2 chunks:
 //   producers  two wavefronts per chunk, one per half of the d_k channels.  A
 //              lane owns one channel pair for TPL consecutive tokens.  They form
 //              the gate g = -5 sigmoid(theta) and its decay as running products
@@ -16,15 +16,20 @@
 //              groups), the tiles -K+, Q+, Kend^T, V^T and Gamma_C, copy T', and
 //              each forms the part of A_qk = LowerIncl(Q+ K-^T) that its own
 //              channels contribute -- so the two never wait for each other.
-//              They also write out the o tiles staged two steps earlier.
-//   consumers  hold the state in fp32 accumulator registers (one 16-column tile
-//              each at d_v = 128) and run only the chain
+//              Their inputs are loaded two steps ahead (two register sets).  They
+//              also write out the o tiles staged two steps earlier, each the
+//              columns of its own channel half.
+//   consumers  hold the state in fp32 accumulator registers (two 16-column
+//              tiles each at d_v = 128) and run only the chain
 //                  Y = V - K+ S,  O1^T = S^T Q+^T,  U = T' Y,
 //                  O^T = O1^T + U^T (A_qk,0 + A_qk,1)^T,
 //                  S <- Diag(Gamma_C) S + Kend^T U,
 //              staging each o tile in LDS.
 // LDS slots are double buffered, so one workgroup barrier per step separates the
-// roles, as in the map kernel (kda_map.hip).
+// roles, as in the map kernel (kda_map.hip).  The launcher merges pairs of map
+// segments when that keeps the whole grid resident at one workgroup per compute
+// unit: concurrent reads of a token row then cover every head, which was worth
+// more than any change to the roles' arithmetic.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
