@@ -189,6 +189,9 @@ GATED_CASES = [
     ("small", {}, "f32", 4),
     ("small", dict(dk=32, dv=32, H=3, T=333), None, 3),
     ("prefill_64k", dict(H=2, T=2048 + 9), None, 0),
+    ("prefill_64k", dict(T=8192 - 11), None, 32),                 # merged segment pairs
+    ("prefill_64k", dict(T=4096 + 16), None, 17),                 # two resident rounds
+    ("tiny", dict(T=77), "bf16", 2),                              # bf16 at d = 16 (chunk_kernel)
 ]
 
 
