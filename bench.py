@@ -9,8 +9,11 @@ synthetic data already resident in HBM.  The timed region is exactly K steps
 between two device synchronisations, measured with HIP events on the stream the
 kernels run on, after W untimed warm-up calls (the clocks settle after about
 60 calls).  The same prefill with the output gate (kda_chunk_fwd_gated) is
-timed the same way and reported in the "output_gate" object.  The decode step
-(B=256, H=16 fp32 state, in place) is timed the same way and reported in the
+timed the same way and reported in the "output_gate" object.  The 1M-token
+prefill (B=1, H=16, T=2^20) is reported in "prefill_1m", and the ablation of the
+bounded gate (kda_chunk_fwd against kda_chunk_fwd_unbounded at B=32, H=16,
+T=4096, one segment) in "ablation".  The decode step (B=256, H=16 fp32 state, in
+place) is timed over 1,024 consecutive steps as one interval and reported in the
 "decode" object.  The fp64 oracle is timed on the host cores on a bounded
 sample of the same prefill ("cpu_baseline").  Prints one JSON line.
 """
@@ -132,7 +135,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--segments", type=int, default=0)
-    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--decode-steps", type=int, default=1024,
+                    help="decode steps timed as one interval (the workload is 1,024 consecutive steps)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gated", action="store_true",
                     help="skip the timing of the calls with the output gate")
