@@ -58,6 +58,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step.restype = c_int
     lib.kda_chunk_fwd_gated.argtypes = [c_int] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, fp, vp, c_size, vp]
     lib.kda_chunk_fwd_gated.restype = c_int
+    lib.kda_chunk_bwd.argtypes = [c_int] * 6 + [vp] * 3 + [fp] * 3 + [vp, fp] + [fp] * 6 + [vp, c_size, vp]
+    lib.kda_chunk_bwd.restype = c_int
+    lib.kda_chunk_bwd_workspace_size.argtypes = [c_int] * 5 + [ctypes.POINTER(c_size)]
+    lib.kda_chunk_bwd_workspace_size.restype = c_int
     lib.kda_chunk_fwd_unbounded.argtypes = [c_int] * 6 + [vp] * 3 + [fp] * 3 + [vp, fp, vp]
     lib.kda_chunk_fwd_unbounded.restype = c_int
     lib.kda_decode_step_gated.argtypes = [c_int] * 5 + [vp] * 3 + [fp] * 3 + [vp, vp, vp]
@@ -194,6 +198,50 @@ def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, worksp
     return o, S_T
 
 
+def kda_chunk_bwd_workspace_size(B, T, H, dk, dv) -> int:
+    n = ctypes.c_size_t(0)
+    _check("kda_chunk_bwd_workspace_size",
+           load_library().kda_chunk_bwd_workspace_size(B, T, H, dk, dv, ctypes.byref(n)))
+    return int(n.value)
+
+
+def kda_chunk_bwd(q, k, v, theta, beta, do, S0=None, dS_T=None, *, want_dS0=True, workspace=None,
+                  stream=None):
+    """Backward pass of kda_chunk_fwd for L = sum <do, o> + <dS_T, S_T>.  Inputs as
+    kda_chunk_fwd plus do [B,T,H,dv] (q's dtype) and dS_T [B,H,dk,dv] fp32 or None.
+    Returns a dict of fp32 tensors dq, dk, dv, dtheta, dbeta and dS0 (None unless
+    want_dS0)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(q, "q", dt, (B, T, H, dk), dev)
+    _need(k, "k", dt, (B, T, H, dk), dev)
+    _need(v, "v", dt, (B, T, H, dv), dev)
+    _need(theta, "theta", torch.float32, (B, T, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(do, "do", dt, (B, T, H, dv), dev)
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, dk, dv), dev)
+    if dS_T is not None:
+        _need(dS_T, "dS_T", torch.float32, (B, H, dk, dv), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+         "dv": torch.empty((B, T, H, dv), **f32), "dtheta": torch.empty((B, T, H, dk), **f32),
+         "dbeta": torch.empty((B, T, H), **f32),
+         "dS0": torch.empty((B, H, dk, dv), **f32) if want_dS0 else None}
+    nbytes = kda_chunk_bwd_workspace_size(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_bwd(code, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta), _ptr(beta), _ptr(S0),
+                           _ptr(do), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dtheta"]),
+                           _ptr(g["dbeta"]), _ptr(g["dS0"]), _ptr(workspace), ws_bytes, _stream(q, stream))
+    _check("kda_chunk_bwd", st)
+    return g
+
+
 def kda_decode_step(q, k, v, theta, beta, S, *, o=None, stream=None):
     """One decode step.  q, k [B,H,dk], v [B,H,dv] (bf16 or fp32), theta [B,H,dk]
     fp32, beta [B,H] fp32, S [B,H,dk,dv] fp32 (updated in place).  Returns o."""
@@ -254,7 +302,8 @@ def kda_gate(theta, *, g=True, g_cum=True, stream=None):
     return g, g_cum
 
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_unbounded", "kda_decode_step",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_unbounded", "kda_chunk_bwd",
+           "kda_chunk_bwd_workspace_size", "kda_decode_step",
            "kda_decode_step_gated", "kda_gate", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_auto_segments", "load_library", "header_functions", "KdaError",
            "KDA_BF16", "KDA_F32", "KDA_CHUNK", "KDA_G_MIN"]

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_decode.hip", "kda_chunk.hip", "kda_map.hip", "kda_out.hip"]
+SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_decode.hip", "kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -196,6 +196,57 @@ int kda_chunk_fwd_unbounded(int dtype, int B, int T, int H, int dk, int dv, cons
                           stream, true);
 }
 
+int kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, size_t* bytes) {
+    if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
+    int st = check_common(KDA_BF16, B, H, dk, dv);
+    if (st) return st;
+    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
+    *bytes = kda::chunk_bwd_workspace_bytes(B, T, H, dk);
+    return ok();
+}
+
+int kda_chunk_bwd(int dtype, int B, int T, int H, int dk, int dv, const void* q, const void* k,
+                  const void* v, const float* theta, const float* beta, const float* S0, const void* dout,
+                  const float* dS_T, float* dq, float* dkk, float* dvv, float* dtheta, float* dbeta,
+                  float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(dtype, B, H, dk, dv);
+    if (st) return st;
+    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
+    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*d too large");
+    if (!q || !k || !v || !theta || !beta || !dout || !dq || !dkk || !dvv || !dtheta || !dbeta)
+        return fail(KDA_ERR_NULL, "q, k, v, theta, beta, do and every gradient but dS0 must be non-NULL");
+    const void* all[] = {q, k, v, theta, beta, S0, dout, dS_T, dq, dkk, dvv, dtheta, dbeta, dS0, workspace};
+    const char* names[] = {"q", "k", "v", "theta", "beta", "S0", "do", "dS_T", "dq", "dk", "dv",
+                           "dtheta", "dbeta", "dS0", "workspace"};
+    for (int i = 0; i < 15; ++i)
+        if (all[i] && !aligned16(all[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const size_t need = kda::chunk_bwd_workspace_bytes(B, T, H, dk);
+    if (!workspace || workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    const size_t es = dtype == KDA_BF16 ? 2 : 4;
+    const size_t tok = (size_t)B * T * H;
+    const size_t st_bytes = (size_t)B * H * dk * dv * 4;
+    const Range in[] = {rng("q", q, tok * dk * es), rng("k", k, tok * dk * es), rng("v", v, tok * dv * es),
+                        rng("theta", theta, tok * dk * 4), rng("beta", beta, tok * 4),
+                        rng("S0", S0, S0 ? st_bytes : 0), rng("do", dout, tok * dv * es),
+                        rng("dS_T", dS_T, dS_T ? st_bytes : 0)};
+    const Range out[] = {rng("dq", dq, tok * dk * 4), rng("dk", dkk, tok * dk * 4), rng("dv", dvv, tok * dv * 4),
+                         rng("dtheta", dtheta, tok * dk * 4), rng("dbeta", dbeta, tok * 4),
+                         rng("dS0", dS0, dS0 ? st_bytes : 0), rng("workspace", workspace, need)};
+    for (const Range& o : out) {
+        for (const Range& x : in)
+            if (overlap(o, x)) return fail(KDA_ERR_ALIAS, "%s overlaps %s", o.name, x.name);
+        for (const Range& o2 : out)
+            if (&o2 != &o && overlap(o, o2)) return fail(KDA_ERR_ALIAS, "%s overlaps %s", o.name, o2.name);
+    }
+    hipError_t e = kda::launch_chunk_bwd(dtype == KDA_F32, B, T, H, dk, q, k, v, theta, beta, S0, dout, dS_T,
+                                         dq, dkk, dvv, dtheta, dbeta, dS0, workspace,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 // kda_decode_step and kda_decode_step_gated; z is NULL for the former.
 static int decode_step_impl(int dtype, int B, int H, int dk, int dv, const void* q, const void* k,
                             const void* v, const float* theta, const float* beta, float* S,

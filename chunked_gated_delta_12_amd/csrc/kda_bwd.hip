@@ -1,0 +1,394 @@
+// kda_bwd.hip -- backward pass of the chunked KDA prefill on gfx950, first version.
+//
+// Gradients of L = sum_t <do_t, o_t> + <dS_T, S_T> with respect to q, k, v, theta,
+// beta and S0, evaluated chunk by chunk.  With the forward quantities of a chunk
+// (kda_chunk.hip; "Kimi K3 Deep Dive...", "The Problem: The Diagonal-Block
+// Dilemma"; the bounded gate of "Architecture Deep Dive: Kimi K3...", section
+// 3.2) -- start state S, K+ = K*Gamma, K- = K/Gamma, Q+ = Q*Gamma, Kend =
+// K*Gamma_C/Gamma, A = StrictLower(diag(beta) K+ K-^T), T = (I + A)^-1,
+// Y = V - K+ S, U = T diag(beta) Y, A_qk = LowerIncl(Q+ K-^T) -- and the
+// gradients dO of the chunk's outputs and dS' of its end state:
+//     dU = A_qk^T dO + Kend dS',   Z = T^T dU,   dY = diag(beta) Z,   dV = dY
+//     dS = Diag(Gamma_C) dS' + Q+^T dO - K+^T dY          (to the previous chunk)
+//     dA_qk = LowerIncl(dO U^T),   dA = StrictLower(-Z U^T)
+//     dQ+ = dO S^T + dA_qk K-,     dK+ = -dY S^T + diag(beta) dA K-
+//     dK- = dA_qk^T Q+ + (diag(beta) dA)^T K+,   dKend = U dS'^T
+//     dbeta = rowsum(dA * K+ K-^T) + rowsum(Z * Y),   dGamma_C = rowsum(dS' * S)
+// then the chain through the decay scalings to K, Q and the chunk-local
+// cumulative log-decay, whose reverse prefix sum over the chunk gives dg, and
+// dtheta = dg * (-5) sigmoid(theta) (1 - sigmoid(theta)).
+//
+// One workgroup per (batch, head) walks the chunks forward, saving every chunk's
+// start state to the workspace, then backward.  The state recurrences act on
+// columns separately, so S and dS' live in registers by column (TPC threads per
+// column, RPT rows each); products over the state's columns read S rows from the
+// workspace and dS' rows from LDS; every row-space gradient element has one
+// owning thread, so results are deterministic.  All arithmetic is fp32 on the
+// vector units: this version is correct and simple, not yet tiled for the
+// matrix cores.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <int D>
+struct BwdCfg {
+    static constexpr int NTHR = 256;
+    static constexpr int TPC = NTHR / D;     // threads per state column
+    static constexpr int RPT = D / TPC;      // state rows per thread
+    static constexpr int LDS_ = D + 1;       // row stride of the staged dS'
+    // row-space work: thread owns channel i = tid / RT and tokens th*TT .. +TT-1
+    static constexpr int RT = NTHR / D;      // threads per channel
+    static constexpr int TT = CHUNK / RT;    // tokens per thread
+    static_assert(TPC >= 1 && TPC <= 16 && RT * TT == CHUNK, "mappings");
+};
+
+template <int D>
+struct BwdSmem {
+    float gam[CHUNK][D];      // Gamma
+    float kp[CHUNK][D];       // K+
+    float km[CHUNK][D];       // K-
+    float qp[CHUNK][D];       // Q+
+    float ke[CHUNK][D];       // Kend
+    float dO[CHUNK][D];       // incoming output gradient
+    float U[CHUNK][D];
+    float Z[CHUNK][D];        // T^T dU
+    float dU[CHUNK][D];       // A_qk^T dO + Kend dS'
+    float Y[CHUNK][D];        // V - K+ S
+    float dS[D * BwdCfg<D>::LDS_];   // dS' of the chunk, row-major
+    float KK[CHUNK][CHUNK];   // K+ K-^T
+    float A[CHUNK][CHUNK];    // StrictLower(diag(beta) K+ K-^T)
+    float Tm[CHUNK][CHUNK + 1];
+    float Aqk[CHUNK][CHUNK];
+    float dAqk[CHUNK][CHUNK];
+    float dA[CHUNK][CHUNK];
+    float gc[D], beta[CHUNK];
+};
+
+template <typename E, int D>
+__global__ void __launch_bounds__(256)
+bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restrict__ k,
+           const E* __restrict__ v, const float* __restrict__ theta, const float* __restrict__ beta,
+           const float* __restrict__ S0, const E* __restrict__ dout, const float* __restrict__ dS_T,
+           float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+           float* __restrict__ dtheta, float* __restrict__ dbeta, float* __restrict__ dS0,
+           float* __restrict__ ws) {
+    typedef BwdCfg<D> C;
+    __shared__ BwdSmem<D> sm;
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int64_t tstr = (int64_t)H * D;                              // elements between tokens
+    const int64_t hb = (int64_t)b * T * H * D + (int64_t)h * D;       // token 0 of this head
+    const int64_t bstr = H;                                            // beta: between tokens
+    const int64_t bb = (int64_t)b * T * H + h;
+    float* Ssave = ws + (int64_t)bh * nchunks * D * D;                 // chunk start states
+
+    // column-space mapping: column j, rows r0 .. r0 + RPT - 1
+    const int j = tid / C::TPC, pc = tid % C::TPC, r0 = pc * C::RPT;
+    // row-space mapping: channel i, tokens t0 .. t0 + TT - 1
+    const int ich = tid / C::RT, t0r = (tid % C::RT) * C::TT;
+
+    constexpr float LOG2E = 1.4426950408889634f;
+
+    float S[C::RPT], dS[C::RPT];
+#pragma unroll
+    for (int r = 0; r < C::RPT; ++r) {
+        S[r] = S0 ? S0[((int64_t)bh * D + r0 + r) * D + j] : 0.0f;
+        dS[r] = dS_T ? dS_T[((int64_t)bh * D + r0 + r) * D + j] : 0.0f;
+    }
+
+    // sum over the TPC threads of one column (adjacent lanes)
+    auto colsum = [&](float x) {
+#pragma unroll
+        for (int o = 1; o < C::TPC; o <<= 1) x += __shfl_xor(x, o);
+        return x;
+    };
+
+    // gate, decay tiles and the chunk's small matrices (KK, A, T, A_qk); padding
+    // tokens of a partial chunk get g = 0, k = q = v = beta = 0
+    auto prepare = [&](int n) {
+        const int tc = n * CHUNK;
+        const int nv = min(CHUNK, T - tc);
+        if (tid < D) {
+            const int c = tid;
+            float G = 0.0f;
+            float gam[CHUNK];
+#pragma unroll
+            for (int t = 0; t < CHUNK; ++t) {
+                float g2 = 0.0f;
+                if (t < nv) {
+                    const float th = theta[hb + (tc + t) * tstr + c];
+                    g2 = G_MIN * LOG2E * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th));
+                }
+                G += g2;
+                gam[t] = __builtin_amdgcn_exp2f(G);
+            }
+            const float gC = gam[CHUNK - 1];
+#pragma unroll
+            for (int t = 0; t < CHUNK; ++t) {
+                const float kk = t < nv ? to_f(k[hb + (tc + t) * tstr + c]) : 0.0f;
+                const float qq = t < nv ? to_f(q[hb + (tc + t) * tstr + c]) : 0.0f;
+                const float ig = __builtin_amdgcn_rcpf(gam[t]);   // <= e^80: the bound
+                sm.gam[t][c] = gam[t];
+                sm.kp[t][c] = kk * gam[t];
+                sm.km[t][c] = kk * ig;
+                sm.qp[t][c] = qq * gam[t];
+                sm.ke[t][c] = kk * (gC * ig);
+            }
+            sm.gc[c] = gC;
+        }
+        if (tid < CHUNK) sm.beta[tid] = tid < nv ? beta[bb + (int64_t)(tc + tid) * bstr] : 0.0f;
+        __syncthreads();
+        {   // one (t, s) entry per thread
+            const int t = tid / CHUNK, s = tid % CHUNK;
+            float kk = 0.0f, qk = 0.0f;
+            for (int c = 0; c < D; ++c) {
+                kk = fmaf(sm.kp[t][c], sm.km[s][c], kk);
+                qk = fmaf(sm.qp[t][c], sm.km[s][c], qk);
+            }
+            sm.KK[t][s] = kk;
+            sm.A[t][s] = s < t ? sm.beta[t] * kk : 0.0f;
+            sm.Aqk[t][s] = s <= t ? qk : 0.0f;
+        }
+        __syncthreads();
+        if (tid < CHUNK) {   // T = (I + A)^-1, column tid, forward substitution
+            const int cj = tid;
+            float x[CHUNK];
+#pragma unroll
+            for (int r = 0; r < CHUNK; ++r) {
+                float a = (r == cj) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < CHUNK; ++s2)
+                    if (s2 < r) a = fmaf(-sm.A[r][s2], x[s2], a);
+                x[r] = a;
+            }
+#pragma unroll
+            for (int r = 0; r < CHUNK; ++r) sm.Tm[r][cj] = x[r];
+        }
+        __syncthreads();
+    };
+
+    // Y = V - K+ S and U = T diag(beta) Y for this thread's column, into sm.Y and sm.U
+    // (written by the first thread of the column; its partners are in the same wavefront)
+    auto forward_cols = [&](int n) {
+        const int tc = n * CHUNK;
+        const int nv = min(CHUNK, T - tc);
+        for (int t = 0; t < CHUNK; ++t) {
+            float a = 0.0f;
+#pragma unroll
+            for (int r = 0; r < C::RPT; ++r) a = fmaf(sm.kp[t][r0 + r], S[r], a);
+            a = colsum(a);
+            const float vv = t < nv ? to_f(v[hb + (tc + t) * tstr + j]) : 0.0f;
+            if (pc == 0) sm.Y[t][j] = vv - a;
+        }
+        wave_lds_sync();
+        for (int t = 0; t < CHUNK; ++t) {
+            float a = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < CHUNK; ++s2) a = fmaf(sm.Tm[t][s2], sm.beta[s2] * sm.Y[s2][j], a);
+            if (pc == 0) sm.U[t][j] = a;
+        }
+        wave_lds_sync();
+    };
+
+    // ---------------- forward sweep: save every chunk's start state
+    for (int n = 0; n < nchunks; ++n) {
+        prepare(n);
+#pragma unroll
+        for (int r = 0; r < C::RPT; ++r) Ssave[((int64_t)n * D + r0 + r) * D + j] = S[r];
+        forward_cols(n);
+#pragma unroll
+        for (int r = 0; r < C::RPT; ++r) S[r] *= sm.gc[r0 + r];
+        for (int t = 0; t < CHUNK; ++t) {
+            const float u = sm.U[t][j];
+#pragma unroll
+            for (int r = 0; r < C::RPT; ++r) S[r] = fmaf(sm.ke[t][r0 + r], u, S[r]);
+        }
+        __syncthreads();   // before the next chunk's tiles overwrite these
+    }
+
+    // ---------------- backward sweep
+    for (int n = nchunks - 1; n >= 0; --n) {
+        const int tc = n * CHUNK;
+        const int nv = min(CHUNK, T - tc);
+        prepare(n);
+        for (int x = tid; x < CHUNK * D; x += C::NTHR) {
+            const int t = x / D, c = x % D;
+            sm.dO[t][c] = t < nv ? to_f(dout[hb + (tc + t) * tstr + c]) : 0.0f;
+        }
+        const float* Sn = Ssave + (int64_t)n * D * D;
+#pragma unroll
+        for (int r = 0; r < C::RPT; ++r) {
+            S[r] = Sn[(r0 + r) * D + j];
+            sm.dS[(r0 + r) * C::LDS_ + j] = dS[r];
+        }
+        __syncthreads();
+
+        forward_cols(n);
+        // dU = A_qk^T dO + Kend dS',  Z = T^T dU,  dV = dY = diag(beta) Z
+        for (int t = 0; t < CHUNK; ++t) {
+            float a = 0.0f;
+#pragma unroll
+            for (int r = 0; r < C::RPT; ++r) a = fmaf(sm.ke[t][r0 + r], dS[r], a);
+            a = colsum(a);
+#pragma unroll
+            for (int s2 = 0; s2 < CHUNK; ++s2) a = fmaf(sm.Aqk[s2][t], sm.dO[s2][j], a);
+            if (pc == 0) sm.dU[t][j] = a;
+        }
+        wave_lds_sync();
+        for (int t = 0; t < CHUNK; ++t) {
+            float a = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < CHUNK; ++s2) a = fmaf(sm.Tm[s2][t], sm.dU[s2][j], a);
+            if (pc == 0) {
+                sm.Z[t][j] = a;
+                if (t < nv) dv[hb + (tc + t) * tstr + j] = sm.beta[t] * a;
+            }
+        }
+        wave_lds_sync();
+        // dS <- Diag(Gamma_C) dS' + Q+^T dO - K+^T dY   (dS' itself is staged in LDS)
+#pragma unroll
+        for (int r = 0; r < C::RPT; ++r) dS[r] *= sm.gc[r0 + r];
+        for (int t = 0; t < CHUNK; ++t) {
+            const float o = sm.dO[t][j], zy = sm.beta[t] * sm.Z[t][j];
+#pragma unroll
+            for (int r = 0; r < C::RPT; ++r) dS[r] = fmaf(sm.qp[t][r0 + r], o, fmaf(-sm.kp[t][r0 + r], zy, dS[r]));
+        }
+        __syncthreads();
+
+        {   // dA_qk = LowerIncl(dO U^T), dA = StrictLower(-Z U^T): one (t, s) entry per thread
+            const int t = tid / CHUNK, s = tid % CHUNK;
+            float a = 0.0f, z = 0.0f;
+            for (int c = 0; c < D; ++c) {
+                a = fmaf(sm.dO[t][c], sm.U[s][c], a);
+                z = fmaf(sm.Z[t][c], sm.U[s][c], z);
+            }
+            sm.dAqk[t][s] = s <= t ? a : 0.0f;
+            sm.dA[t][s] = s < t ? -z : 0.0f;
+        }
+        __syncthreads();
+        if (tid < CHUNK) {   // dbeta
+            const int t = tid;
+            float a = 0.0f;
+            for (int s2 = 0; s2 < CHUNK; ++s2) a = fmaf(sm.dA[t][s2], sm.KK[t][s2], a);
+            for (int c = 0; c < D; ++c) a = fmaf(sm.Z[t][c], sm.Y[t][c], a);
+            if (t < nv) dbeta[bb + (int64_t)(tc + t) * bstr] = a;
+        }
+
+        {   // row space: channel ich, tokens t0r .. t0r + TT - 1
+            const int c = ich;
+            const float* Srow = Sn + (int64_t)c * D;
+            const float* dSrow = &sm.dS[c * C::LDS_];
+            // the products over the state's columns, each S and dS' row element read once
+            float dgc = 0.0f;
+            float dqp[C::TT], dkp[C::TT], dke[C::TT];
+#pragma unroll
+            for (int u = 0; u < C::TT; ++u) dqp[u] = dkp[u] = dke[u] = 0.0f;
+            for (int jj = 0; jj < D; ++jj) {
+                const float sv = Srow[jj], dsv = dSrow[jj];
+                dgc = fmaf(dsv, sv, dgc);
+#pragma unroll
+                for (int u = 0; u < C::TT; ++u) {
+                    const int t = t0r + u;
+                    dqp[u] = fmaf(sm.dO[t][jj], sv, dqp[u]);
+                    dkp[u] = fmaf(-sm.beta[t] * sm.Z[t][jj], sv, dkp[u]);
+                    dke[u] = fmaf(sm.U[t][jj], dsv, dke[u]);
+                }
+            }
+            float dG[C::TT], kesum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < C::TT; ++u) {
+                const int t = t0r + u;
+                float dkm = 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < CHUNK; ++s2) {
+                    dqp[u] = fmaf(sm.dAqk[t][s2], sm.km[s2][c], dqp[u]);
+                    dkp[u] = fmaf(sm.beta[t] * sm.dA[t][s2], sm.km[s2][c], dkp[u]);
+                    dkm = fmaf(sm.dAqk[s2][t], sm.qp[s2][c], dkm);
+                    dkm = fmaf(sm.beta[s2] * sm.dA[s2][t], sm.kp[s2][c], dkm);
+                }
+                const float gm = sm.gam[t][c], gC = sm.gc[c];
+                const float ig = __builtin_amdgcn_rcpf(gm);
+                if (t < nv) {
+                    dk[hb + (tc + t) * tstr + c] = dkp[u] * gm + dkm * ig + dke[u] * (gC * ig);
+                    dq[hb + (tc + t) * tstr + c] = dqp[u] * gm;
+                }
+                const float ked = dke[u] * sm.ke[t][c];
+                kesum += ked;
+                dG[u] = dkp[u] * sm.kp[t][c] - dkm * sm.km[t][c] + dqp[u] * sm.qp[t][c] - ked;
+            }
+            // the chunk's last row also carries the end decay: d(G_C) = sum_t dKend*Kend + dGamma_C*Gamma_C
+            float ktot = kesum;
+#pragma unroll
+            for (int o = 1; o < C::RT; o <<= 1) ktot += __shfl_xor(ktot, o);
+            if (t0r + C::TT == CHUNK) dG[C::TT - 1] += ktot + dgc * sm.gc[c];
+            // reverse prefix sum over the chunk's tokens: within the thread, then across
+            // the RT threads of the channel (adjacent lanes, later tokens in higher lanes)
+            float suf = 0.0f;
+#pragma unroll
+            for (int u = C::TT - 1; u >= 0; --u) {
+                suf += dG[u];
+                dG[u] = suf;
+            }
+            // the totals of the threads of this channel that hold later tokens
+            const int rl = tid % C::RT;
+            float later = 0.0f;
+#pragma unroll
+            for (int o = 1; o < C::RT; ++o) {
+                const float x = __shfl_down(suf, o);
+                if (rl + o < C::RT) later += x;
+            }
+#pragma unroll
+            for (int u = 0; u < C::TT; ++u) {
+                const int t = t0r + u;
+                if (t < nv) {
+                    const float th = theta[hb + (tc + t) * tstr + c];
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th));
+                    dtheta[hb + (tc + t) * tstr + c] = (dG[u] + later) * G_MIN * sg * (1.0f - sg);
+                }
+            }
+        }
+        __syncthreads();   // before the next chunk overwrites the tiles
+    }
+    if (dS0) {
+#pragma unroll
+        for (int r = 0; r < C::RPT; ++r) dS0[((int64_t)bh * D + r0 + r) * D + j] = dS[r];
+    }
+}
+
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d) {
+    const size_t nchunks = ((size_t)T + CHUNK - 1) / CHUNK;
+    return nchunks * (size_t)B * H * d * d * sizeof(float);
+}
+
+hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q, const void* k,
+                            const void* v, const float* theta, const float* beta, const float* S0,
+                            const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
+                            float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int BH = B * H;
+#define KDA_BWD(E, D)                                                                                  \
+    hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)BH), dim3(256), 0, stream, T, H, nchunks,     \
+                       (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const E*)dout, dS_T, dq, \
+                       dk, dv, dtheta, dbeta, dS0, (float*)workspace);                                  \
+    return hipGetLastError()
+    if (f32) {
+        switch (d) {
+            case 16: KDA_BWD(float, 16);
+            case 32: KDA_BWD(float, 32);
+            case 64: KDA_BWD(float, 64);
+            case 128: KDA_BWD(float, 128);
+        }
+    } else {
+        switch (d) {
+            case 16: KDA_BWD(bf16, 16);
+            case 32: KDA_BWD(bf16, 32);
+            case 64: KDA_BWD(bf16, 64);
+            case 128: KDA_BWD(bf16, 128);
+        }
+    }
+#undef KDA_BWD
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

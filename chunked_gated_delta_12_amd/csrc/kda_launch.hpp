@@ -53,4 +53,13 @@ hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan&
                             const float* beta, const float* S0, const void* z, void* o, float* S_T,
                             void* workspace, hipStream_t stream, bool unbounded = false);
 
+// Backward pass of the chunked prefill (one workgroup per sequence and head):
+// fp32 gradients dq, dk, dv, dtheta, dbeta and dS0 (nullable); the workspace
+// holds every chunk's start state (chunk_bwd_workspace_bytes).
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d);
+hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q, const void* k,
+                            const void* v, const float* theta, const float* beta, const float* S0,
+                            const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
+                            float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream);
+
 }  // namespace kda

@@ -143,6 +143,42 @@ int kda_chunk_fwd_unbounded(int dtype, int B, int T, int H, int dk, int dv,
                             const float* theta, const float* beta, const float* S0,
                             void* o, float* S_T, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * kda_chunk_bwd: the backward pass of kda_chunk_fwd.  For the scalar
+ *     L = sum_t <do_t, o_t> + <dS_T, S_T>
+ * it writes the gradients of L with respect to q, k, v, theta, beta and S0, by
+ * the chain rule through the recurrence taken chunk by chunk (the chunk form of
+ * "Kimi K3 Deep Dive...", "The Problem: The Diagonal-Block Dilemma", run in
+ * reverse; the training step the pages' kernel design serves, "Architecture
+ * Deep Dive...", section 3.2).  dtheta includes the gate's derivative
+ * KDA_G_MIN * sigmoid(theta) (1 - sigmoid(theta)).
+ *
+ *   dtype, B, T, H, dk, dv, q, k, v, theta, beta, S0   as kda_chunk_fwd
+ *   do           [B, T, H, dv]   dtype, gradient of L with respect to o
+ *   dS_T         [B, H, dk, dv]  fp32, gradient with respect to S_T, or NULL (zero)
+ *   dq, dk       [B, T, H, dk]   fp32, written
+ *   dv           [B, T, H, dv]   fp32, written
+ *   dtheta       [B, T, H, dk]   fp32, written
+ *   dbeta        [B, T, H]       fp32, written
+ *   dS0          [B, H, dk, dv]  fp32, written; or NULL to skip
+ *   workspace    kda_chunk_bwd_workspace_size bytes of device memory (every
+ *                chunk's start state, fp32); contents on entry do not matter
+ *   stream       hipStream_t the work is enqueued on
+ * Returns KDA_OK once enqueued.  Errors (before any HIP call): as kda_chunk_fwd;
+ * every gradient output must not overlap an input, another output or the
+ * workspace.  One workgroup per (batch, head): the evaluation is sequential
+ * over T within a sequence.  Results are deterministic run to run.
+ * ------------------------------------------------------------------------- */
+int kda_chunk_bwd(int dtype, int B, int T, int H, int dk, int dv,
+                  const void* q, const void* k, const void* v,
+                  const float* theta, const float* beta, const float* S0,
+                  const void* do_, const float* dS_T,
+                  float* dq, float* dk_, float* dv_, float* dtheta, float* dbeta, float* dS0,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace kda_chunk_bwd needs.  Writes *bytes; returns a kda_status. */
+int kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, size_t* bytes);
+
 /* Bytes of workspace kda_chunk_fwd needs for these sizes and this segment
  * count (0 = automatic).  Writes *bytes; returns a kda_status. */
 int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segments,

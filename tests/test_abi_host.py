@@ -127,6 +127,44 @@ def test_chunk_fwd_unbounded_validation(lib):
     assert call(S_T=b.addr["beta"]) == ALIAS
 
 
+def test_chunk_bwd_validation(lib):
+    """The backward entry point checks sizes, NULLs, alignment, overlaps and the
+    workspace on the host before any HIP call."""
+    b = Bufs()
+    tok = b.B * b.T * b.H
+    base = 1 << 44
+    grads = {}
+    for name, n in (("dq", tok * b.d * 4), ("dk", tok * b.d * 4), ("dv", tok * b.d * 4),
+                    ("dtheta", tok * b.d * 4), ("dbeta", tok * 4), ("dS0", b.H * b.d * b.d * 4),
+                    ("do", tok * b.d * 2), ("dS_T", b.H * b.d * b.d * 4)):
+        grads[name] = base
+        base += (n + 4095) // 4096 * 4096 + 4096
+    need = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(b.B, b.T, b.H, b.d, b.d, ctypes.byref(need)) == OK
+    assert need.value == (b.T // 16) * b.B * b.H * b.d * b.d * 4
+    vp = ctypes.c_void_p
+
+    def call(dtype=0, ws_bytes=None, **over):
+        a = dict(b.addr)
+        a.update(grads)
+        a.update(over)
+        p = lambda n: vp(a[n]) if a[n] is not None else None
+        return lib.kda_chunk_bwd(dtype, b.B, b.T, b.H, b.d, b.d, p("q"), p("k"), p("v"), p("theta"), p("beta"),
+                                 p("S0"), p("do"), p("dS_T"), p("dq"), p("dk"), p("dv"), p("dtheta"),
+                                 p("dbeta"), p("dS0"), p("ws"), need.value if ws_bytes is None else ws_bytes,
+                                 None)
+
+    assert call(dtype=3) == DTYPE
+    for name in ("q", "do", "dq", "dtheta", "dbeta"):
+        assert call(**{name: None}) == NULL, name
+    assert call(dq=grads["dq"] + 4) == ALIGN
+    assert call(ws_bytes=need.value - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(dq=b.addr["q"]) == ALIAS               # a gradient over an input
+    assert call(dk=grads["dq"]) == ALIAS               # two gradients over each other
+    assert call(dv=b.addr["ws"]) == ALIAS              # a gradient over the workspace
+
+
 def test_chunk_fwd_workspace_checks(lib):
     b = Bufs(T=1024, H=2, d=64)
     need = kda.kda_chunk_fwd_workspace_size(1, 1024, 2, 64, 64, 4)

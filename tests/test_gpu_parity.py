@@ -344,6 +344,50 @@ def test_prefill_64k_unbounded_sampled_columns(oracle_mod):
     assert eo <= 2e-2 and es <= 2e-2
 
 
+# ----------------------------------------------------------------------------- backward pass
+# kda_chunk_bwd against the oracle's backward for L = sum <do, o> + <dS_T, S_T>.
+BWD_CASES = [
+    ("tiny", {}, None, True),                             # fp32, d = 16
+    ("tiny", dict(T=61), None, True),                     # ragged tail
+    ("tiny", dict(T=5), None, False),                     # shorter than one chunk, no dS_T
+    ("small", dict(T=1000 + 7), None, True),              # bf16, d = 64, S0 != 0
+    ("small", dict(dk=32, dv=32, H=3, T=333), "f32", True),
+    ("decay_stress", dict(H=2, T=512), None, True),       # d = 128 at the decay bound
+    ("prefill_64k", dict(H=2, T=2048 + 9), None, False),  # S0 = 0, no dS_T
+]
+
+
+@pytest.mark.parametrize("name,over,dt,with_dst", BWD_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}-dST{int(c[3])}" for c in BWD_CASES])
+def test_chunk_bwd_matches_oracle(oracle_mod, name, over, dt, with_dst):
+    w = _chunk_case(name, over, dt)
+    note(f"chunk_bwd {w} dS_T={with_dst}")
+    x = kin.chunk_inputs(w)
+    gen = torch.Generator().manual_seed(w.seed + 2000)
+    do = torch.randn((w.B, w.T, w.H, w.dv), generator=gen).to(kin.torch_dtype(w.dtype))
+    dS_T = torch.randn((w.B, w.H, w.dk, w.dv), generator=gen) if with_dst else None
+    d = to_dev(x)
+    g = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], do.to(DEV), d["S0"],
+                          dS_T.to(DEV) if dS_T is not None else None)
+    torch.cuda.synchronize()
+    ref = oracle_mod.chunk_bwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], x["S0"], do, dS_T)
+    errs = {key: rel_err(g[key], ref[key]) for key in ("dq", "dk", "dv", "dtheta", "dbeta", "dS0")}
+    note("  " + " ".join(f"{key}={e:.2e}" for key, e in errs.items()))
+    for key, e in errs.items():
+        assert e <= TOL[w.dtype], key
+
+
+def test_chunk_bwd_deterministic():
+    w = kin.scaled(kin.WORKLOADS["small"], B=1, H=2, T=300)
+    d = to_dev(kin.chunk_inputs(w))
+    do = torch.randn((w.B, w.T, w.H, w.dv), device=DEV).to(torch.bfloat16)
+    g1 = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], do, d["S0"])
+    g2 = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["theta"], d["beta"], do, d["S0"])
+    torch.cuda.synchronize()
+    for key in g1:
+        assert torch.equal(g1[key], g2[key]), key
+
+
 # ----------------------------------------------------------------------------- full-size workloads
 def _sampled_chunk_check(oracle_mod, name, cols, heads=None, segments=0):
     w = kin.WORKLOADS[name]
