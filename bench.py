@@ -12,9 +12,10 @@ kernels run on, after W untimed warm-up calls (the clocks settle after about
 timed the same way and reported in the "output_gate" object.  The 1M-token
 prefill (B=1, H=16, T=2^20) is reported in "prefill_1m", and the ablation of the
 bounded gate (kda_chunk_fwd against kda_chunk_fwd_unbounded at B=32, H=16,
-T=4096, one segment) in "ablation".  The decode step (B=256, H=16 fp32 state, in
-place) is timed over 1,024 consecutive steps as one interval and reported in the
-"decode" object.  The fp64 oracle is timed on the host cores on a bounded
+T=4096, one segment) in "ablation".  The backward pass (kda_chunk_bwd) is timed
+at that batch shape and at the 64K prefill ("backward").  The decode step (B=256,
+H=16 fp32 state, in place) is timed over 1,024 consecutive steps as one interval
+and reported in the "decode" object.  The fp64 oracle is timed on the host cores on a bounded
 sample of the same prefill ("cpu_baseline").  Prints one JSON line.
 """
 from __future__ import annotations
@@ -143,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-1m", action="store_true",
                     help="skip the timing of the 1M-token prefill (B=1, H=16, T=2^20)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the backward pass (kda_chunk_bwd)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the timing of the unbounded-gate ablation (kda_chunk_fwd_unbounded)")
     ap.add_argument("--cpu-tokens", type=int, default=65536)
@@ -287,6 +290,33 @@ def main():
                              "frac": mby / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": mby,
                              "calls_timed": 5}
         del mx, mo, mS, mws
+
+    if not args.no_backward and w.name == "prefill_64k":
+        # The backward pass (first version: one workgroup per sequence and head, fp32 vector
+        # arithmetic): at the batch shape of the ablation and at this 64K prefill.
+        bw = {}
+        for label, bwk, reps in (("B32_T4096", kin.scaled(w, B=32, T=4096), 3), ("prefill_64k", w, 1)):
+            bx = kin.chunk_inputs(bwk, device=dev) if bwk is not w else x
+            gdo = torch.Generator(device=dev).manual_seed(bwk.seed + 2000)
+            bdo = torch.randn((bwk.B, bwk.T, bwk.H, bwk.dv), generator=gdo, device=dev).to(bx["q"].dtype)
+            bws = torch.empty(kda.kda_chunk_bwd_workspace_size(bwk.B, bwk.T, bwk.H, bwk.dk, bwk.dv),
+                              dtype=torch.uint8, device=dev)
+
+            def bwstep():
+                kda.kda_chunk_bwd(bx["q"], bx["k"], bx["v"], bx["theta"], bx["beta"], bdo, bx["S0"],
+                                  workspace=bws, stream=stream)
+
+            bms, _ = time_calls(bwstep, reps, 1, stream)
+            th = bwk.B * bwk.T * bwk.H
+            bby = th * (es * (2 * bwk.dk + 2 * bwk.dv) + 4 * bwk.dk + 4 + 4 * (3 * bwk.dk + bwk.dv) + 4)
+            bw[label] = {"B": bwk.B, "H": bwk.H, "T": bwk.T, "d": bwk.dk, "ms_per_call": bms,
+                         "tokens_per_s": bwk.B * bwk.T / (bms * 1e-3), "algorithmic_bytes": bby,
+                         "achieved": bby / (bms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": bby / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, "calls_timed": reps}
+            del bdo, bws
+            if bwk is not w:
+                del bx
+        out["backward"] = {"call": "kda_chunk_bwd", **bw}
 
     if not args.no_ablation:
         # What the bound buys: the same batch-parallel prefill (one segment, 512 sequences

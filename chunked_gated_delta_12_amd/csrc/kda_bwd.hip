@@ -40,7 +40,7 @@ struct BwdCfg {
     // row-space work: thread owns channel i = tid / RT and tokens th*TT .. +TT-1
     static constexpr int RT = NTHR / D;      // threads per channel
     static constexpr int TT = CHUNK / RT;    // tokens per thread
-    static_assert(TPC >= 1 && TPC <= 16 && RT * TT == CHUNK, "mappings");
+    static_assert(TPC >= 1 && TPC <= 16 && RPT >= 1 && RT * TT == CHUNK, "mappings");
 };
 
 template <int D>
@@ -66,7 +66,7 @@ struct BwdSmem {
 };
 
 template <typename E, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(BwdCfg<D>::NTHR)
 bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restrict__ k,
            const E* __restrict__ v, const float* __restrict__ theta, const float* __restrict__ beta,
            const float* __restrict__ S0, const E* __restrict__ dout, const float* __restrict__ dS_T,
@@ -139,7 +139,7 @@ bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restri
         }
         if (tid < CHUNK) sm.beta[tid] = tid < nv ? beta[bb + (int64_t)(tc + tid) * bstr] : 0.0f;
         __syncthreads();
-        {   // one (t, s) entry per thread
+        if (tid < CHUNK * CHUNK) {   // one (t, s) entry per thread
             const int t = tid / CHUNK, s = tid % CHUNK;
             float kk = 0.0f, qk = 0.0f;
             for (int c = 0; c < D; ++c) {
@@ -173,13 +173,16 @@ bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restri
     auto forward_cols = [&](int n) {
         const int tc = n * CHUNK;
         const int nv = min(CHUNK, T - tc);
+        if (pc == 0) {   // V into Y first: the loads are independent and all in flight at once
+#pragma unroll
+            for (int t = 0; t < CHUNK; ++t) sm.Y[t][j] = t < nv ? to_f(v[hb + (tc + t) * tstr + j]) : 0.0f;
+        }
         for (int t = 0; t < CHUNK; ++t) {
             float a = 0.0f;
 #pragma unroll
             for (int r = 0; r < C::RPT; ++r) a = fmaf(sm.kp[t][r0 + r], S[r], a);
             a = colsum(a);
-            const float vv = t < nv ? to_f(v[hb + (tc + t) * tstr + j]) : 0.0f;
-            if (pc == 0) sm.Y[t][j] = vv - a;
+            if (pc == 0) sm.Y[t][j] -= a;
         }
         wave_lds_sync();
         for (int t = 0; t < CHUNK; ++t) {
@@ -256,7 +259,7 @@ bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restri
         }
         __syncthreads();
 
-        {   // dA_qk = LowerIncl(dO U^T), dA = StrictLower(-Z U^T): one (t, s) entry per thread
+        if (tid < CHUNK * CHUNK) {   // dA_qk = LowerIncl(dO U^T), dA = StrictLower(-Z U^T): one entry per thread
             const int t = tid / CHUNK, s = tid % CHUNK;
             float a = 0.0f, z = 0.0f;
             for (int c = 0; c < D; ++c) {
@@ -284,15 +287,23 @@ bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restri
             float dqp[C::TT], dkp[C::TT], dke[C::TT];
 #pragma unroll
             for (int u = 0; u < C::TT; ++u) dqp[u] = dkp[u] = dke[u] = 0.0f;
-            for (int jj = 0; jj < D; ++jj) {
-                const float sv = Srow[jj], dsv = dSrow[jj];
-                dgc = fmaf(dsv, sv, dgc);
+            // the S row in blocks of 16, each fetched with four 16-byte loads in flight together
+            for (int jb = 0; jb < D; jb += 16) {
+                f32x4 s4[4];
 #pragma unroll
-                for (int u = 0; u < C::TT; ++u) {
-                    const int t = t0r + u;
-                    dqp[u] = fmaf(sm.dO[t][jj], sv, dqp[u]);
-                    dkp[u] = fmaf(-sm.beta[t] * sm.Z[t][jj], sv, dkp[u]);
-                    dke[u] = fmaf(sm.U[t][jj], dsv, dke[u]);
+                for (int e = 0; e < 4; ++e) s4[e] = *reinterpret_cast<const f32x4*>(Srow + jb + 4 * e);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int jj = jb + e;
+                    const float sv = s4[e >> 2][e & 3], dsv = dSrow[jj];
+                    dgc = fmaf(dsv, sv, dgc);
+#pragma unroll
+                    for (int u = 0; u < C::TT; ++u) {
+                        const int t = t0r + u;
+                        dqp[u] = fmaf(sm.dO[t][jj], sv, dqp[u]);
+                        dkp[u] = fmaf(-sm.beta[t] * sm.Z[t][jj], sv, dkp[u]);
+                        dke[u] = fmaf(sm.U[t][jj], dsv, dke[u]);
+                    }
                 }
             }
             float dG[C::TT], kesum = 0.0f;
@@ -368,7 +379,8 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int BH = B * H;
 #define KDA_BWD(E, D)                                                                                  \
-    hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)BH), dim3(256), 0, stream, T, H, nchunks,     \
+    hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)BH), dim3(BwdCfg<D>::NTHR), 0, stream, T, H,  \
+                       nchunks,                                                                         \
                        (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const E*)dout, dS_T, dq, \
                        dk, dv, dtheta, dbeta, dS0, (float*)workspace);                                  \
     return hipGetLastError()
