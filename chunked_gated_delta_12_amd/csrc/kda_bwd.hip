@@ -367,9 +367,461 @@ bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restri
     }
 }
 
+// ----------------------------------------------------------------------------
+// Matrix-core version for d = 64 and 128.  Same algebra and the same two sweeps;
+// the products run as fp32 16x16x4 matrix-core steps and the state lives in
+// the accumulator layout: wavefront w owns the column tiles w*NCW .. w*NCW+NCW-1
+// of S (forward sweep) and of dS' (backward sweep), lane (g = lane/16, li =
+// lane%16) holding rows 4g..4g+3 of column li of each 16x16 tile.  That layout
+// is the B operand of a step that contracts over the tile's rows (step i takes
+// row 4g+i), so K+ S, Kend dS', T' Y, T^T dU and the rank-16 state updates
+// read the state, U, dU and dY straight from registers.  The forward sweep
+// saves every chunk's start state (row-major) and its U and Y tiles; the
+// backward sweep reads them back for the products over the state's columns
+// (dO S^T, dY S^T, U dS'^T), which run with the tokens as rows and the state's
+// rows as columns.  Deterministic: every output element has one owner and a
+// fixed summation order.
+template <int D>
+struct BmCfg {
+    static constexpr int NT = D / 16;     // 16-wide tiles along a state dimension
+    static constexpr int NCW = NT / 4;    // column tiles per wavefront
+    static constexpr int LDR = D + 4;     // row stride of the [16][D] tiles: rows start 4 banks apart
+    static constexpr int LS = CHUNK + 4;  // row stride of the 16x16 matrices
+    static constexpr int64_t CW = (int64_t)D * D + 2 * CHUNK * D;   // workspace floats per chunk
+    static constexpr int EPT = CHUNK * D / 256;  // elements of a [16][D] tile per thread
+    static_assert(NCW >= 1 && NT % 4 == 0, "d = 64 or 128");
+};
+
+// N consecutive elements of E, loaded as one unit (16-byte aligned at most)
+template <typename E, int N>
+struct alignas(N * sizeof(E) >= 16 ? 16 : N * sizeof(E)) Row {
+    E x[N];
+};
+
+template <int D>
+struct BmSmem {
+    typedef BmCfg<D> C;
+    float kp[CHUNK][C::LDR];   // K+
+    float km[CHUNK][C::LDR];   // K-
+    float qp[CHUNK][C::LDR];   // Q+
+    float ke[CHUNK][C::LDR];   // Kend
+    float gam[CHUNK][C::LDR];  // Gamma
+    float dO[CHUNK][C::LDR];
+    float U[CHUNK][C::LDR];
+    float Z[CHUNK][C::LDR];    // T^T dU
+    float Y[CHUNK][C::LDR];    // V - K+ S (backward sweep); V (forward sweep)
+    float dsg[CHUNK][C::LDR];  // d g / d theta = G_MIN sigmoid(theta) (1 - sigmoid(theta))
+    float X[D][C::LDR];        // dS' of the chunk
+    float KK[CHUNK][C::LS];    // K+ K-^T
+    float A[CHUNK][C::LS];     // StrictLower(diag(beta) K+ K-^T)
+    float Tm[CHUNK][C::LS];    // (I + A)^-1
+    float Aqk[CHUNK][C::LS];
+    float dAqk[CHUNK][C::LS];
+    float dA[CHUNK][C::LS];
+    float gc[D], beta[CHUNK], zy[CHUNK];
+};
+
+template <typename E, int D>
+__global__ void __launch_bounds__(256)
+bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restrict__ k,
+                const E* __restrict__ v, const float* __restrict__ theta, const float* __restrict__ beta,
+                const float* __restrict__ S0, const E* __restrict__ dout, const float* __restrict__ dS_T,
+                float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+                float* __restrict__ dtheta, float* __restrict__ dbeta, float* __restrict__ dS0,
+                float* __restrict__ ws) {
+    typedef BmCfg<D> C;
+    __shared__ BmSmem<D> sm;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int64_t tstr = (int64_t)H * D;                              // elements between tokens
+    const int64_t hb = (int64_t)b * T * H * D + (int64_t)h * D;       // token 0 of this head
+    const int64_t bb = (int64_t)b * T * H + h;                        // beta of token 0
+    float* wsh = ws + (int64_t)bh * nchunks * C::CW;
+    constexpr float LOG2E = 1.4426950408889634f;
+    const f32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto ld4 = [](const float* p) { return *reinterpret_cast<const f32x4*>(p); };
+
+    // raw inputs of one chunk, loaded into registers a chunk ahead and written
+    // to LDS when that chunk starts: theta, k, q, then v (forward sweep) or
+    // dO and the saved U and Y tiles (backward sweep), and beta.  Thread tid
+    // holds token xt, channels xc .. xc + EPT - 1; padding tokens read as zero.
+    const int xt = tid * C::EPT / D, xc = tid * C::EPT % D;
+    struct Raw {
+        Row<float, C::EPT> th, u, y;
+        Row<E, C::EPT> k, q, x;
+        float b;
+    };
+    auto zero_row = [](auto& r) {
+#pragma unroll
+        for (int e = 0; e < C::EPT; ++e) r.x[e] = 0.0f;
+    };
+    auto load_raw = [&](int m, bool bwd, Raw& r) {
+        const int tm = m * CHUNK;
+        const int nvm = min(CHUNK, T - tm);
+        if (xt < nvm) {
+            const int64_t off = hb + (tm + xt) * tstr + xc;
+            r.th = *reinterpret_cast<const Row<float, C::EPT>*>(theta + off);
+            r.k = *reinterpret_cast<const Row<E, C::EPT>*>(k + off);
+            r.q = *reinterpret_cast<const Row<E, C::EPT>*>(q + off);
+            r.x = *reinterpret_cast<const Row<E, C::EPT>*>((bwd ? dout : v) + off);
+        } else {
+            zero_row(r.th);
+            zero_row(r.k);
+            zero_row(r.q);
+            zero_row(r.x);
+        }
+        if (bwd) {
+            const float* wsm = wsh + (int64_t)m * C::CW + (int64_t)D * D + xt * D + xc;
+            r.u = *reinterpret_cast<const Row<float, C::EPT>*>(wsm);
+            r.y = *reinterpret_cast<const Row<float, C::EPT>*>(wsm + CHUNK * D);
+        }
+        r.b = (tid < nvm) ? beta[bb + (int64_t)(tm + tid) * H] : 0.0f;
+    };
+    auto store_raw = [&](const Raw& r, bool bwd) {
+#pragma unroll
+        for (int e = 0; e < C::EPT; ++e) {
+            sm.gam[xt][xc + e] = r.th.x[e];          // theta until the gate overwrites it
+            sm.kp[xt][xc + e] = to_f(r.k.x[e]);      // k until the gate overwrites it
+            sm.qp[xt][xc + e] = to_f(r.q.x[e]);      // q until the gate overwrites it
+            if (bwd) {
+                sm.dO[xt][xc + e] = to_f(r.x.x[e]);
+                sm.U[xt][xc + e] = r.u.x[e];
+                sm.Y[xt][xc + e] = r.y.x[e];
+            } else {
+                sm.Y[xt][xc + e] = to_f(r.x.x[e]);   // V
+            }
+        }
+        if (tid < CHUNK) sm.beta[tid] = r.b;
+    };
+
+    // gate, decay tiles, KK, A, T and (backward sweep) A_qk and dg/dtheta of the
+    // chunk whose raw inputs are in LDS
+    auto prepare = [&](bool bwd, int nv) {
+        lds_barrier();
+        if (tid < D) {
+            const int c = tid;
+            float G = 0.0f;
+            float gam[CHUNK];
+#pragma unroll
+            for (int t = 0; t < CHUNK; ++t) {
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * sm.gam[t][c]));
+                if (t < nv) G += G_MIN * LOG2E * sg;
+                gam[t] = __builtin_amdgcn_exp2f(G);
+                if (bwd) sm.dsg[t][c] = G_MIN * sg * (1.0f - sg);
+            }
+            const float gC = gam[CHUNK - 1];
+#pragma unroll
+            for (int t = 0; t < CHUNK; ++t) {
+                const float kk = sm.kp[t][c], qq = sm.qp[t][c];
+                const float ig = __builtin_amdgcn_rcpf(gam[t]);   // <= e^80: the bound
+                sm.gam[t][c] = gam[t];
+                sm.kp[t][c] = kk * gam[t];
+                sm.km[t][c] = kk * ig;
+                sm.qp[t][c] = qq * gam[t];
+                sm.ke[t][c] = kk * (gC * ig);
+            }
+            sm.gc[c] = gC;
+        }
+        lds_barrier();
+        // KK = K+ K-^T (wavefront 0) and A_qk = Q+ K-^T (wavefront 1): rows t = li of the
+        // A operand, step i contracts channel 16kb + 4g + i; lane holds rows 4g..4g+3, column li
+        if (w == 0 || (bwd && w == 1)) {
+            const float(*Am)[C::LDR] = w == 0 ? sm.kp : sm.qp;
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int kb = 0; kb < C::NT; ++kb) {
+                const f32x4 a4 = ld4(&Am[li][16 * kb + 4 * g]), b4 = ld4(&sm.km[li][16 * kb + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma_k4(a4[i], b4[i], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r, s = li;
+                if (w == 0) {
+                    sm.KK[t][s] = acc[r];
+                    sm.A[t][s] = s < t ? sm.beta[t] * acc[r] : 0.0f;
+                } else {
+                    sm.Aqk[t][s] = s <= t ? acc[r] : 0.0f;
+                }
+            }
+        }
+        lds_barrier();
+        if (tid < CHUNK) {   // T = (I + A)^-1, column tid, forward substitution
+            const int cj = tid;
+            float x[CHUNK];
+#pragma unroll
+            for (int r = 0; r < CHUNK; ++r) {
+                float a = (r == cj) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < CHUNK; ++s2)
+                    if (s2 < r) a = fmaf(-sm.A[r][s2], x[s2], a);
+                x[r] = a;
+            }
+#pragma unroll
+            for (int r = 0; r < CHUNK; ++r) sm.Tm[r][cj] = x[r];
+        }
+        lds_barrier();
+    };
+
+    // ---------------- forward sweep: S in registers, every chunk's S, U, Y saved
+    f32x4 St[C::NT][C::NCW];
+#pragma unroll
+    for (int rt = 0; rt < C::NT; ++rt)
+#pragma unroll
+        for (int cw = 0; cw < C::NCW; ++cw)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                St[rt][cw][r] = S0 ? S0[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * C::NCW + cw) + li]
+                                   : 0.0f;
+    Raw raw;
+    load_raw(0, false, raw);
+    for (int n = 0; n < nchunks; ++n) {
+        const int nv = min(CHUNK, T - n * CHUNK);
+        store_raw(raw, false);
+        if (n + 1 < nchunks) load_raw(n + 1, false, raw);   // in flight during this chunk
+        prepare(false, nv);
+        float* wsn = wsh + (int64_t)n * C::CW;
+#pragma unroll
+        for (int cw = 0; cw < C::NCW; ++cw) {
+            const int col = 16 * (w * C::NCW + cw) + li;
+#pragma unroll
+            for (int rt = 0; rt < C::NT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wsn[(16 * rt + 4 * g + r) * D + col] = St[rt][cw][r];
+            // P = K+ S: A[t][c] = K+[li][c], B[c][j] = S tile rows
+            f32x4 p = zero4;
+#pragma unroll
+            for (int rt = 0; rt < C::NT; ++rt) {
+                const f32x4 a4 = ld4(&sm.kp[li][16 * rt + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p = mfma_k4(a4[i], St[rt][cw][i], p);
+            }
+            f32x4 y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = sm.Y[4 * g + r][col] - p[r];   // V - K+ S
+            // U = T diag(beta) Y: A[t][s] = T[li][s] beta[s], B[s][j] = Y rows
+            f32x4 u = zero4;
+            const f32x4 t4 = ld4(&sm.Tm[li][4 * g]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u = mfma_k4(t4[i] * sm.beta[4 * g + i], y[i], u);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                wsn[(int64_t)D * D + (4 * g + r) * D + col] = u[r];
+                wsn[(int64_t)D * D + CHUNK * D + (4 * g + r) * D + col] = y[r];
+            }
+            // S <- Diag(Gamma_C) S + Kend^T U: A[c][t] = Kend[t][c], B[t][j] = U rows
+#pragma unroll
+            for (int rt = 0; rt < C::NT; ++rt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) St[rt][cw][r] *= sm.gc[16 * rt + 4 * g + r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) St[rt][cw] = mfma_k4(sm.ke[4 * g + i][16 * rt + li], u[i], St[rt][cw]);
+            }
+        }
+        lds_barrier();   // before the next chunk's tiles overwrite these
+    }
+    __syncthreads();   // the saved states, U and Y are in memory before the backward sweep reads them
+
+    // ---------------- backward sweep: dS' in registers
+    f32x4 Xt[C::NT][C::NCW];
+#pragma unroll
+    for (int rt = 0; rt < C::NT; ++rt)
+#pragma unroll
+        for (int cw = 0; cw < C::NCW; ++cw)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Xt[rt][cw][r] = dS_T ? dS_T[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * C::NCW + cw) + li]
+                                     : 0.0f;
+    load_raw(nchunks - 1, true, raw);
+    for (int n = nchunks - 1; n >= 0; --n) {
+        const int tc = n * CHUNK;
+        const int nv = min(CHUNK, T - tc);
+        const float* wsn = wsh + (int64_t)n * C::CW;
+        store_raw(raw, true);
+        if (n > 0) load_raw(n - 1, true, raw);   // in flight during this chunk
+#pragma unroll
+        for (int rt = 0; rt < C::NT; ++rt)
+#pragma unroll
+            for (int cw = 0; cw < C::NCW; ++cw)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.X[16 * rt + 4 * g + r][16 * (w * C::NCW + cw) + li] = Xt[rt][cw][r];
+        prepare(true, nv);
+
+        // column space: dU, Z, dV and the carried gradient, per owned column tile
+#pragma unroll
+        for (int cw = 0; cw < C::NCW; ++cw) {
+            const int col = 16 * (w * C::NCW + cw) + li;
+            float dob[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dob[i] = sm.dO[4 * g + i][col];
+            // dU = A_qk^T dO + Kend dS'
+            f32x4 du = zero4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) du = mfma_k4(sm.Aqk[4 * g + i][li], dob[i], du);
+#pragma unroll
+            for (int rt = 0; rt < C::NT; ++rt) {
+                const f32x4 a4 = ld4(&sm.ke[li][16 * rt + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) du = mfma_k4(a4[i], Xt[rt][cw][i], du);
+            }
+            // Z = T^T dU,  dY = diag(beta) Z = dV
+            f32x4 z = zero4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z = mfma_k4(sm.Tm[4 * g + i][li], du[i], z);
+            f32x4 dy;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                dy[r] = sm.beta[t] * z[r];
+                sm.Z[t][col] = z[r];
+                if (t < nv) dv[hb + (tc + t) * tstr + col] = dy[r];
+            }
+            // dS' <- Diag(Gamma_C) dS' + Q+^T dO - K+^T dY
+#pragma unroll
+            for (int rt = 0; rt < C::NT; ++rt) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Xt[rt][cw][r] *= sm.gc[16 * rt + 4 * g + r];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Xt[rt][cw] = mfma_k4(sm.qp[4 * g + i][16 * rt + li], dob[i], Xt[rt][cw]);
+                    Xt[rt][cw] = mfma_k4(-sm.kp[4 * g + i][16 * rt + li], dy[i], Xt[rt][cw]);
+                }
+            }
+        }
+        // the S rows of this lane's channels, in flight across the next barriers
+        f32x4 srow[C::NCW][C::NT];
+#pragma unroll
+        for (int cw = 0; cw < C::NCW; ++cw)
+#pragma unroll
+            for (int kb = 0; kb < C::NT; ++kb)
+                srow[cw][kb] = ld4(wsn + (int64_t)(16 * (w * C::NCW + cw) + li) * D + 16 * kb + 4 * g);
+        lds_barrier();   // Z complete
+
+        if (w < 2) {   // dA_qk = LowerIncl(dO U^T) (wavefront 0), dA = StrictLower(-Z U^T) (wavefront 1)
+            const float(*Am)[C::LDR] = w == 0 ? sm.dO : sm.Z;
+            f32x4 acc = zero4;
+#pragma unroll
+            for (int kb = 0; kb < C::NT; ++kb) {
+                const f32x4 a4 = ld4(&Am[li][16 * kb + 4 * g]), b4 = ld4(&sm.U[li][16 * kb + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mfma_k4(a4[i], b4[i], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r, s = li;
+                if (w == 0) sm.dAqk[t][s] = s <= t ? acc[r] : 0.0f;
+                else sm.dA[t][s] = s < t ? -acc[r] : 0.0f;
+            }
+        } else {   // rowsum(Z * Y): 8 threads per token
+            const int t = (tid - 128) >> 3, part = tid & 7;
+            float a = 0.0f;
+            for (int c = part; c < D; c += 8) a = fmaf(sm.Z[t][c], sm.Y[t][c], a);
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) a += __shfl_xor(a, o);
+            if (part == 0) sm.zy[t] = a;
+        }
+        lds_barrier();
+        if (tid < CHUNK) {   // dbeta = rowsum(dA * K+ K-^T) + rowsum(Z * Y)
+            const int t = tid;
+            float a = sm.zy[t];
+#pragma unroll
+            for (int s2 = 0; s2 < CHUNK; ++s2) a = fmaf(sm.dA[t][s2], sm.KK[t][s2], a);
+            if (t < nv) dbeta[bb + (int64_t)(tc + t) * H] = a;
+        }
+
+        // row space: channel tiles owned like the column tiles; rows are tokens,
+        // step i contracts state column 16kb + 4g + i (S and dS' rows as B operands)
+#pragma unroll
+        for (int cw = 0; cw < C::NCW; ++cw) {
+            const int cc = 16 * (w * C::NCW + cw) + li;   // this lane's channel
+            f32x4 aq = zero4, ak = zero4, ae = zero4, am = zero4;   // dQ+, dK+, dKend, dK-
+            float dgc = 0.0f;
+            const float nbl = -sm.beta[li];
+#pragma unroll
+            for (int kb = 0; kb < C::NT; ++kb) {
+                const f32x4 s4 = srow[cw][kb];
+                const f32x4 x4 = ld4(&sm.X[cc][16 * kb + 4 * g]);
+                const f32x4 o4 = ld4(&sm.dO[li][16 * kb + 4 * g]);
+                const f32x4 z4 = ld4(&sm.Z[li][16 * kb + 4 * g]);
+                const f32x4 u4 = ld4(&sm.U[li][16 * kb + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    aq = mfma_k4(o4[i], s4[i], aq);
+                    ak = mfma_k4(nbl * z4[i], s4[i], ak);
+                    ae = mfma_k4(u4[i], x4[i], ae);
+                    dgc = fmaf(x4[i], s4[i], dgc);
+                }
+            }
+            // + dA_qk K-, + diag(beta) dA K-;  dK- = dA_qk^T Q+ + (diag(beta) dA)^T K+
+            const f32x4 daq4 = ld4(&sm.dAqk[li][4 * g]), da4 = ld4(&sm.dA[li][4 * g]);
+            const float bl = sm.beta[li];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 4 * g + i;
+                const float kmv = sm.km[s][cc];
+                aq = mfma_k4(daq4[i], kmv, aq);
+                ak = mfma_k4(bl * da4[i], kmv, ak);
+                am = mfma_k4(sm.dAqk[s][li], sm.qp[s][cc], am);
+                am = mfma_k4(sm.beta[s] * sm.dA[s][li], sm.kp[s][cc], am);
+            }
+            dgc += __shfl_xor(dgc, 16);
+            dgc += __shfl_xor(dgc, 32);
+            // chain through the decay scalings; lane holds tokens 4g..4g+3 of channel cc
+            const float gC = sm.gc[cc];
+            float dG[4], kesum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                const float gm = sm.gam[t][cc], ig = __builtin_amdgcn_rcpf(gm);
+                if (t < nv) {
+                    dk[hb + (tc + t) * tstr + cc] = ak[r] * gm + am[r] * ig + ae[r] * (gC * ig);
+                    dq[hb + (tc + t) * tstr + cc] = aq[r] * gm;
+                }
+                const float ked = ae[r] * sm.ke[t][cc];
+                kesum += ked;
+                dG[r] = ak[r] * sm.kp[t][cc] - am[r] * sm.km[t][cc] + aq[r] * sm.qp[t][cc] - ked;
+            }
+            kesum += __shfl_xor(kesum, 16);
+            kesum += __shfl_xor(kesum, 32);
+            // the chunk's last token also carries the end decay: d(G_C) = sum_t dKend*Kend + dGamma_C*Gamma_C
+            if (g == 3) dG[3] += kesum + dgc * gC;
+            // reverse prefix sum over the chunk's tokens: within the lane, then the
+            // totals of the lane groups holding later tokens
+            float suf = 0.0f;
+#pragma unroll
+            for (int r = 3; r >= 0; --r) {
+                suf += dG[r];
+                dG[r] = suf;
+            }
+            float later = 0.0f;
+#pragma unroll
+            for (int o = 1; o < 4; ++o) {
+                const float x = __shfl_down(suf, 16 * o);
+                if (g + o < 4) later += x;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * g + r;
+                if (t < nv) dtheta[hb + (tc + t) * tstr + cc] = (dG[r] + later) * sm.dsg[t][cc];
+            }
+        }
+        lds_barrier();   // before the next chunk overwrites the tiles
+    }
+    if (dS0) {
+#pragma unroll
+        for (int rt = 0; rt < C::NT; ++rt)
+#pragma unroll
+            for (int cw = 0; cw < C::NCW; ++cw)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dS0[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * C::NCW + cw) + li] = Xt[rt][cw][r];
+    }
+}
+
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d) {
     const size_t nchunks = ((size_t)T + CHUNK - 1) / CHUNK;
-    return nchunks * (size_t)B * H * d * d * sizeof(float);
+    // every chunk's start state; the matrix-core kernel also keeps its U and Y tiles
+    return nchunks * (size_t)B * H * ((size_t)d * d + 2 * CHUNK * (size_t)d) * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q, const void* k,
@@ -378,6 +830,11 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
                             float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int BH = B * H;
+#define KDA_BWD_MFMA(E, D)                                                                             \
+    hipLaunchKernelGGL((bwd_mfma_kernel<E, D>), dim3((unsigned)BH), dim3(256), 0, stream, T, H, nchunks, \
+                       (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const E*)dout, dS_T, dq, \
+                       dk, dv, dtheta, dbeta, dS0, (float*)workspace);                                  \
+    return hipGetLastError()
 #define KDA_BWD(E, D)                                                                                  \
     hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)BH), dim3(BwdCfg<D>::NTHR), 0, stream, T, H,  \
                        nchunks,                                                                         \
@@ -388,18 +845,19 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
         switch (d) {
             case 16: KDA_BWD(float, 16);
             case 32: KDA_BWD(float, 32);
-            case 64: KDA_BWD(float, 64);
-            case 128: KDA_BWD(float, 128);
+            case 64: KDA_BWD_MFMA(float, 64);
+            case 128: KDA_BWD_MFMA(float, 128);
         }
     } else {
         switch (d) {
             case 16: KDA_BWD(bf16, 16);
             case 32: KDA_BWD(bf16, 32);
-            case 64: KDA_BWD(bf16, 64);
-            case 128: KDA_BWD(bf16, 128);
+            case 64: KDA_BWD_MFMA(bf16, 64);
+            case 128: KDA_BWD_MFMA(bf16, 128);
         }
     }
 #undef KDA_BWD
+#undef KDA_BWD_MFMA
     return hipErrorInvalidValue;
 }
 

@@ -141,7 +141,8 @@ def test_chunk_bwd_validation(lib):
         base += (n + 4095) // 4096 * 4096 + 4096
     need = ctypes.c_size_t(0)
     assert lib.kda_chunk_bwd_workspace_size(b.B, b.T, b.H, b.d, b.d, ctypes.byref(need)) == OK
-    assert need.value == (b.T // 16) * b.B * b.H * b.d * b.d * 4
+    # per chunk: its start state and its 16-token U and V - K+ S tiles, fp32
+    assert need.value == (b.T // 16) * b.B * b.H * (b.d * b.d + 32 * b.d) * 4
     vp = ctypes.c_void_p
 
     def call(dtype=0, ws_bytes=None, **over):

@@ -352,6 +352,7 @@ BWD_CASES = [
     ("tiny", dict(T=5), None, False),                     # shorter than one chunk, no dS_T
     ("small", dict(T=1000 + 7), None, True),              # bf16, d = 64, S0 != 0
     ("small", dict(dk=32, dv=32, H=3, T=333), "f32", True),
+    ("small", dict(H=2, T=250), "f32", True),             # fp32, d = 64 on the matrix cores
     ("decay_stress", dict(H=2, T=512), None, True),       # d = 128 at the decay bound
     ("prefill_64k", dict(H=2, T=2048 + 9), None, False),  # S0 = 0, no dS_T
 ]
