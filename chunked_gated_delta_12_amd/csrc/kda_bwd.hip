@@ -384,12 +384,14 @@ bwd_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restri
 template <int D>
 struct BmCfg {
     static constexpr int NT = D / 16;     // 16-wide tiles along a state dimension
-    static constexpr int NCW = NT / 4;    // column tiles per wavefront
+    static constexpr int NW = D == 128 ? 8 : 4;   // wavefronts
+    static constexpr int NTHR = 64 * NW;
+    static constexpr int NCW = NT / NW;   // column tiles per wavefront
     static constexpr int LDR = D + 4;     // row stride of the [16][D] tiles: rows start 4 banks apart
     static constexpr int LS = CHUNK + 4;  // row stride of the 16x16 matrices
     static constexpr int64_t CW = (int64_t)D * D + 2 * CHUNK * D;   // workspace floats per chunk
-    static constexpr int EPT = CHUNK * D / 256;  // elements of a [16][D] tile per thread
-    static_assert(NCW >= 1 && NT % 4 == 0, "d = 64 or 128");
+    static constexpr int EPT = CHUNK * D / NTHR;  // elements of a [16][D] tile per thread
+    static_assert(NCW >= 1 && NT % NW == 0, "d = 64 or 128");
 };
 
 // N consecutive elements of E, loaded as one unit (16-byte aligned at most)
@@ -422,7 +424,7 @@ struct BmSmem {
 };
 
 template <typename E, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(BmCfg<D>::NTHR)
 bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restrict__ k,
                 const E* __restrict__ v, const float* __restrict__ theta, const float* __restrict__ beta,
                 const float* __restrict__ S0, const E* __restrict__ dout, const float* __restrict__ dS_T,
@@ -712,7 +714,7 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
                 if (w == 0) sm.dAqk[t][s] = s <= t ? acc[r] : 0.0f;
                 else sm.dA[t][s] = s < t ? -acc[r] : 0.0f;
             }
-        } else {   // rowsum(Z * Y): 8 threads per token
+        } else if (w < 4) {   // rowsum(Z * Y): wavefronts 2 and 3, 8 threads per token
             const int t = (tid - 128) >> 3, part = tid & 7;
             float a = 0.0f;
             for (int c = part; c < D; c += 8) a = fmaf(sm.Z[t][c], sm.Y[t][c], a);
@@ -831,7 +833,7 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int BH = B * H;
 #define KDA_BWD_MFMA(E, D)                                                                             \
-    hipLaunchKernelGGL((bwd_mfma_kernel<E, D>), dim3((unsigned)BH), dim3(256), 0, stream, T, H, nchunks, \
+    hipLaunchKernelGGL((bwd_mfma_kernel<E, D>), dim3((unsigned)BH), dim3(BmCfg<D>::NTHR), 0, stream, T, H, nchunks, \
                        (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const E*)dout, dS_T, dq, \
                        dk, dv, dtheta, dbeta, dS0, (float*)workspace);                                  \
     return hipGetLastError()
