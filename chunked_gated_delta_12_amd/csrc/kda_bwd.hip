@@ -423,18 +423,33 @@ struct BmSmem {
     float gc[D], beta[CHUNK], zy[CHUNK];
 };
 
-template <typename E, int D>
+// MODE 0: both sweeps over one segment of chunks, from the state at its start
+// (Sinit) and the gradient at its end (Xinit), writing the gradients.
+// MODE 1 and 2 are the segment maps: the forward sweep (1) or the chain of
+// the carried gradient alone (2) over one segment, run on the widened state
+// [0 | I] (d x 2d), whose end value [N | M] gives the segment's affine map
+// (end = M start + N for the state; start = M end + N for the gradient).
+// They write it, row-major, to maps.  The carried gradient does not depend on
+// the state, so both maps are independent of each other.
+enum { BWD_FULL = 0, BWD_FMAP = 1, BWD_BMAP = 2 };
+
+template <typename E, int D, int MODE>
 __global__ void __launch_bounds__(BmCfg<D>::NTHR)
-bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __restrict__ k,
-                const E* __restrict__ v, const float* __restrict__ theta, const float* __restrict__ beta,
-                const float* __restrict__ S0, const E* __restrict__ dout, const float* __restrict__ dS_T,
-                float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-                float* __restrict__ dtheta, float* __restrict__ dbeta, float* __restrict__ dS0,
-                float* __restrict__ ws) {
+bwd_mfma_kernel(int T, int H, int BH, int nchunks, int seg_len, const E* __restrict__ q,
+                const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ theta,
+                const float* __restrict__ beta, const float* __restrict__ Sinit, const E* __restrict__ dout,
+                const float* __restrict__ Xinit, float* __restrict__ dq, float* __restrict__ dk,
+                float* __restrict__ dv, float* __restrict__ dtheta, float* __restrict__ dbeta,
+                float* __restrict__ dS0, float* __restrict__ ws, float* __restrict__ maps) {
     typedef BmCfg<D> C;
+    constexpr bool FULL = MODE == BWD_FULL;
+    constexpr int NCX = FULL ? C::NCW : 2 * C::NCW;   // column tiles per wavefront (widened in the maps)
+    constexpr int WD = FULL ? D : 2 * D;              // columns of the state
     __shared__ BmSmem<D> sm;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int bh = blockIdx.x % BH, seg = blockIdx.x / BH, b = bh / H, h = bh % H;
+    const int n_lo = seg * seg_len, n_hi = min(nchunks, n_lo + seg_len);
+    const int64_t sb = ((int64_t)seg * BH + bh) * D * D;              // this segment's start / end matrix
     const int64_t tstr = (int64_t)H * D;                              // elements between tokens
     const int64_t hb = (int64_t)b * T * H * D + (int64_t)h * D;       // token 0 of this head
     const int64_t bb = (int64_t)b * T * H + h;                        // beta of token 0
@@ -472,7 +487,7 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
             zero_row(r.q);
             zero_row(r.x);
         }
-        if (bwd) {
+        if (FULL && bwd) {
             const float* wsm = wsh + (int64_t)m * C::CW + (int64_t)D * D + xt * D + xc;
             r.u = *reinterpret_cast<const Row<float, C::EPT>*>(wsm);
             r.y = *reinterpret_cast<const Row<float, C::EPT>*>(wsm + CHUNK * D);
@@ -487,8 +502,10 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
             sm.qp[xt][xc + e] = to_f(r.q.x[e]);      // q until the gate overwrites it
             if (bwd) {
                 sm.dO[xt][xc + e] = to_f(r.x.x[e]);
-                sm.U[xt][xc + e] = r.u.x[e];
-                sm.Y[xt][xc + e] = r.y.x[e];
+                if (FULL) {
+                    sm.U[xt][xc + e] = r.u.x[e];
+                    sm.Y[xt][xc + e] = r.y.x[e];
+                }
             } else {
                 sm.Y[xt][xc + e] = to_f(r.x.x[e]);   // V
             }
@@ -566,30 +583,48 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
     };
 
     // ---------------- forward sweep: S in registers, every chunk's S, U, Y saved
-    f32x4 St[C::NT][C::NCW];
+    // the widened state starts as [0 | I]
+    auto init_state = [&](f32x4 (&W)[C::NT][NCX], const float* init) {
 #pragma unroll
-    for (int rt = 0; rt < C::NT; ++rt)
+        for (int rt = 0; rt < C::NT; ++rt)
 #pragma unroll
-        for (int cw = 0; cw < C::NCW; ++cw)
+            for (int cw = 0; cw < NCX; ++cw)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                St[rt][cw][r] = S0 ? S0[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * C::NCW + cw) + li]
-                                   : 0.0f;
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * rt + 4 * g + r, col = 16 * (w * NCX + cw) + li;
+                    if (FULL) W[rt][cw][r] = init ? init[sb + (int64_t)row * D + col] : 0.0f;
+                    else W[rt][cw][r] = (col - D == row) ? 1.0f : 0.0f;
+                }
+    };
+    auto store_map = [&](const f32x4 (&W)[C::NT][NCX]) {
+        float* mp = maps + ((int64_t)seg * BH + bh) * D * WD;
+#pragma unroll
+        for (int rt = 0; rt < C::NT; ++rt)
+#pragma unroll
+            for (int cw = 0; cw < NCX; ++cw)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mp[(int64_t)(16 * rt + 4 * g + r) * WD + 16 * (w * NCX + cw) + li] = W[rt][cw][r];
+    };
     Raw raw;
-    load_raw(0, false, raw);
-    for (int n = 0; n < nchunks; ++n) {
+    if (MODE != BWD_BMAP) {
+    f32x4 St[C::NT][NCX];
+    init_state(St, Sinit);
+    load_raw(n_lo, false, raw);
+    for (int n = n_lo; n < n_hi; ++n) {
         const int nv = min(CHUNK, T - n * CHUNK);
         store_raw(raw, false);
-        if (n + 1 < nchunks) load_raw(n + 1, false, raw);   // in flight during this chunk
+        if (n + 1 < n_hi) load_raw(n + 1, false, raw);   // in flight during this chunk
         prepare(false, nv);
         float* wsn = wsh + (int64_t)n * C::CW;
 #pragma unroll
-        for (int cw = 0; cw < C::NCW; ++cw) {
-            const int col = 16 * (w * C::NCW + cw) + li;
+        for (int cw = 0; cw < NCX; ++cw) {
+            const int col = 16 * (w * NCX + cw) + li;
+            if (FULL) {
 #pragma unroll
-            for (int rt = 0; rt < C::NT; ++rt)
+                for (int rt = 0; rt < C::NT; ++rt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) wsn[(16 * rt + 4 * g + r) * D + col] = St[rt][cw][r];
+                    for (int r = 0; r < 4; ++r) wsn[(16 * rt + 4 * g + r) * D + col] = St[rt][cw][r];
+            }
             // P = K+ S: A[t][c] = K+[li][c], B[c][j] = S tile rows
             f32x4 p = zero4;
 #pragma unroll
@@ -600,16 +635,18 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
             }
             f32x4 y;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = sm.Y[4 * g + r][col] - p[r];   // V - K+ S
+            for (int r = 0; r < 4; ++r) y[r] = (col < D ? sm.Y[4 * g + r][col] : 0.0f) - p[r];   // V - K+ S
             // U = T diag(beta) Y: A[t][s] = T[li][s] beta[s], B[s][j] = Y rows
             f32x4 u = zero4;
             const f32x4 t4 = ld4(&sm.Tm[li][4 * g]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) u = mfma_k4(t4[i] * sm.beta[4 * g + i], y[i], u);
+            if (FULL) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                wsn[(int64_t)D * D + (4 * g + r) * D + col] = u[r];
-                wsn[(int64_t)D * D + CHUNK * D + (4 * g + r) * D + col] = y[r];
+                for (int r = 0; r < 4; ++r) {
+                    wsn[(int64_t)D * D + (4 * g + r) * D + col] = u[r];
+                    wsn[(int64_t)D * D + CHUNK * D + (4 * g + r) * D + col] = y[r];
+                }
             }
             // S <- Diag(Gamma_C) S + Kend^T U: A[c][t] = Kend[t][c], B[t][j] = U rows
 #pragma unroll
@@ -622,40 +659,40 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
         }
         lds_barrier();   // before the next chunk's tiles overwrite these
     }
+    if (MODE == BWD_FMAP) {
+        store_map(St);
+        return;
+    }
+    }
     __syncthreads();   // the saved states, U and Y are in memory before the backward sweep reads them
 
     // ---------------- backward sweep: dS' in registers
-    f32x4 Xt[C::NT][C::NCW];
-#pragma unroll
-    for (int rt = 0; rt < C::NT; ++rt)
-#pragma unroll
-        for (int cw = 0; cw < C::NCW; ++cw)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Xt[rt][cw][r] = dS_T ? dS_T[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * C::NCW + cw) + li]
-                                     : 0.0f;
-    load_raw(nchunks - 1, true, raw);
-    for (int n = nchunks - 1; n >= 0; --n) {
+    f32x4 Xt[C::NT][NCX];
+    init_state(Xt, Xinit);
+    load_raw(n_hi - 1, true, raw);
+    for (int n = n_hi - 1; n >= n_lo; --n) {
         const int tc = n * CHUNK;
         const int nv = min(CHUNK, T - tc);
         const float* wsn = wsh + (int64_t)n * C::CW;
         store_raw(raw, true);
-        if (n > 0) load_raw(n - 1, true, raw);   // in flight during this chunk
+        if (n > n_lo) load_raw(n - 1, true, raw);   // in flight during this chunk
+        if (FULL) {
 #pragma unroll
-        for (int rt = 0; rt < C::NT; ++rt)
+            for (int rt = 0; rt < C::NT; ++rt)
 #pragma unroll
-            for (int cw = 0; cw < C::NCW; ++cw)
+                for (int cw = 0; cw < NCX; ++cw)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sm.X[16 * rt + 4 * g + r][16 * (w * C::NCW + cw) + li] = Xt[rt][cw][r];
+                    for (int r = 0; r < 4; ++r) sm.X[16 * rt + 4 * g + r][16 * (w * NCX + cw) + li] = Xt[rt][cw][r];
+        }
         prepare(true, nv);
 
         // column space: dU, Z, dV and the carried gradient, per owned column tile
 #pragma unroll
-        for (int cw = 0; cw < C::NCW; ++cw) {
-            const int col = 16 * (w * C::NCW + cw) + li;
+        for (int cw = 0; cw < NCX; ++cw) {
+            const int col = 16 * (w * NCX + cw) + li;
             float dob[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dob[i] = sm.dO[4 * g + i][col];
+            for (int i = 0; i < 4; ++i) dob[i] = col < D ? sm.dO[4 * g + i][col] : 0.0f;
             // dU = A_qk^T dO + Kend dS'
             f32x4 du = zero4;
 #pragma unroll
@@ -675,8 +712,10 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
             for (int r = 0; r < 4; ++r) {
                 const int t = 4 * g + r;
                 dy[r] = sm.beta[t] * z[r];
-                sm.Z[t][col] = z[r];
-                if (t < nv) dv[hb + (tc + t) * tstr + col] = dy[r];
+                if (FULL) {
+                    sm.Z[t][col] = z[r];
+                    if (t < nv) dv[hb + (tc + t) * tstr + col] = dy[r];
+                }
             }
             // dS' <- Diag(Gamma_C) dS' + Q+^T dO - K+^T dY
 #pragma unroll
@@ -689,6 +728,10 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
                     Xt[rt][cw] = mfma_k4(-sm.kp[4 * g + i][16 * rt + li], dy[i], Xt[rt][cw]);
                 }
             }
+        }
+        if (!FULL) {
+            lds_barrier();   // before the next chunk overwrites the tiles
+            continue;
         }
         // the S rows of this lane's channels, in flight across the next barriers
         f32x4 srow[C::NCW][C::NT];
@@ -809,21 +852,91 @@ bwd_mfma_kernel(int T, int H, int nchunks, const E* __restrict__ q, const E* __r
         }
         lds_barrier();   // before the next chunk overwrites the tiles
     }
-    if (dS0) {
+    if (!FULL) {
+        store_map(Xt);
+    } else if (dS0 && seg == 0) {
 #pragma unroll
         for (int rt = 0; rt < C::NT; ++rt)
 #pragma unroll
-            for (int cw = 0; cw < C::NCW; ++cw)
+            for (int cw = 0; cw < NCX; ++cw)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    dS0[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * C::NCW + cw) + li] = Xt[rt][cw][r];
+                    dS0[((int64_t)bh * D + 16 * rt + 4 * g + r) * D + 16 * (w * NCX + cw) + li] = Xt[rt][cw][r];
     }
+}
+
+// Chains the segment maps of one head along its segments, 16 state columns per
+// workgroup (the maps act on columns separately).  With [N_s | M_s] the map of
+// segment s: forward, Y_0 = init and Y_{s+1} = M_s Y_s + N_s (the state at
+// each segment's start); reverse, Y_{nseg-1} = init and Y_{s-1} = M_s Y_s + N_s
+// (the carried gradient at each segment's end).  Writes every Y_s to out.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_combine_kernel(int BH, int nseg, int reverse, const float* __restrict__ maps,
+                   const float* __restrict__ init, float* __restrict__ out) {
+    constexpr int NT = D / 16, R = D / 16;   // column tiles; rows per thread
+    __shared__ float Ys[D][17];
+    const int bh = blockIdx.x / NT, ct = blockIdx.x % NT;
+    const int tid = threadIdx.x, cl = tid & 15, r0 = (tid >> 4) * R;
+    const int col = 16 * ct + cl;
+    float y[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) y[r] = init ? init[((int64_t)bh * D + r0 + r) * D + col] : 0.0f;
+    int s = reverse ? nseg - 1 : 0;
+    for (int step = 0;; ++step) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            Ys[r0 + r][cl] = y[r];
+            out[(((int64_t)s * BH + bh) * D + r0 + r) * D + col] = y[r];
+        }
+        if (step == nseg - 1) break;
+        __syncthreads();
+        const float* mp = maps + ((int64_t)s * BH + bh) * D * 2 * D;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = mp[(int64_t)(r0 + r) * 2 * D + col];   // N_s
+        for (int kk = 0; kk < D; kk += 4) {
+            float yk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yk[e] = Ys[kk + e][cl];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const f32x4 m4 = *reinterpret_cast<const f32x4*>(mp + (int64_t)(r0 + r) * 2 * D + D + kk);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[r] = fmaf(m4[e], yk[e], acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) y[r] = acc[r];
+        s += reverse ? -1 : 1;
+        __syncthreads();
+    }
+}
+
+// Segments of the matrix-core backward: one per workgroup slot the heads leave
+// free, at least 16 chunks each, used only when they give four or more
+// workgroups per head (the maps cost about as much again as the pass itself).
+static int bwd_segments(int BH, int nchunks, int d, int* seg_len) {
+    *seg_len = nchunks;
+    if ((d != 64 && d != 128) || BH > 64 || nchunks < 64) return 1;
+    const int want = (256 + BH - 1) / BH;
+    int L = (nchunks + want - 1) / want;
+    if (L < 16) L = 16;
+    *seg_len = L;
+    return (nchunks + L - 1) / L;
 }
 
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d) {
     const size_t nchunks = ((size_t)T + CHUNK - 1) / CHUNK;
+    const size_t BH = (size_t)B * H;
     // every chunk's start state; the matrix-core kernel also keeps its U and Y tiles
-    return nchunks * (size_t)B * H * ((size_t)d * d + 2 * CHUNK * (size_t)d) * sizeof(float);
+    size_t n = nchunks * BH * ((size_t)d * d + 2 * CHUNK * (size_t)d);
+    int L;
+    const size_t nseg = bwd_segments((int)BH, (int)nchunks, d, &L);
+    // segmented: both maps of every segment (d x 2d), the states at the segments'
+    // starts and the carried gradients at their ends (d x d)
+    if (nseg > 1) n += nseg * BH * (4 * (size_t)d * d + 2 * (size_t)d * d);
+    return n * sizeof(float);
 }
 
 hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q, const void* k,
@@ -832,10 +945,30 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
                             float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int BH = B * H;
-#define KDA_BWD_MFMA(E, D)                                                                             \
-    hipLaunchKernelGGL((bwd_mfma_kernel<E, D>), dim3((unsigned)BH), dim3(BmCfg<D>::NTHR), 0, stream, T, H, nchunks, \
-                       (const E*)q, (const E*)k, (const E*)v, theta, beta, S0, (const E*)dout, dS_T, dq, \
-                       dk, dv, dtheta, dbeta, dS0, (float*)workspace);                                  \
+    int L;
+    const int nseg = bwd_segments(BH, nchunks, d, &L);
+    float* wsf = (float*)workspace;
+    const size_t DD = (size_t)d * d;
+    float* mapF = wsf + (size_t)nchunks * BH * (DD + 2 * CHUNK * (size_t)d);
+    float* mapB = mapF + (size_t)nseg * BH * 2 * DD;
+    float* Sst = mapB + (size_t)nseg * BH * 2 * DD;
+    float* Xen = Sst + (size_t)nseg * BH * DD;
+#define KDA_BWD_MODE(E, D, MODE, GRID, SI, XI, MP)                                                        \
+    hipLaunchKernelGGL((bwd_mfma_kernel<E, D, MODE>), dim3((unsigned)(GRID)), dim3(BmCfg<D>::NTHR), 0, stream, \
+                       T, H, BH, nchunks, L, (const E*)q, (const E*)k, (const E*)v, theta, beta, SI,          \
+                       (const E*)dout, XI, dq, dk, dv, dtheta, dbeta, dS0, wsf, MP)
+#define KDA_BWD_MFMA(E, D)                                                                              \
+    if (nseg == 1) {                                                                                    \
+        KDA_BWD_MODE(E, D, BWD_FULL, BH, S0, dS_T, nullptr);                                            \
+    } else {                                                                                            \
+        KDA_BWD_MODE(E, D, BWD_FMAP, nseg * BH, nullptr, nullptr, mapF);                                \
+        KDA_BWD_MODE(E, D, BWD_BMAP, nseg * BH, nullptr, nullptr, mapB);                                \
+        hipLaunchKernelGGL((bwd_combine_kernel<D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, stream, \
+                           BH, nseg, 0, (const float*)mapF, S0, Sst);                                   \
+        hipLaunchKernelGGL((bwd_combine_kernel<D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, stream, \
+                           BH, nseg, 1, (const float*)mapB, dS_T, Xen);                                 \
+        KDA_BWD_MODE(E, D, BWD_FULL, nseg * BH, (const float*)Sst, (const float*)Xen, nullptr);         \
+    }                                                                                                   \
     return hipGetLastError()
 #define KDA_BWD(E, D)                                                                                  \
     hipLaunchKernelGGL((bwd_kernel<E, D>), dim3((unsigned)BH), dim3(BwdCfg<D>::NTHR), 0, stream, T, H,  \
@@ -860,6 +993,7 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
     }
 #undef KDA_BWD
 #undef KDA_BWD_MFMA
+#undef KDA_BWD_MODE
     return hipErrorInvalidValue;
 }
 

@@ -240,3 +240,18 @@ def test_gate_validation(lib):
     assert lib.kda_gate(1, 64, 2, 16, vp(th), vp(th), vp(gc), None) == ALIAS
     assert lib.kda_gate(1, 64, 2, 16, vp(th), vp(g), vp(g), None) == ALIAS
     assert lib.kda_gate(1, 64, 2, 16, vp(th + 4), vp(g), None, None) == ALIGN
+
+
+def test_chunk_bwd_workspace_segmented(lib):
+    """Few heads over a long sequence: the backward splits each sequence into
+    segments and its workspace adds, per segment and head, both segment maps
+    (d x 2d each) and the state and carried gradient at the segment's ends."""
+    need = ctypes.c_size_t(0)
+    B, T, H, d = 1, 65536, 16, 128
+    assert lib.kda_chunk_bwd_workspace_size(B, T, H, d, d, ctypes.byref(need)) == OK
+    nchunks, nseg = T // 16, 16                 # 256 chunks per segment, 16 x 16 workgroups
+    per_chunk = d * d + 32 * d
+    assert need.value == 4 * (nchunks * B * H * per_chunk + nseg * B * H * 6 * d * d)
+    # many heads: one segment, no extra workspace
+    assert lib.kda_chunk_bwd_workspace_size(32, 4096, 16, d, d, ctypes.byref(need)) == OK
+    assert need.value == 4 * (4096 // 16) * 32 * 16 * per_chunk

@@ -354,7 +354,10 @@ BWD_CASES = [
     ("small", dict(dk=32, dv=32, H=3, T=333), "f32", True),
     ("small", dict(H=2, T=250), "f32", True),             # fp32, d = 64 on the matrix cores
     ("decay_stress", dict(H=2, T=512), None, True),       # d = 128 at the decay bound
-    ("prefill_64k", dict(H=2, T=2048 + 9), None, False),  # S0 = 0, no dS_T
+    ("prefill_64k", dict(H=2, T=2048 + 9), None, False),  # S0 = 0, no dS_T; 9 segments
+    ("small", dict(T=2000 + 5), None, True),              # bf16, d = 64, S0 and dS_T; 8 segments
+    ("small", dict(B=1, H=1, T=1500), "f32", True),       # fp32, d = 64; 6 segments
+    ("decay_stress", dict(H=2, T=2048 + 3), None, True),  # d = 128 at the decay bound; 9 segments
 ]
 
 
