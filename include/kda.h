@@ -162,12 +162,16 @@ int kda_chunk_fwd_unbounded(int dtype, int B, int T, int H, int dk, int dv,
  *   dbeta        [B, T, H]       fp32, written
  *   dS0          [B, H, dk, dv]  fp32, written; or NULL to skip
  *   workspace    kda_chunk_bwd_workspace_size bytes of device memory (every
- *                chunk's start state, fp32); contents on entry do not matter
+ *                chunk's start state, and at dk = 64 and 128 its U and
+ *                V - K+ S tiles and the segment maps and boundary values, fp32);
+ *                contents on entry do not matter
  *   stream       hipStream_t the work is enqueued on
  * Returns KDA_OK once enqueued.  Errors (before any HIP call): as kda_chunk_fwd;
  * every gradient output must not overlap an input, another output or the
- * workspace.  One workgroup per (batch, head): the evaluation is sequential
- * over T within a sequence.  Results are deterministic run to run.
+ * workspace.  One workgroup per (batch, head) walks the chunks in order; with
+ * at most 64 (batch, head) pairs and at least 64 chunks (dk = 64 and 128) each
+ * sequence is split into segments joined by their affine maps, as in the
+ * forward.  Results are deterministic run to run.
  * ------------------------------------------------------------------------- */
 int kda_chunk_bwd(int dtype, int B, int T, int H, int dk, int dv,
                   const void* q, const void* k, const void* v,
