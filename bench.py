@@ -292,10 +292,10 @@ def main():
         del mx, mo, mS, mws
 
     if not args.no_backward and w.name == "prefill_64k":
-        # The backward pass (first version: one workgroup per sequence and head, fp32 vector
-        # arithmetic): at the batch shape of the ablation and at this 64K prefill.
+        # The backward pass (fp32 matrix cores; segmented at this 64K prefill, one segment at
+        # the batch shape): at the batch shape of the ablation and at this 64K prefill.
         bw = {}
-        for label, bwk, reps in (("B32_T4096", kin.scaled(w, B=32, T=4096), 3), ("prefill_64k", w, 1)):
+        for label, bwk, reps in (("B32_T4096", kin.scaled(w, B=32, T=4096), 10), ("prefill_64k", w, 10)):
             bx = kin.chunk_inputs(bwk, device=dev) if bwk is not w else x
             gdo = torch.Generator(device=dev).manual_seed(bwk.seed + 2000)
             bdo = torch.randn((bwk.B, bwk.T, bwk.H, bwk.dv), generator=gdo, device=dev).to(bx["q"].dtype)
@@ -306,7 +306,7 @@ def main():
                 kda.kda_chunk_bwd(bx["q"], bx["k"], bx["v"], bx["theta"], bx["beta"], bdo, bx["S0"],
                                   workspace=bws, stream=stream)
 
-            bms, _ = time_calls(bwstep, reps, 1, stream)
+            bms, _ = time_calls(bwstep, reps, 3, stream)
             th = bwk.B * bwk.T * bwk.H
             bby = th * (es * (2 * bwk.dk + 2 * bwk.dv) + 4 * bwk.dk + 4 + 4 * (3 * bwk.dk + bwk.dv) + 4)
             bw[label] = {"B": bwk.B, "H": bwk.H, "T": bwk.T, "d": bwk.dk, "ms_per_call": bms,

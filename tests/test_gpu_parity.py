@@ -393,6 +393,31 @@ def test_chunk_bwd_deterministic():
 
 
 # ----------------------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("label,B,T,pick", [("prefill_64k", 1, 65536, (0, 5)),
+                                             ("B32_T4096", 32, 4096, (17, 3))])
+def test_chunk_bwd_full_size(oracle_mod, label, B, T, pick):
+    """The backward at the shapes and launch configuration the benchmark times (16 segments
+    of 256 chunks at the 64K prefill; one segment, 512 workgroups at B = 32), all heads
+    computed, one (sequence, head) compared with the oracle (15 s of fp64 at 64K)."""
+    w = kin.scaled(kin.WORKLOADS["prefill_64k"], B=B, T=T)
+    note(f"full-size chunk_bwd {label} {w} compared at (b, h) = {pick}")
+    x = kin.chunk_inputs(w, device=DEV)
+    gdo = torch.Generator(device=DEV).manual_seed(w.seed + 2000)
+    do = torch.randn((w.B, w.T, w.H, w.dv), generator=gdo, device=DEV).to(x["q"].dtype)
+    g = kda.kda_chunk_bwd(x["q"], x["k"], x["v"], x["theta"], x["beta"], do, x["S0"])
+    torch.cuda.synchronize()
+    b, h = pick
+    one = lambda t: t[b:b + 1, :, h:h + 1].contiguous().cpu()
+    S0 = x["S0"][b:b + 1, h:h + 1].contiguous().cpu() if x["S0"] is not None else None
+    ref = oracle_mod.chunk_bwd(one(x["q"]), one(x["k"]), one(x["v"]), one(x["theta"]), one(x["beta"]),
+                               S0, one(do), None)
+    errs = {key: rel_err(one(g[key]) if key != "dS0" else g[key][b:b + 1, h:h + 1].cpu(), ref[key])
+            for key in ("dq", "dk", "dv", "dtheta", "dbeta", "dS0")}
+    note("  " + " ".join(f"{key}={e:.2e}" for key, e in errs.items()))
+    for key, e in errs.items():
+        assert e <= TOL[w.dtype], key
+
+
 def _sampled_chunk_check(oracle_mod, name, cols, heads=None, segments=0):
     w = kin.WORKLOADS[name]
     note(f"full-size chunk_fwd {name} {w}")
