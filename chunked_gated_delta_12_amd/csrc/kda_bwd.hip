@@ -1,4 +1,4 @@
-// kda_bwd.hip -- backward pass of the chunked KDA prefill on gfx950, first version.
+// kda_bwd.hip -- backward pass of the chunked KDA prefill on gfx950.
 //
 // Gradients of L = sum_t <do_t, o_t> + <dS_T, S_T> with respect to q, k, v, theta,
 // beta and S0, evaluated chunk by chunk.  With the forward quantities of a chunk
@@ -18,19 +18,23 @@
 // cumulative log-decay, whose reverse prefix sum over the chunk gives dg, and
 // dtheta = dg * (-5) sigmoid(theta) (1 - sigmoid(theta)).
 //
-// One workgroup per (batch, head) walks the chunks forward, saving every chunk's
-// start state to the workspace, then backward.  The state recurrences act on
-// columns separately, so S and dS' live in registers by column (TPC threads per
-// column, RPT rows each); products over the state's columns read S rows from the
-// workspace and dS' rows from LDS; every row-space gradient element has one
-// owning thread, so results are deterministic.  All arithmetic is fp32 on the
-// vector units: this version is correct and simple, not yet tiled for the
-// matrix cores.
+// Two kernels evaluate it.  bwd_kernel (d = 16 and 32) is the plain fp32
+// vector-unit form: one workgroup per (batch, head) walks the chunks forward,
+// saving every chunk's start state, then backward.  bwd_mfma_kernel (d = 64
+// and 128) runs every product on the fp32 matrix cores and, for few long
+// sequences, splits them into segments joined by their affine maps
+// (bwd_combine_kernel chains them).
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
+// ---------------------------------------------------------------------------- bwd_kernel
+// One workgroup of 256 threads per (batch, head).  The state recurrences act on
+// columns separately, so S and dS' live in registers by column (TPC threads
+// per column, RPT rows each); products over the state's columns read S rows
+// from the workspace and dS' rows from LDS; every row-space gradient element
+// has one owning thread, so results are deterministic.
 template <int D>
 struct BwdCfg {
     static constexpr int NTHR = 256;
