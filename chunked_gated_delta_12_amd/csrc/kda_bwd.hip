@@ -424,6 +424,7 @@ struct BmSmem {
     float Aqk[CHUNK][C::LS];
     float dAqk[CHUNK][C::LS];
     float dA[CHUNK][C::LS];
+    float gpart[4][D];         // the gate's partial sums over each quarter of the chunk
     float gc[D], beta[CHUNK], zy[CHUNK];
 };
 
@@ -520,31 +521,45 @@ bwd_mfma_kernel(int T, int H, int BH, int nchunks, int seg_len, const E* __restr
     // gate, decay tiles, KK, A, T and (backward sweep) A_qk and dg/dtheta of the
     // chunk whose raw inputs are in LDS
     auto prepare = [&](bool bwd, int nv) {
+        static_assert(C::NTHR == 4 * D, "four threads per channel");
         lds_barrier();
-        if (tid < D) {
-            const int c = tid;
-            float G = 0.0f;
-            float gam[CHUNK];
+        // the gate: four threads per channel c, tokens 4 part .. 4 part + 3 each; the
+        // running sum of the log-decay restarts at the chunk and takes the totals of
+        // the lower quarters from LDS
+        const int c = tid % D, part = tid / D;
+        float gl[4], sgv[4], Gl = 0.0f;
 #pragma unroll
-            for (int t = 0; t < CHUNK; ++t) {
-                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * sm.gam[t][c]));
-                if (t < nv) G += G_MIN * LOG2E * sg;
-                gam[t] = __builtin_amdgcn_exp2f(G);
-                if (bwd) sm.dsg[t][c] = G_MIN * sg * (1.0f - sg);
-            }
-            const float gC = gam[CHUNK - 1];
-#pragma unroll
-            for (int t = 0; t < CHUNK; ++t) {
-                const float kk = sm.kp[t][c], qq = sm.qp[t][c];
-                const float ig = __builtin_amdgcn_rcpf(gam[t]);   // <= e^80: the bound
-                sm.gam[t][c] = gam[t];
-                sm.kp[t][c] = kk * gam[t];
-                sm.km[t][c] = kk * ig;
-                sm.qp[t][c] = qq * gam[t];
-                sm.ke[t][c] = kk * (gC * ig);
-            }
-            sm.gc[c] = gC;
+        for (int u = 0; u < 4; ++u) {
+            const int t = 4 * part + u;
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * sm.gam[t][c]));
+            sgv[u] = sg;
+            if (t < nv) Gl += G_MIN * LOG2E * sg;
+            gl[u] = Gl;
         }
+        sm.gpart[part][c] = Gl;
+        lds_barrier();
+        float off = 0.0f, tot = 0.0f;
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+            const float x = sm.gpart[p2][c];
+            if (p2 < part) off += x;
+            tot += x;
+        }
+        const float gC = __builtin_amdgcn_exp2f(tot);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = 4 * part + u;
+            const float gm = __builtin_amdgcn_exp2f(off + gl[u]);
+            const float kk = sm.kp[t][c], qq = sm.qp[t][c];
+            const float ig = __builtin_amdgcn_rcpf(gm);   // <= e^80: the bound
+            sm.gam[t][c] = gm;
+            sm.kp[t][c] = kk * gm;
+            sm.km[t][c] = kk * ig;
+            sm.qp[t][c] = qq * gm;
+            sm.ke[t][c] = kk * (gC * ig);
+            if (bwd) sm.dsg[t][c] = G_MIN * sgv[u] * (1.0f - sgv[u]);
+        }
+        if (part == 0) sm.gc[c] = gC;
         lds_barrier();
         // KK = K+ K-^T (wavefront 0) and A_qk = Q+ K-^T (wavefront 1): rows t = li of the
         // A operand, step i contracts channel 16kb + 4g + i; lane holds rows 4g..4g+3, column li
