@@ -425,7 +425,8 @@ struct BmSmem {
     float dAqk[CHUNK][C::LS];
     float dA[CHUNK][C::LS];
     float gpart[4][D];         // the gate's partial sums over each quarter of the chunk
-    float gc[D], beta[CHUNK], zy[CHUNK];
+    float zyw[BmCfg<D>::NW][CHUNK];   // rowsum(Z * Y) over each wavefront's columns
+    float gc[D], beta[CHUNK];
 };
 
 // MODE 0: both sweeps over one segment of chunks, from the state at its start
@@ -518,6 +519,33 @@ bwd_mfma_kernel(int T, int H, int BH, int nchunks, int seg_len, const E* __restr
         if (tid < CHUNK) sm.beta[tid] = r.b;
     };
 
+    // nprod (1 or 2) 16x16 products over the d channels, P0 = A0 Bm^T and P1 = A1 Bm^T
+    // (token rows in LDS).  The contraction is split over the wavefronts, the first
+    // half (all, for one product) on P0, the second on P1, each over its own channel
+    // blocks; the partial tiles meet in scratch ([wavefront][16][16], an LDS array not
+    // in use at that point) and finish(p, t, s, value) takes each summed element.
+    auto small_products = [&](const float(*A0)[C::LDR], const float(*A1)[C::LDR], const float(*Bm)[C::LDR],
+                              float* scratch, int nprod, auto finish) {
+        const int wpp = C::NW / nprod, pr = w / wpp, wl = w % wpp, kpw = C::NT / wpp;
+        const float(*Am)[C::LDR] = pr == 0 ? A0 : A1;
+        f32x4 acc = zero4;
+        for (int j = 0; j < kpw; ++j) {
+            const int kb = wl * kpw + j;
+            const f32x4 a4 = ld4(&Am[li][16 * kb + 4 * g]), b4 = ld4(&Bm[li][16 * kb + 4 * g]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = mfma_k4(a4[i], b4[i], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scratch[w * 256 + (4 * g + r) * 16 + li] = acc[r];
+        lds_barrier();
+        for (int e = tid; e < nprod * 256; e += C::NTHR) {
+            const int p = e >> 8, ts = e & 255;
+            float v = 0.0f;
+            for (int x = 0; x < wpp; ++x) v += scratch[(p * wpp + x) * 256 + ts];
+            finish(p, ts >> 4, ts & 15, v);
+        }
+    };
+
     // gate, decay tiles, KK, A, T and (backward sweep) A_qk and dg/dtheta of the
     // chunk whose raw inputs are in LDS
     auto prepare = [&](bool bwd, int nv) {
@@ -561,28 +589,15 @@ bwd_mfma_kernel(int T, int H, int BH, int nchunks, int seg_len, const E* __restr
         }
         if (part == 0) sm.gc[c] = gC;
         lds_barrier();
-        // KK = K+ K-^T (wavefront 0) and A_qk = Q+ K-^T (wavefront 1): rows t = li of the
-        // A operand, step i contracts channel 16kb + 4g + i; lane holds rows 4g..4g+3, column li
-        if (w == 0 || (bwd && w == 1)) {
-            const float(*Am)[C::LDR] = w == 0 ? sm.kp : sm.qp;
-            f32x4 acc = zero4;
-#pragma unroll
-            for (int kb = 0; kb < C::NT; ++kb) {
-                const f32x4 a4 = ld4(&Am[li][16 * kb + 4 * g]), b4 = ld4(&sm.km[li][16 * kb + 4 * g]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma_k4(a4[i], b4[i], acc);
+        // KK = K+ K-^T and (backward sweep) A_qk = Q+ K-^T; Z is not in use yet
+        small_products(sm.kp, sm.qp, sm.km, &sm.Z[0][0], bwd ? 2 : 1, [&](int p, int t, int s2, float x) {
+            if (p == 0) {
+                sm.KK[t][s2] = x;
+                sm.A[t][s2] = s2 < t ? sm.beta[t] * x : 0.0f;
+            } else {
+                sm.Aqk[t][s2] = s2 <= t ? x : 0.0f;
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r, s = li;
-                if (w == 0) {
-                    sm.KK[t][s] = acc[r];
-                    sm.A[t][s] = s < t ? sm.beta[t] * acc[r] : 0.0f;
-                } else {
-                    sm.Aqk[t][s] = s <= t ? acc[r] : 0.0f;
-                }
-            }
-        }
+        });
         lds_barrier();
         if (tid < CHUNK) {   // T = (I + A)^-1, column tid, forward substitution
             const int cj = tid;
@@ -736,6 +751,16 @@ bwd_mfma_kernel(int T, int H, int BH, int nchunks, int seg_len, const E* __restr
                     if (t < nv) dv[hb + (tc + t) * tstr + col] = dy[r];
                 }
             }
+            if (FULL) {   // rowsum(Z * Y) over this column tile (NCW = 1): the 16 lanes of a lane group
+                static_assert(!FULL || C::NCW == 1, "one column tile per wavefront");
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float zy = z[r] * sm.Y[4 * g + r][col];
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) zy += __shfl_xor(zy, o);
+                    if (li == 0) sm.zyw[w][4 * g + r] = zy;
+                }
+            }
             // dS' <- Diag(Gamma_C) dS' + Q+^T dO - K+^T dY
 #pragma unroll
             for (int rt = 0; rt < C::NT; ++rt) {
@@ -761,33 +786,17 @@ bwd_mfma_kernel(int T, int H, int BH, int nchunks, int seg_len, const E* __restr
                 srow[cw][kb] = ld4(wsn + (int64_t)(16 * (w * C::NCW + cw) + li) * D + 16 * kb + 4 * g);
         lds_barrier();   // Z complete
 
-        if (w < 2) {   // dA_qk = LowerIncl(dO U^T) (wavefront 0), dA = StrictLower(-Z U^T) (wavefront 1)
-            const float(*Am)[C::LDR] = w == 0 ? sm.dO : sm.Z;
-            f32x4 acc = zero4;
-#pragma unroll
-            for (int kb = 0; kb < C::NT; ++kb) {
-                const f32x4 a4 = ld4(&Am[li][16 * kb + 4 * g]), b4 = ld4(&sm.U[li][16 * kb + 4 * g]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc = mfma_k4(a4[i], b4[i], acc);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r, s = li;
-                if (w == 0) sm.dAqk[t][s] = s <= t ? acc[r] : 0.0f;
-                else sm.dA[t][s] = s < t ? -acc[r] : 0.0f;
-            }
-        } else if (w < 4) {   // rowsum(Z * Y): wavefronts 2 and 3, 8 threads per token
-            const int t = (tid - 128) >> 3, part = tid & 7;
-            float a = 0.0f;
-            for (int c = part; c < D; c += 8) a = fmaf(sm.Z[t][c], sm.Y[t][c], a);
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1) a += __shfl_xor(a, o);
-            if (part == 0) sm.zy[t] = a;
-        }
+        // dA_qk = LowerIncl(dO U^T), dA = StrictLower(-Z U^T); Y is no longer needed
+        small_products(sm.dO, sm.Z, sm.U, &sm.Y[0][0], 2, [&](int p, int t, int s2, float x) {
+            if (p == 0) sm.dAqk[t][s2] = s2 <= t ? x : 0.0f;
+            else sm.dA[t][s2] = s2 < t ? -x : 0.0f;
+        });
         lds_barrier();
         if (tid < CHUNK) {   // dbeta = rowsum(dA * K+ K-^T) + rowsum(Z * Y)
             const int t = tid;
-            float a = sm.zy[t];
+            float a = 0.0f;
+#pragma unroll
+            for (int x = 0; x < C::NW; ++x) a += sm.zyw[x][t];
 #pragma unroll
             for (int s2 = 0; s2 < CHUNK; ++s2) a = fmaf(sm.dA[t][s2], sm.KK[t][s2], a);
             if (t < nv) dbeta[bb + (int64_t)(tc + t) * H] = a;
