@@ -358,6 +358,7 @@ BWD_CASES = [
     ("small", dict(T=2000 + 5), None, True),              # bf16, d = 64, S0 and dS_T; 8 segments
     ("small", dict(B=1, H=1, T=1500), "f32", True),       # fp32, d = 64; 6 segments
     ("decay_stress", dict(H=2, T=2048 + 3), None, True),  # d = 128 at the decay bound; 9 segments
+    ("decay_stress", dict(B=1, H=1, T=1100), "f32", True),  # fp32, d = 128; 5 segments
 ]
 
 
