@@ -10,6 +10,7 @@ has not been built, every call raises.
     o, S_T = kda_chunk_fwd(q, k, v, theta, beta, S0=None)
     o      = kda_decode_step(q, k, v, theta, beta, S)        # S updated in place
     o, S_T = kda_chunk_fwd_gated(q, k, v, theta, beta, z)    # o * sigmoid(z)
+    o, S_T = kda_chunk_fwd_noalloc(q, k, v, theta, beta, S0=None, o=o, S_T=S_T)
     o      = kda_decode_step_gated(q, k, v, theta, beta, S, z)
     g, gc  = kda_gate(theta)
 """
@@ -56,6 +57,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_auto_segments.restype = c_int
     lib.kda_decode_step.argtypes = [c_int] * 5 + [vp] * 3 + [fp] * 3 + [vp, vp]
     lib.kda_decode_step.restype = c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [c_int] * 7 + [vp] * 3 + [fp] * 3 + [vp, fp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = c_int
     lib.kda_chunk_fwd_gated.argtypes = [c_int] * 7 + [vp] * 3 + [fp] * 3 + [vp, vp, fp, vp, c_size, vp]
     lib.kda_chunk_fwd_gated.restype = c_int
     lib.kda_chunk_bwd.argtypes = [c_int] * 6 + [vp] * 3 + [fp] * 3 + [vp, fp] + [fp] * 6 + [vp, c_size, vp]
@@ -147,6 +150,14 @@ def kda_chunk_fwd_gated(q, k, v, theta, beta, z, S0=None, *, segments=0, o=None,
     return _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream)
 
 
+def kda_chunk_fwd_noalloc(q, k, v, theta, beta, S0=None, *, segments=0, o=None, S_T=None,
+                          want_state=True, stream=None):
+    """kda_chunk_fwd without a workspace: libkda uses its static per-device scratch
+    (KDA_NOALLOC_SCRATCH_BYTES).  Pass o and S_T to make the call allocate nothing."""
+    return _chunk_fwd(q, k, v, theta, beta, S0, None, segments, o, S_T, want_state, None, stream,
+                      noalloc=True)
+
+
 def kda_chunk_fwd_unbounded(q, k, v, theta, beta, S0=None, *, o=None, S_T=None, want_state=True,
                             stream=None):
     """The ablation of the bound: the recurrence with the unbounded gate
@@ -155,7 +166,7 @@ def kda_chunk_fwd_unbounded(q, k, v, theta, beta, S0=None, *, o=None, S_T=None, 
 
 
 def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, workspace, stream,
-               unbounded=False):
+               unbounded=False, noalloc=False):
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -177,7 +188,7 @@ def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, worksp
         S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     if S_T is not None:
         _need(S_T, "S_T", torch.float32, (B, H, dk, dv), dev)
-    nbytes = 0 if unbounded else kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments)
+    nbytes = 0 if (unbounded or noalloc) else kda_chunk_fwd_workspace_size(B, T, H, dk, dv, segments)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -185,6 +196,11 @@ def _chunk_fwd(q, k, v, theta, beta, S0, z, segments, o, S_T, want_state, worksp
         st = lib.kda_chunk_fwd_unbounded(code, B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
                                          _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _stream(q, stream))
         _check("kda_chunk_fwd_unbounded", st)
+    elif noalloc:
+        st = lib.kda_chunk_fwd_noalloc(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(theta), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+                                       _stream(q, stream))
+        _check("kda_chunk_fwd_noalloc", st)
     elif z is None:
         st = lib.kda_chunk_fwd(code, B, T, H, dk, dv, segments, _ptr(q), _ptr(k), _ptr(v), _ptr(theta),
                                _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes,
@@ -302,7 +318,7 @@ def kda_gate(theta, *, g=True, g_cum=True, stream=None):
     return g, g_cum
 
 
-__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_unbounded", "kda_chunk_bwd",
+__all__ = ["kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_gated", "kda_chunk_fwd_unbounded", "kda_chunk_bwd",
            "kda_chunk_bwd_workspace_size", "kda_decode_step",
            "kda_decode_step_gated", "kda_gate", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_auto_segments", "load_library", "header_functions", "KdaError",

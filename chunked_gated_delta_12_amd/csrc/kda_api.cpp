@@ -10,10 +10,25 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "kda.h"
 #include "kda_launch.hpp"
 
+// Device scratch of kda_chunk_fwd_noalloc: the workspace of a segmented
+// prefill (segment maps, segment start states, every chunk's T') for callers
+// that cannot allocate.  Each device holds its own copy from the first call on
+// it until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels and copies get the per-device
+// address that hipGetSymbolAddress returns (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device addresses of `scratch`, one per device, resolved once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 thread_local char g_last_error[512] = "";
 
@@ -117,12 +132,35 @@ int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segmen
     return ok();
 }
 
-// kda_chunk_fwd, kda_chunk_fwd_gated and kda_chunk_fwd_unbounded; z (the output
-// gate's pre-activation) is NULL for the first and the last.
+// The address of `scratch` on the calling thread's current device (resolved
+// with that device current on its first use there).
+static int scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_HIP, "device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
+// kda_chunk_fwd, kda_chunk_fwd_gated, kda_chunk_fwd_unbounded and
+// kda_chunk_fwd_noalloc; z (the output gate's pre-activation) is NULL but for
+// the gated call.  noalloc: the workspace is the current device's static
+// scratch instead of the caller's (workspace is then NULL and workspace_bytes 0).
 static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
                           const void* k, const void* v, const float* theta, const float* beta,
                           const float* S0, const void* z, void* o, float* S_T, void* workspace,
-                          size_t workspace_bytes, void* stream, bool unbounded = false) {
+                          size_t workspace_bytes, void* stream, bool unbounded = false,
+                          bool noalloc = false) {
     int st = check_common(dtype, B, H, dk, dv);
     if (st) return st;
     if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
@@ -142,9 +180,16 @@ static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int se
     const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
     const kda::SegPlan plan = kda::plan_segments(T, req);
     const size_t need = kda::chunk_workspace_bytes(B, H, dk, dv, plan.nseg, plan.nchunks);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (noalloc) {
+        if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+            return fail(KDA_ERR_WORKSPACE,
+                        "%d segments need %zu bytes of scratch, more than the static %zu; pass fewer "
+                        "segments (1 needs none) or call kda_chunk_fwd with a workspace",
+                        plan.nseg, need, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need,
                     workspace_bytes, workspace ? "" : " (NULL)");
+    }
 
     const size_t es = dtype == KDA_BF16 ? 2 : 4;
     const size_t tok = (size_t)B * T * H;
@@ -165,6 +210,10 @@ static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int se
     if (overlap(r_o, r_ws)) return fail(KDA_ERR_ALIAS, "o overlaps workspace");
     if (overlap(r_st, r_ws)) return fail(KDA_ERR_ALIAS, "S_T overlaps workspace");
 
+    if (noalloc && need > 0) {   // every argument check is done: now the first HIP call
+        st = scratch_on_current_device(&workspace);
+        if (st) return st;
+    }
     hipError_t e = kda::launch_chunk_fwd(dtype == KDA_F32, B, T, H, dk, plan, q, k, v, theta, beta, S0,
                                          z, o, S_T, need ? workspace : nullptr,
                                          reinterpret_cast<hipStream_t>(stream), unbounded);
@@ -178,6 +227,13 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments, 
                   void* stream) {
     return chunk_fwd_impl(dtype, B, T, H, dk, dv, segments, q, k, v, theta, beta, S0, nullptr, o, S_T,
                           workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_noalloc(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,
+                          const void* k, const void* v, const float* theta, const float* beta,
+                          const float* S0, void* o, float* S_T, void* stream) {
+    return chunk_fwd_impl(dtype, B, T, H, dk, dv, segments, q, k, v, theta, beta, S0, nullptr, o, S_T,
+                          nullptr, 0, stream, false, true);
 }
 
 int kda_chunk_fwd_gated(int dtype, int B, int T, int H, int dk, int dv, int segments, const void* q,

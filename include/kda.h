@@ -15,8 +15,9 @@
  *
  * Conventions shared by every call:
  *  - Pointers are DEVICE pointers into memory the caller owns (for instance
- *    torch tensors).  The library never allocates, frees or retains them, and
- *    keeps no global mutable state apart from a thread-local error string.
+ *    torch tensors).  The library never allocates, frees or retains them.
+ *    Its only global state is a thread-local error string and, for
+ *    kda_chunk_fwd_noalloc, one static device scratch array per device.
  *  - Tensors are dense and row-major in the layouts stated per argument; the
  *    innermost dimension is contiguous.  Every pointer must be 16-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -100,6 +101,35 @@ int kda_chunk_fwd(int dtype, int B, int T, int H, int dk, int dv, int segments,
                   const float* theta, const float* beta, const float* S0,
                   void* o, float* S_T,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch that kda_chunk_fwd_noalloc holds per device. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* ---------------------------------------------------------------------------
+ * kda_chunk_fwd_noalloc: kda_chunk_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It takes no workspace: a segmented call uses a static
+ * device array of KDA_NOALLOC_SCRATCH_BYTES (128 MiB) that each device the
+ * library runs on holds from its first call there until the process ends.
+ * The call itself allocates and frees nothing.
+ *
+ *   Every argument and the result are those of kda_chunk_fwd, without
+ *   workspace and workspace_bytes.  The scratch is the one of the calling
+ *   thread's current device; `stream` must belong to that device.
+ *   Errors: those of kda_chunk_fwd, and KDA_ERR_WORKSPACE when the segment
+ *   count (given, or the automatic one for segments = 0) needs more than
+ *   KDA_NOALLOC_SCRATCH_BYTES (kda_chunk_fwd_workspace_size gives the need;
+ *   one segment needs none).  The 64K-token prefill of 16 heads at d = 128
+ *   with its automatic 16 segments needs 110 MiB and fits.
+ *   The scratch holds nothing that must start at zero and keeps the last
+ *   call's contents.  Every call on one device shares that device's scratch:
+ *   calls that overlap in time on one device (several streams or threads)
+ *   race and give undefined results; serialise them.
+ * ------------------------------------------------------------------------- */
+int kda_chunk_fwd_noalloc(int dtype, int B, int T, int H, int dk, int dv, int segments,
+                          const void* q, const void* k, const void* v,
+                          const float* theta, const float* beta, const float* S0,
+                          void* o, float* S_T, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kda_chunk_fwd_gated: kda_chunk_fwd with the output gate applied to o

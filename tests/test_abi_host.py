@@ -104,6 +104,38 @@ def test_chunk_fwd_gated_validation(lib):
     assert call(z, o=b.addr["q"]) == ALIAS
 
 
+def test_chunk_fwd_noalloc_validation(lib):
+    """The no-allocation entry point runs kda_chunk_fwd's host checks and refuses a
+    segment count whose workspace exceeds its static scratch, before any HIP call."""
+    vp = ctypes.c_void_p
+
+    def call(b, segments=1, dtype=0, **over):
+        a = dict(b.addr)
+        a.update(over)
+        p = lambda n: vp(a[n]) if a[n] is not None else None
+        return lib.kda_chunk_fwd_noalloc(dtype, b.B, b.T, b.H, b.d, b.d, segments, p("q"), p("k"), p("v"),
+                                         p("theta"), p("beta"), p("S0"), p("o"), p("S_T"), None)
+
+    b = Bufs()
+    assert call(b, dtype=2) == DTYPE
+    for name in ("q", "k", "v", "theta", "beta", "o"):
+        assert call(b, **{name: None}) == NULL, name
+    assert call(b, q=b.addr["q"] + 8) == ALIGN
+    assert call(b, o=b.addr["k"]) == ALIAS
+    assert call(b, segments=5) == SHAPE
+    limit = 128 * MB
+    # 2^17 tokens of 16 heads at d = 128: the automatic 16 segments need 182 MB
+    big = Bufs(T=1 << 17, H=16, d=128)
+    need = kda.kda_chunk_fwd_workspace_size(1, 1 << 17, 16, 128, 128, 0)
+    assert need > limit
+    assert call(big, segments=0) == WORKSPACE
+    msg = lib.kda_last_error().decode()
+    assert "scratch" in msg and str(limit) in msg
+    assert call(big, segments=64) == WORKSPACE
+    # the 64K prefill at its automatic segment count fits the scratch
+    assert 0 < kda.kda_chunk_fwd_workspace_size(1, 65536, 16, 128, 128, 0) <= limit
+
+
 def test_chunk_fwd_unbounded_validation(lib):
     """The ablation entry point runs the same host checks as kda_chunk_fwd (before any
     HIP call) and takes no workspace."""
