@@ -3,8 +3,10 @@
     python -m chunked_gated_delta_12_amd.build
 
 Each translation unit is compiled on its own (in parallel) and then linked into
-chunked_gated_delta_12_amd/libkda.so.  Packed fp32 instructions are disabled
-for all device code.
+chunked_gated_delta_12_amd/libkda.so.  The reference measurements of
+include/kda_peaks.h (a streaming copy, a bf16 matrix-core loop, the device's
+description) go into a library of their own, libkda_peaks.so.  Packed fp32
+instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
+PEAKS_LIB = os.path.join(HERE, "libkda_peaks.so")
+PEAKS_SOURCES = ["kda_peaks.hip"]
 SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_decode.hip", "kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_bwd.hip"]
 ARCH = "gfx950"
 
@@ -46,18 +50,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{res.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

@@ -194,6 +194,34 @@ def chunk_fwd(q, k, v, theta, beta, S0=None, cols=None, nthreads=None):
     return _run(_load().kda_oracle_chunk_fwd, q, k, v, theta, beta, S0, cols, nthreads)
 
 
+def chunk_fwd_column_blocks(q, k, v, theta, beta, S0=None, nthreads=None):
+    """chunk_fwd over every value column for few (batch, head) sequences: the
+    columns are cut into blocks that run concurrently (each block is the column
+    subset of the same recurrence, which evolves independently of the other
+    columns), so all threads work even when B*H is small.  Returns (o, S_T)."""
+    import concurrent.futures as cf
+    q, k, v, theta, beta, S0 = _d(q), _d(k), _d(v), _d(theta), _d(beta), _d(S0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    n = nthreads or default_threads()
+    nblk = max(1, min(n // max(1, B * H), dv))
+    if nblk == 1:
+        return chunk_fwd(q, k, v, theta, beta, S0, nthreads=n)
+    g = gate(theta)
+    blocks = [list(range(i * dv // nblk, (i + 1) * dv // nblk)) for i in range(nblk)]
+    o = np.empty((B, T, H, dv))
+    S_T = np.empty((B, H, dk, dv))
+
+    def one(cols):
+        ob, sb = recurrence(q, k, v, g, beta, S0, cols=cols, nthreads=B * H)
+        o[..., cols] = ob
+        S_T[..., cols] = sb
+
+    with cf.ThreadPoolExecutor(max_workers=nblk) as ex:
+        list(ex.map(one, blocks))
+    return o, S_T
+
+
 def decode_step(q, k, v, theta, beta, S, nthreads=None):
     """One decode step. q,k,theta [B,H,dk], v [B,H,dv], beta [B,H], S [B,H,dk,dv].
     Returns (o [B,H,dv], S_new) without modifying the caller's S."""

@@ -28,6 +28,26 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
 
+def test_peaks_library_exports_its_header():
+    """libkda_peaks.so (the benchmark's reference copy and matrix-core loops) exports
+    every function include/kda_peaks.h declares, and rejects bad arguments on the host."""
+    from chunked_gated_delta_12_amd import peaks
+    try:
+        plib = peaks.load_library()
+    except RuntimeError as e:
+        pytest.skip(str(e))
+    names = kda.header_functions(peaks.HEADER_PATH)
+    assert set(names) == {"kda_peaks_copy", "kda_peaks_mfma_bf16", "kda_peaks_device"}
+    for n in names:
+        assert hasattr(plib, n), n
+    vp = ctypes.c_void_p
+    assert plib.kda_peaks_copy(vp(1 << 40), vp(1 << 41), 100, None) == 1          # not a multiple of 16
+    assert plib.kda_peaks_copy(vp(1 << 40), vp((1 << 40) + 64), 1 << 20, None) == 1   # overlap
+    assert plib.kda_peaks_copy(None, vp(1 << 41), 16, None) == 1
+    assert plib.kda_peaks_mfma_bf16(None, 8, 10, None) == 1
+    assert plib.kda_peaks_mfma_bf16(vp(1 << 40), 0, 10, None) == 1
+
+
 def test_abi_version_and_strings(lib):
     assert lib.kda_abi_version() == 1
     for s in range(8):

@@ -397,3 +397,101 @@ def test_workload_chunk_decay_within_bound(oracle_mod, name):
     assert G.min() >= -80.0
     if name == "decay_stress":   # sigma(8 +- 1): most chunks come within 1% of the bound
         assert G.min() < -79.0
+
+
+# ----------------------------------------------------------------------------- brute force
+def _expanded_products(q, k, v, g, beta, S0):
+    """The recurrence written as a sum of products of per-token transition matrices,
+    vectorised over a batch of independent sequences ([N, T, d] arrays, S0 [N, d, d]).
+    Decay, read and write of one token combine into S_t = M_t S_{t-1} + beta_t k_t v_t^T
+    with M_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)), hence
+        S_t = P_{t,0} S0 + sum_{s<=t} P_{t,s} beta_s k_s v_s^T,  P_{t,s} = M_t ... M_{s+1},
+    and o_t = S_t^T q_t.  Every product P_{t,s} is formed explicitly."""
+    N, T, d = q.shape
+    eye = np.broadcast_to(np.eye(d), (N, d, d))
+    M = [(eye - beta[:, t, None, None] * np.einsum("ni,nj->nij", k[:, t], k[:, t]))
+         @ (np.exp(g[:, t])[:, None, :] * eye) for t in range(T)]
+    o = np.empty((N, T, d))
+    S = None
+    for t in range(T):
+        P = eye.copy()                      # P_{t,t}
+        S = np.zeros((N, d, d))
+        for s in range(t, -1, -1):
+            S = S + P @ (beta[:, s, None, None] * np.einsum("ni,nj->nij", k[:, s], v[:, s]))
+            P = P @ M[s]                    # P_{t,s-1}
+        S = S + P @ S0                      # P_{t,0} S0
+        o[:, t] = np.einsum("nij,ni->nj", S, q[:, t])
+    return o, S
+
+
+def test_brute_force_grid_against_expanded_products(oracle_mod):
+    """Every combination, at each of 4 tokens with d = 2, of the per-channel log-decay
+    g in {0, -ln 2, -5} and beta in {0, 1/2, 1} (27^4 = 531,441 sequences), with fixed
+    non-orthogonal keys, values, queries and a non-zero start state: the oracle's
+    outputs and final state match the expanded-product form to 1e-12."""
+    levels_g = [0.0, -math.log(2.0), -5.0]
+    levels_b = [0.0, 0.5, 1.0]
+    per_tok = [(g0, g1, b) for g0 in levels_g for g1 in levels_g for b in levels_b]   # 27
+    T, d = 4, 2
+    idx = np.stack(np.meshgrid(*[np.arange(27)] * T, indexing="ij"), -1).reshape(-1, T)
+    tab = np.array(per_tok)                                  # [27, 3]
+    N = idx.shape[0]
+    g = tab[idx][..., :2]                                    # [N, T, 2]
+    beta = tab[idx][..., 2]                                  # [N, T]
+    keys = np.array([[1.0, 0.0], [0.6, 0.8], [0.0, 1.0], [0.8, -0.6]])
+    vals = np.array([[2.0, 3.0], [4.0, -2.0], [1.0, 1.0], [-3.0, 0.5]])
+    qs = np.array([[1.0, 1.0], [2.0, 1.0], [1.0, 0.0], [-1.0, 2.0]])
+    k = np.broadcast_to(keys, (N, T, d)).copy()
+    v = np.broadcast_to(vals, (N, T, d)).copy()
+    q = np.broadcast_to(qs, (N, T, d)).copy()
+    S0 = np.broadcast_to(np.array([[0.5, -1.0], [2.0, 0.25]]), (N, d, d)).copy()
+    o, S_T = oracle_mod.recurrence(q[:, :, None], k[:, :, None], v[:, :, None], g[:, :, None],
+                                   beta[:, :, None], S0[:, None])
+    o_x, S_x = _expanded_products(q, k, v, g, beta, S0)
+    np.testing.assert_allclose(o[:, :, 0], o_x, rtol=0, atol=1e-12 * np.abs(o_x).max())
+    np.testing.assert_allclose(S_T[:, 0], S_x, rtol=0, atol=1e-12 * np.abs(S_x).max())
+    # the grid reaches the special cases: beta = 0 everywhere leaves only decay
+    nowrite = np.all(beta == 0, axis=1)
+    decay = np.exp(g.sum(axis=1))                            # [N, 2]
+    np.testing.assert_allclose(S_T[nowrite, 0], decay[nowrite][:, :, None] * S0[nowrite], rtol=1e-13)
+
+
+def test_expanded_products_catch_planted_mistakes(oracle_mod):
+    """The brute-force comparison fails for plausible mistakes in a recurrence: the
+    decay applied after the write, or the read taken before the decay."""
+    rng = np.random.default_rng(21)
+    N, T, d = 64, 4, 2
+    q, v = rng.standard_normal((N, T, d)), rng.standard_normal((N, T, d))
+    k = rng.standard_normal((N, T, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    g = rng.choice([0.0, -math.log(2.0), -5.0], size=(N, T, d))
+    beta = rng.choice([0.5, 1.0], size=(N, T))
+    S0 = rng.standard_normal((N, d, d))
+    o_x, _ = _expanded_products(q, k, v, g, beta, S0)
+
+    def wrong(order):
+        S = S0.copy()
+        o = np.empty((N, T, d))
+        for t in range(T):
+            D = np.exp(g[:, t])[:, :, None]
+            if order == "decay_after_write":
+                u = beta[:, t, None] * (v[:, t] - np.einsum("nij,ni->nj", S, k[:, t]))
+                S = D * (S + np.einsum("ni,nj->nij", k[:, t], u))
+            else:   # read before decay
+                u = beta[:, t, None] * (v[:, t] - np.einsum("nij,ni->nj", S, k[:, t]))
+                S = D * S + np.einsum("ni,nj->nij", k[:, t], u)
+            o[:, t] = np.einsum("nij,ni->nj", S, q[:, t])
+        return o
+
+    for order in ("decay_after_write", "read_before_decay"):
+        assert np.abs(wrong(order) - o_x).max() > 1e-3 * np.abs(o_x).max(), order
+
+
+def test_column_blocks_match_full(oracle_mod):
+    """The concurrent column-block evaluation (for few sequences) equals the plain call."""
+    rng = np.random.default_rng(22)
+    q, k, v, theta, beta, S0 = _rand_case(rng, 1, 45, 2, 8, 12)
+    o, S_T = oracle_mod.chunk_fwd(q, k, v, theta, beta, S0)
+    ob, Sb = oracle_mod.chunk_fwd_column_blocks(q, k, v, theta, beta, S0, nthreads=8)
+    np.testing.assert_array_equal(ob, o)
+    np.testing.assert_array_equal(Sb, S_T)
