@@ -5,7 +5,10 @@ states the compiler inserts after it, came back stale on gfx950 (wrong output
 rows in an otherwise correct kernel), so K = 16 bf16 products are issued as
 16x16x32 with half the k-slots zeroed.  This test compiles every HIP source to
 assembly and fails if the legacy instruction appears again.  It also checks
-that no kernel spills to scratch.
+that no kernel spills to scratch, with one stated exception: the gated
+single-segment chunk kernel at d = 128 keeps one 4-byte value in scratch (8
+bytes per lane) across its chunk loop, stored once before the loop and read
+once after it.
 """
 import os
 import re
@@ -72,22 +75,38 @@ def _loop_bodies(text):
     return out
 
 
+# The one kernel allowed scratch: chunk_kernel<E, 128, 4, single segment, gated, bounded>.
+_SCRATCH_ALLOWED = re.compile(r"_ZN3kda12chunk_kernelI(f|DF16b)Li128ELi4ELb0ELb1ELb0E")
+
+
+def _scratch_per_function(remarks):
+    out, fn = {}, None
+    for l in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", l)
+        if m:
+            fn = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", l)
+        if m and fn:
+            out[fn] = int(m.group(1))
+    return out
+
+
 @pytest.mark.parametrize("src", HIP_SOURCES)
 def test_no_spills_inside_loops(assembly, src):
-    """Registers may spill around a kernel's prologue/epilogue (bounded below), but
-    (almost) never inside a loop, where it costs memory traffic every iteration."""
+    """No kernel uses scratch, except the gated single-segment chunk kernel at d = 128
+    (8 bytes per lane, outside its loops); and no loop body touches scratch."""
     text, remarks = assembly[src]
-    sizes = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", remarks)]
-    assert sizes and max(sizes) <= 64, f"{src}: scratch use {max(sizes)} bytes/lane"
+    per = _scratch_per_function(remarks)
+    assert per, f"{src}: no resource-usage remarks"
+    bad = {fn: n for fn, n in per.items() if n and not (_SCRATCH_ALLOWED.match(fn) and n <= 8)}
+    assert not bad, f"{src}: scratch use (bytes/lane): {bad}"
     bodies = _loop_bodies(text)
     if src in ("kda_chunk.hip", "kda_map.hip", "kda_out.hip"):
         assert bodies, "the per-chunk loops were not found"
     per_fn = {}
     for fn, body in bodies:
         per_fn[fn] = per_fn.get(fn, 0) + sum("scratch_" in l for l in body)
-    # A stray reload or two per iteration is noise next to the loop's hundreds of
-    # instructions; anything more means the kernel's registers no longer fit.
-    bad = {fn: n for fn, n in per_fn.items() if n > 2}
+    bad = {fn: n for fn, n in per_fn.items() if n}
     assert not bad, f"{src}: spills inside loops: {bad}"
 
 
