@@ -954,6 +954,23 @@ static int bwd_segments(int BH, int nchunks, int d, int* seg_len) {
     return (nchunks + L - 1) / L;
 }
 
+hipError_t launch_bwd_combine(int d, int BH, int nseg, int reverse, const float* maps, const float* init,
+                              float* out, hipStream_t stream) {
+    switch (d) {
+        case 64:
+            hipLaunchKernelGGL((bwd_combine_kernel<64>), dim3((unsigned)(BH * 4)), dim3(256), 0, stream, BH, nseg,
+                               reverse, maps, init, out);
+            return hipGetLastError();
+        case 128:
+            hipLaunchKernelGGL((bwd_combine_kernel<128>), dim3((unsigned)(BH * 8)), dim3(256), 0, stream, BH, nseg,
+                               reverse, maps, init, out);
+            return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+// The size serves both input types: the fp32 kernels' layout (fp32 chunk states,
+// U and Y) and, for d = 64 and 128, the bf16 kernel's (kda_bwd2.hip).
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d) {
     const size_t nchunks = ((size_t)T + CHUNK - 1) / CHUNK;
     const size_t BH = (size_t)B * H;
@@ -964,7 +981,12 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d) {
     // segmented: both maps of every segment (d x 2d), the states at the segments'
     // starts and the carried gradients at their ends (d x d)
     if (nseg > 1) n += nseg * BH * (4 * (size_t)d * d + 2 * (size_t)d * d);
-    return n * sizeof(float);
+    size_t bytes = n * sizeof(float);
+    if (d == 64 || d == 128) {
+        const size_t b2 = chunk_bwd2_workspace_bytes(B, T, H, d, (int)nseg);
+        if (b2 > bytes) bytes = b2;
+    }
+    return bytes;
 }
 
 hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q, const void* k,
@@ -975,6 +997,9 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
     const int BH = B * H;
     int L;
     const int nseg = bwd_segments(BH, nchunks, d, &L);
+    if (!f32 && (d == 64 || d == 128))   // bf16 inputs: the bf16 matrix-core kernel
+        return launch_chunk_bwd2(B, T, H, d, nseg, L, q, k, v, theta, beta, S0, dout, dS_T, dq, dk, dv, dtheta,
+                                 dbeta, dS0, workspace, stream);
     float* wsf = (float*)workspace;
     const size_t DD = (size_t)d * d;
     float* mapF = wsf + (size_t)nchunks * BH * (DD + 2 * CHUNK * (size_t)d);

@@ -1,0 +1,730 @@
+// kda_bwd2.hip -- backward pass of the chunked KDA prefill for bf16 inputs at
+// d = 64 and 128, on the bf16 matrix cores (16x16x32, fp32 accumulation).
+//
+// The chunk algebra is the one of kda_bwd.hip ("Kimi K3 Deep Dive...", "The
+// Problem: The Diagonal-Block Dilemma" for the chunk form; the bounded gate of
+// "Architecture Deep Dive: Kimi K3...", section 3.2).  Per chunk, with start
+// state S, K+ = K*Gamma, K- = K/Gamma, Q+ = Q*Gamma, Kend = K*Gamma_C/Gamma,
+// T = (I + StrictLower(diag(beta) K+ K-^T))^-1, Y = V - K+ S, U = T diag(beta) Y,
+// A_qk = LowerIncl(Q+ K-^T), and the gradients dO of its outputs and dS' of its
+// end state:
+//     dU = A_qk^T dO + Kend dS',  Z = T^T dU,  dY = diag(beta) Z = dV
+//     dS = Diag(Gamma_C) dS' + Q+^T dO - K+^T dY            (to the previous chunk)
+//     dQ+ = dO S^T + dA_qk K-,   dK+ = diag(beta) (dA K- - Z S^T)
+//     dK- = dA_qk^T Q+ + (diag(beta) dA)^T K+,   dKend = U dS'^T
+//     dA_qk = LowerIncl(dO U^T),  dA = StrictLower(-Z U^T)
+//     dbeta = rowsum(dA * K+ K-^T) + rowsum(Z * V) - rowsum(K+ * (Z S^T))
+// (the last two terms are rowsum(Z * Y), with Y = V - K+ S expanded so that Y
+// need not be kept), then the chain through the decay scalings to K, Q and the
+// chunk-local cumulative log-decay as in kda_bwd.hip.
+//
+// Layout of the work.  One workgroup per (segment, batch, head), D/16
+// wavefronts; wavefront w owns state tile w: columns 16w.. of the state in the
+// column products (the forward state S and the carried gradient dS', rows in
+// accumulator registers), and channels 16w.. in the row products.  Products
+// that contract over the state's columns (dO S^T, Z S^T, U dS'^T) need the
+// state and the carried gradient with the columns as the contraction index:
+// the forward sweep saves every chunk's start state in bf16, laid out as the
+// operand fragments the row products load (16 bytes per lane, coalesced); the
+// carried gradient is copied to LDS in bf16, row-major, at every chunk.
+// The forward sweep also saves U (bf16 rows) and T^T (bf16), so the backward
+// sweep neither recomputes the state chain nor solves the triangular system.
+//
+// MODE FULL runs both sweeps over one segment and writes the gradients.  MODE
+// FMAP / BMAP are the segment maps for few long sequences: the forward sweep
+// (FMAP, which also saves every chunk's T^T) or the carried-gradient chain
+// (BMAP) over one segment with the state widened to [0 | I] (d x 2d), whose
+// end value [N | M] is stored as the segment's affine map; bwd_combine_kernel
+// chains the maps.
+#include <type_traits>
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <int D>
+struct B2Cfg {
+    static constexpr int NT = D / 16;        // 16-wide tiles along a state dimension
+    static constexpr int NW = NT;            // wavefronts: one tile each
+    static constexpr int NTHR = 64 * NW;
+    static constexpr int KB = D / 32;        // 32-deep contraction blocks over D
+    static constexpr int LDR = D + 4;        // bf16 row stride of [16][D] tiles
+    static constexpr int LDK = 20;           // bf16 row stride of [.][16] tiles
+    static constexpr int LS = 20;            // fp32 row stride of 16x16 tiles
+    // workspace of one chunk of one sequence, in bf16 elements: the start state
+    // as row-product operand fragments, U rows [16][D], and T^T [16][16]
+    static constexpr int64_t WS_S = (int64_t)D * D;
+    static constexpr int64_t WS_U = 16 * (int64_t)D;
+    static constexpr int64_t WSC = WS_S + WS_U + 256;
+    static_assert(D == 64 || D == 128, "d = 64 or 128");
+};
+
+template <int D>
+struct B2Smem {
+    typedef B2Cfg<D> C;
+    alignas(16) bf16 kp[16 * C::LDR];    // K+   [token][channel]
+    alignas(16) bf16 km[16 * C::LDR];    // K-
+    alignas(16) bf16 ke[16 * C::LDR];    // Kend (backward)
+    alignas(16) bf16 kpT[D * C::LDK];    // K+^T [channel][token]
+    alignas(16) bf16 kmT[D * C::LDK];    // K-^T (backward)
+    alignas(16) bf16 keT[D * C::LDK];    // Kend^T (forward)
+    alignas(16) bf16 U[16 * C::LDR];     // U [token][value column]
+    union {
+        alignas(16) bf16 Sst[D * C::LDR];   // forward: the chunk's start state [channel][column]
+        alignas(16) bf16 Xs[D * C::LDR];    // backward: dS' of the chunk's end [channel][column]
+    } u;
+    struct {
+        alignas(16) bf16 qp[16 * C::LDR];    // Q+
+        alignas(16) bf16 qpT[D * C::LDK];    // Q+^T
+        alignas(16) bf16 dO[16 * C::LDR];    // dO [token][column]
+        alignas(16) bf16 Z[16 * C::LDR];     // Z = T^T dU [token][column]
+    } b;
+    alignas(16) bf16 tp[16 * C::LDK];    // forward: T diag(beta) [row][col]
+    alignas(16) bf16 ttT[16 * C::LDK];   // backward: T^T
+    alignas(16) float KK[16 * C::LS];    // K+ K-^T [t][s]
+    alignas(16) float AmT[16 * C::LS];   // forward: A^T, A = StrictLower(diag(beta) KK)
+    alignas(16) float Aqk[16 * C::LS];   // LowerIncl(Q+ K-^T) [t][s]
+    alignas(16) float dAqk[16 * C::LS];
+    alignas(16) float dA[16 * C::LS];
+    alignas(16) float gc[D];             // Gamma_C per channel
+    float beta[16];
+    float zv[C::NW][16];                 // rowsum(Z * V) over each wavefront's columns
+    float kz[C::NW][16];                 // rowsum(K+ * (Z S^T)) over each wavefront's channels
+};
+
+enum { B2_FULL = 0, B2_FMAP = 1, B2_BMAP = 2 };
+
+__device__ __forceinline__ bf16x4 bq(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
+__device__ __forceinline__ bf16x4 bq4(float a, float b, float c, float d) {
+    return bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+__device__ __forceinline__ bf16 b16_of(uint32_t raw) { return __builtin_bit_cast(bf16, (unsigned short)raw); }
+// per-lane offset voff plus a wave-uniform offset soff (bytes)
+__device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_st32(float x, Rsrc r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)voff, (int)soff, 0);
+}
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+__device__ __forceinline__ bf16x8 buf_ld_b8(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ bf16x4 buf_ld_b4(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_st_b8(bf16x8 x, Rsrc r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)voff, (int)soff, 0);
+}
+
+// 16x16 product P = A B^T over the D channels, A and B row-major [16][LDR] in
+// LDS: lane (g, r) gets P[4g + i][r].  k-map: block kb, slot i of group g is
+// channel 32kb + 4g + i, slot 4 + i channel 32kb + 16 + 4g + i.
+template <int D>
+__device__ __forceinline__ f32x4 small_abt(const bf16* A, const bf16* B, int r, int g) {
+    constexpr int LDR = B2Cfg<D>::LDR;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < D / 32; ++kb) {
+        const int o = r * LDR + 32 * kb + 4 * g;
+        acc = mfma_k32(cat8(ld_b4(A + o), ld_b4(A + o + 16)), cat8(ld_b4(B + o), ld_b4(B + o + 16)), acc);
+    }
+    return acc;
+}
+
+template <int D, int MODE>
+__global__ void __launch_bounds__(B2Cfg<D>::NTHR)
+bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restrict__ q,
+            const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ theta,
+            const float* __restrict__ beta, const float* __restrict__ Sinit, const bf16* __restrict__ dout,
+            const float* __restrict__ Xinit, float* __restrict__ dq, float* __restrict__ dk,
+            float* __restrict__ dv, float* __restrict__ dtheta, float* __restrict__ dbeta,
+            float* __restrict__ dS0, bf16* __restrict__ ws, float* __restrict__ maps) {
+    typedef B2Cfg<D> C;
+    constexpr bool FULL = MODE == B2_FULL;
+    constexpr int NCX = FULL ? 1 : 2;   // column tiles per wavefront (the widened state in the maps)
+    constexpr int NT = C::NT, KB = C::KB, LDR = C::LDR, LDK = C::LDK, LS = C::LS;
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr float GMIN2 = G_MIN * LOG2E;
+    __shared__ B2Smem<D> sm;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Lane-derived indices.  They are re-derived at the top of every chunk from an
+    // opaque copy of the lane id (relane), so that the address arithmetic built on
+    // them is recomputed inside the loops instead of being hoisted out of them,
+    // which would keep dozens of loop-invariant address registers alive.
+    int g = lane >> 4, li = lane & 15;
+    const int bh = blockIdx.x % BH, seg = blockIdx.x / BH, b = bh / H, h = bh % H;
+    const int n_lo = seg * seg_len, n_hi = min(nchunks, n_lo + seg_len);
+    const int64_t sb = ((int64_t)seg * BH + bh) * D * D;             // this segment's start / end matrix
+    const uint32_t tstr = (uint32_t)(H * D);                          // elements between tokens
+    const int64_t hb = (int64_t)b * T * H * D + (int64_t)h * D;      // token 0 of this head
+    const int64_t bb = (int64_t)b * T * H + h;                       // beta of token 0
+    bf16* wsh = ws + (int64_t)bh * nchunks * C::WSC;
+    int ch = 16 * w + li;   // this lane's channel (gate, row products) and value column (column products)
+    // byte offsets of element (token 4g, ch) in a [token][H][D] tensor of 4- and 2-byte
+    // elements; token 4g + i adds i rows, a wave-uniform offset
+    uint32_t vo4 = ((uint32_t)(4 * g) * tstr + (uint32_t)ch) * 4u, vo2 = vo4 >> 1;
+    const uint32_t row4 = tstr * 4u, row2 = tstr * 2u;
+    auto relane = [&]() {
+        int lv = lane;
+        asm volatile("" : "+v"(lv));
+        g = lv >> 4;
+        li = lv & 15;
+        ch = 16 * w + li;
+        vo4 = ((uint32_t)(4 * g) * tstr + (uint32_t)ch) * 4u;
+        vo2 = vo4 >> 1;
+    };
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const bf16x4 zb4 = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+
+    // ------------------------------------------------------------ raw inputs of a chunk
+    // lane (g, li) holds tokens 4g .. 4g+3 of element ch; padding tokens read zero
+    struct Raw {
+        float th[4], bt[4];
+        uint32_t k[4], q[4], x[4], o[4];   // bf16 bits: k, q, v (x), dO (o)
+    };
+    auto load_raw = [&](int m, Raw& r, auto bwd_tag) {
+        constexpr bool BWD = decltype(bwd_tag)::value;
+        const int tm = m * CHUNK;
+        const uint32_t nv = __builtin_amdgcn_readfirstlane(max(0, min(CHUNK, T - tm)));
+        const int64_t base = hb + (int64_t)tm * tstr;
+        const uint32_t span = nv * tstr;
+        const Rsrc rth = make_rsrc(theta + base, span * 4u);
+        const Rsrc rk = make_rsrc(k + base, span * 2u);
+        const Rsrc rb = make_rsrc(beta + bb + (int64_t)tm * H, nv * (uint32_t)H * 4u);
+        const uint32_t vb = (uint32_t)(4 * g) * (uint32_t)H * 4u, hrow = (uint32_t)H * 4u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r.th[i] = __builtin_bit_cast(float, buf_ld32(rth, vo4, (uint32_t)i * row4));
+            r.k[i] = buf_ld16(rk, vo2, (uint32_t)i * row2);
+            r.bt[i] = __builtin_bit_cast(float, buf_ld32(rb, vb, (uint32_t)i * hrow));
+        }
+        if constexpr (BWD) {
+            const Rsrc rq = make_rsrc(q + base, span * 2u);
+            const Rsrc ro = make_rsrc(dout + base, span * 2u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                r.q[i] = buf_ld16(rq, vo2, (uint32_t)i * row2);
+                r.o[i] = buf_ld16(ro, vo2, (uint32_t)i * row2);
+            }
+        }
+        if constexpr (!BWD || FULL) {   // v: the forward sweep's Y, the backward sweep's rowsum(Z * V)
+            const Rsrc rv = make_rsrc(v + base, span * 2u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.x[i] = buf_ld16(rv, vo2, (uint32_t)i * row2);
+        }
+    };
+
+    // ------------------------------------------------------------ the gate of a chunk
+    // Per lane: channel ch, tokens 4g+i.  The in-chunk prefix of the log-decay (base
+    // 2) runs inside the lane and then over the four lane groups.
+    struct Gate {
+        float gam[4], igam[4], gC, dsg[4], kf[4], qf[4];
+    };
+    auto gate = [&](const Raw& r, int nv, Gate& G, bool want_q) {
+        float g2[4], sgv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * r.th[i]));
+            sgv[i] = sg;
+            g2[i] = (4 * g + i < nv) ? GMIN2 * sg : 0.0f;   // padding tokens do not decay
+        }
+        float pre[4], run = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run += g2[i];
+            pre[i] = run;
+        }
+        const float t0 = __shfl(run, li), t1 = __shfl(run, 16 + li), t2 = __shfl(run, 32 + li),
+                    t3 = __shfl(run, 48 + li);
+        const float off = (g > 0 ? t0 : 0.0f) + (g > 1 ? t1 : 0.0f) + (g > 2 ? t2 : 0.0f);
+        G.gC = __builtin_amdgcn_exp2f(((t0 + t1) + t2) + t3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float gm = __builtin_amdgcn_exp2f(off + pre[i]);
+            G.gam[i] = gm;
+            G.igam[i] = __builtin_amdgcn_rcpf(gm);   // <= e^80: the bound keeps it finite
+            G.dsg[i] = G_MIN * sgv[i] * (1.0f - sgv[i]);
+            G.kf[i] = (float)b16_of(r.k[i]);
+            G.qf[i] = want_q ? (float)b16_of(r.q[i]) : 0.0f;
+        }
+    };
+
+    // ------------------------------------------------------------ state registers
+    // S (forward) / X = dS' (backward): tile rt holds rows 16rt + 4g + i of column
+    // tile cx (the widened state's column 16 (w + NT cx) + li in the maps).
+    auto init_state = [&](f32x4 (&Wt)[NT][NCX], const float* init) {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int cx = 0; cx < NCX; ++cx)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * rt + 4 * g + i;
+                    if constexpr (FULL) Wt[rt][cx][i] = init ? init[sb + (int64_t)row * D + ch] : 0.0f;
+                    else Wt[rt][cx][i] = (cx == 1 && row == ch) ? 1.0f : 0.0f;   // [0 | I]
+                }
+    };
+    auto store_map = [&](const f32x4 (&Wt)[NT][NCX]) {
+        float* mp = maps + ((int64_t)seg * BH + bh) * D * 2 * D;
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int cx = 0; cx < NCX; ++cx)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    mp[(int64_t)(16 * rt + 4 * g + i) * 2 * D + 16 * (w + NT * cx) + li] = Wt[rt][cx][i];
+    };
+
+    Raw raw = {};
+    const std::integral_constant<bool, false> FWD_T{};
+    const std::integral_constant<bool, true> BWD_T{};
+
+    // ============================================================ forward sweep
+    if constexpr (MODE != B2_BMAP) {
+        f32x4 St[NT][NCX];
+        init_state(St, Sinit);
+        load_raw(n_lo, raw, FWD_T);
+        for (int n = n_lo; n < n_hi; ++n) {
+            relane();
+            const int nv = min(CHUNK, T - n * CHUNK);
+            const Rsrc rws = make_rsrc(wsh + (int64_t)n * C::WSC, (uint32_t)C::WSC * 2u);   // this chunk's saved operands
+            Gate G;
+            gate(raw, nv, G, false);
+            float vf[4], bt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                vf[i] = (float)b16_of(raw.x[i]);
+                bt[i] = raw.bt[i];
+            }
+            if (n + 1 < n_hi) load_raw(n + 1, raw, FWD_T);   // in flight during this chunk
+            // tiles of the chunk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g + i;
+                sm.kp[t * LDR + ch] = (bf16)(G.kf[i] * G.gam[i]);
+                sm.km[t * LDR + ch] = (bf16)(G.kf[i] * G.igam[i]);
+            }
+            *reinterpret_cast<bf16x4*>(&sm.kpT[ch * LDK + 4 * g]) =
+                bq4(G.kf[0] * G.gam[0], G.kf[1] * G.gam[1], G.kf[2] * G.gam[2], G.kf[3] * G.gam[3]);
+            *reinterpret_cast<bf16x4*>(&sm.keT[ch * LDK + 4 * g]) =
+                bq4(G.kf[0] * (G.gC * G.igam[0]), G.kf[1] * (G.gC * G.igam[1]), G.kf[2] * (G.gC * G.igam[2]),
+                    G.kf[3] * (G.gC * G.igam[3]));
+            if (g == 0) sm.gc[ch] = G.gC;
+            if (w == 0 && li == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.beta[4 * g + i] = bt[i];
+            }
+            lds_barrier();
+            // A = StrictLower(diag(beta) K+ K-^T), stored transposed for the solve
+            if (w == 0) {
+                const f32x4 kk = small_abt<D>(sm.kp, sm.km, li, g);
+                f32x4 a;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = (li < 4 * g + i) ? bt[i] * kk[i] : 0.0f;
+                *reinterpret_cast<f32x4*>(&sm.AmT[li * LS + 4 * g]) = a;
+            }
+            lds_barrier();
+            // T = (I + A)^-1: lane (g, r) solves column r (the four lane groups hold
+            // copies) right-looking; group g keeps rows 4g .. 4g+3
+            if (w == 0) {
+                const int j = li;
+                float x[16];
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.0f : 0.0f;
+#pragma unroll
+                for (int s = 0; s < 15; ++s) {
+                    f32x4 col[4];
+#pragma unroll
+                    for (int c = s / 4; c < 4; ++c) col[c] = *reinterpret_cast<const f32x4*>(&sm.AmT[s * LS + 4 * c]);
+                    const float xs = x[s];
+#pragma unroll
+                    for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
+                }
+                if (g == 0) {   // the first lane group writes column j
+                    const float bj = sm.beta[j];
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) sm.tp[rr * LDK + j] = (bf16)(x[rr] * bj);   // T diag(beta)
+                    // T^T row j, for the backward sweep
+                    buf_st_b8(cat8(bq4(x[0], x[1], x[2], x[3]), bq4(x[4], x[5], x[6], x[7])), rws, (uint32_t)j * 32u,
+                              (uint32_t)(C::WS_S + C::WS_U) * 2u);
+                    buf_st_b8(cat8(bq4(x[8], x[9], x[10], x[11]), bq4(x[12], x[13], x[14], x[15])), rws,
+                              (uint32_t)j * 32u, (uint32_t)(C::WS_S + C::WS_U) * 2u + 16u);
+                }
+            }
+            lds_barrier();
+            // column products: Y = V - K+ S, U = T diag(beta) Y, S <- Diag(Gamma_C) S + Kend^T U
+#pragma unroll
+            for (int cx = 0; cx < NCX; ++cx) {
+                f32x4 p = zero4;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int o = li * LDR + 32 * kb + 4 * g;
+                    p = mfma_k32(cat8(ld_b4(&sm.kp[o]), ld_b4(&sm.kp[o + 16])),
+                                 cat8(bq(St[2 * kb][cx]), bq(St[2 * kb + 1][cx])), p);
+                }
+                f32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = (cx == 0 ? vf[i] : 0.0f) - p[i];   // the M part has V = 0
+                const f32x4 uu = mfma_k16(ld_b4(&sm.tp[li * LDK + 4 * g]), bq(y), zero4);
+                if constexpr (FULL) {
+                    // the chunk's start state and U, staged for the workspace
+#pragma unroll
+                    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sm.u.Sst[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)St[rt][cx][i];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = (bf16)uu[i];
+                }
+                const bf16x4 ub = bq(uu);
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * rt + 4 * g]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) St[rt][cx][i] *= gcv[i];
+                    St[rt][cx] = mfma_k16(ld_b4(&sm.keT[(16 * rt + li) * LDK + 4 * g]), ub, St[rt][cx]);
+                }
+            }
+            lds_barrier();
+            if constexpr (FULL) {
+                // start state as row-product fragments: fragment f = (channel tile c, block kb,
+                // lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3] and S[16c + rl][32kb + 16 + 4gl ..+3]
+#pragma unroll
+                for (int jf = 0; jf < NT * KB * 64 / C::NTHR; ++jf) {
+                    const int f = tid + jf * C::NTHR;
+                    const int c = f / (KB * 64), kb = (f / 64) % KB, l = f % 64;
+                    const int o = (16 * c + (l & 15)) * LDR + 32 * kb + 4 * (l >> 4);
+                    const bf16x8 fr = cat8(ld_b4(&sm.u.Sst[o]), ld_b4(&sm.u.Sst[o + 16]));
+                    buf_st_b8(fr, rws, (uint32_t)tid * 16u, (uint32_t)(jf * C::NTHR) * 16u);
+                }
+                if (tid < 2 * D) {   // U rows, 16 bytes per thread
+                    const int row = tid / (D / 8), c8 = (tid % (D / 8)) * 8;
+                    const bf16x8 ur = cat8(ld_b4(&sm.U[row * LDR + c8]), ld_b4(&sm.U[row * LDR + c8 + 4]));
+                    buf_st_b8(ur, rws, (uint32_t)(row * D + c8) * 2u, (uint32_t)C::WS_S * 2u);
+                }
+            }
+        }
+        if constexpr (MODE == B2_FMAP) {
+            store_map(St);
+            return;
+        }
+    }
+    if constexpr (FULL) __syncthreads();   // the saved chunks are in memory; LDS free for the backward tiles
+
+    // ============================================================ backward sweep
+    if constexpr (MODE != B2_FMAP) {
+        f32x4 X[NT][NCX];                 // dS' by value-column tiles
+        init_state(X, Xinit);
+        // chunk-saved operands, loaded a chunk ahead with the raw inputs
+        bf16x8 sfn[KB];                   // start-state fragments of this lane's channel tile
+        bf16x8 ufn = {};                  // 16 bytes of U rows
+        bf16x4 tfn = {};                  // 4 elements of T^T
+        auto load_saved = [&](int m) {
+            const Rsrc rws = make_rsrc(wsh + (int64_t)m * C::WSC, (uint32_t)C::WSC * 2u);
+            if constexpr (FULL) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    sfn[kb] = buf_ld_b8(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
+                // U rows: 16 bytes per thread of the first 2D (a resource of size zero for the rest)
+                // (wave-uniform: 2D threads are whole wavefronts)
+                const Rsrc ru = make_rsrc(wsh + (int64_t)m * C::WSC + C::WS_S, w < 2 * D / 64 ? (uint32_t)C::WS_U * 2u : 0u);
+                ufn = buf_ld_b8(ru, (uint32_t)tid * 16u, 0u);
+            }
+            // T^T: wavefront 0 only
+            const Rsrc rt = make_rsrc(wsh + (int64_t)m * C::WSC + C::WS_S + C::WS_U, w == 0 ? 512u : 0u);
+            tfn = buf_ld_b4(rt, (uint32_t)lane * 8u, 0u);
+        };
+        load_raw(n_hi - 1, raw, BWD_T);
+        load_saved(n_hi - 1);
+        for (int n = n_hi - 1; n >= n_lo; --n) {
+            relane();
+            const int tc = n * CHUNK;
+            const int nv = min(CHUNK, T - tc);
+            Gate G;
+            gate(raw, nv, G, true);
+            float of[4], vf[4], bt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                of[i] = (float)b16_of(raw.o[i]);
+                vf[i] = FULL ? (float)b16_of(raw.x[i]) : 0.0f;
+                bt[i] = raw.bt[i];
+            }
+            // tiles of the chunk (the saved U rows and T^T first: their registers are reloaded next)
+            if constexpr (FULL) {
+                if (tid < 2 * D) {
+                    const int row = tid / (D / 8), c8 = (tid % (D / 8)) * 8;
+                    *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8]) = __builtin_shufflevector(ufn, ufn, 0, 1, 2, 3);
+                    *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8 + 4]) = __builtin_shufflevector(ufn, ufn, 4, 5, 6, 7);
+                }
+            }
+            if (w == 0) *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
+            if (n > n_lo) load_raw(n - 1, raw, BWD_T);   // in flight during this chunk
+            // K+, K-, Q+ and Kend of this lane's channel and tokens (recomputed in the chain rule)
+            auto kpv = [&](int i) { return G.kf[i] * G.gam[i]; };
+            auto kmv = [&](int i) { return G.kf[i] * G.igam[i]; };
+            auto qpv = [&](int i) { return G.qf[i] * G.gam[i]; };
+            auto kev = [&](int i) { return G.kf[i] * (G.gC * G.igam[i]); };
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * g + i;
+                sm.kp[t * LDR + ch] = (bf16)kpv(i);
+                sm.km[t * LDR + ch] = (bf16)kmv(i);
+                sm.ke[t * LDR + ch] = (bf16)kev(i);
+                sm.b.qp[t * LDR + ch] = (bf16)qpv(i);
+                sm.b.dO[t * LDR + ch] = (bf16)of[i];
+            }
+            *reinterpret_cast<bf16x4*>(&sm.kpT[ch * LDK + 4 * g]) = bq4(kpv(0), kpv(1), kpv(2), kpv(3));
+            *reinterpret_cast<bf16x4*>(&sm.kmT[ch * LDK + 4 * g]) = bq4(kmv(0), kmv(1), kmv(2), kmv(3));
+            *reinterpret_cast<bf16x4*>(&sm.b.qpT[ch * LDK + 4 * g]) = bq4(qpv(0), qpv(1), qpv(2), qpv(3));
+            if (g == 0) sm.gc[ch] = G.gC;
+            if constexpr (FULL) {   // dS' of the chunk's end, row-major, for the products over its columns
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sm.u.Xs[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)X[rt][0][i];
+            }
+            lds_barrier();
+
+            // ---- KK = K+ K-^T (wave 0), A_qk = LowerIncl(Q+ K-^T) (wave 1)
+            if (w == 0 && FULL) {
+                const f32x4 kk = small_abt<D>(sm.kp, sm.km, li, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.KK[(4 * g + i) * LS + li] = kk[i];
+            }
+            if (w == (FULL ? 1 : 0)) {
+                const f32x4 aq = small_abt<D>(sm.b.qp, sm.km, li, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.Aqk[(4 * g + i) * LS + li] = (li <= 4 * g + i) ? aq[i] : 0.0f;
+            }
+            lds_barrier();
+
+            // ---- column products: dU, Z, dY = dV, and dS' <- Diag(Gamma_C) dS' + Q+^T dO - K+^T dY
+            float zvp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cx = 0; cx < NCX; ++cx) {
+                f32x4 du = zero4;
+                if (cx == 0) {   // A_qk^T dO (the M part of the widened gradient has dO = 0)
+                    const bf16x4 at = bq4(sm.Aqk[(4 * g + 0) * LS + li], sm.Aqk[(4 * g + 1) * LS + li],
+                                          sm.Aqk[(4 * g + 2) * LS + li], sm.Aqk[(4 * g + 3) * LS + li]);
+                    du = mfma_k16(at, bq4(of[0], of[1], of[2], of[3]), du);
+                }
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) {
+                    const int o = li * LDR + 32 * kb + 4 * g;
+                    du = mfma_k32(cat8(ld_b4(&sm.ke[o]), ld_b4(&sm.ke[o + 16])),
+                                  cat8(bq(X[2 * kb][cx]), bq(X[2 * kb + 1][cx])), du);
+                }
+                const f32x4 z = mfma_k16(ld_b4(&sm.ttT[li * LDK + 4 * g]), bq(du), zero4);
+                f32x4 ndy;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ndy[i] = -bt[i] * z[i];
+                if constexpr (FULL) {
+                    const Rsrc rdv = make_rsrc(dv + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        buf_st32(-ndy[i], rdv, vo4, (uint32_t)i * row4);
+                        sm.b.Z[(4 * g + i) * LDR + ch] = (bf16)z[i];
+                        zvp[i] = z[i] * vf[i];
+                    }
+                }
+                const bf16x4 ob = cx == 0 ? bq4(of[0], of[1], of[2], of[3]) : zb4;
+                const bf16x8 bop = cat8(ob, bq(ndy));
+#pragma unroll
+                for (int rt = 0; rt < NT; ++rt) {
+                    const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * rt + 4 * g]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) X[rt][cx][i] *= gcv[i];
+                    const int o = (16 * rt + li) * LDK + 4 * g;
+                    X[rt][cx] = mfma_k32(cat8(ld_b4(&sm.b.qpT[o]), ld_b4(&sm.kpT[o])), bop, X[rt][cx]);
+                }
+            }
+            if constexpr (!FULL) {
+                if (n > n_lo) load_saved(n - 1);
+                lds_barrier();   // before the next chunk overwrites the tiles
+                continue;
+            }
+            // rowsum(Z * V) over this wavefront's 16 columns
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s = zvp[i];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+                if (li == 0) sm.zv[w][4 * g + i] = s;
+            }
+            lds_barrier();
+
+            // ---- dA_qk = LowerIncl(dO U^T) (wave 0), dA = StrictLower(-Z U^T) (wave 1);
+            // everyone: the row products over the state's columns, dO S^T, U dS'^T and
+            // Z S^T, and dGamma_C = rowsum(dS' * S)
+            if (w == 0) {
+                const f32x4 x = small_abt<D>(sm.b.dO, sm.U, li, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.dAqk[(4 * g + i) * LS + li] = (li <= 4 * g + i) ? x[i] : 0.0f;
+            }
+            if (w == 1) {
+                const f32x4 x = small_abt<D>(sm.b.Z, sm.U, li, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.dA[(4 * g + i) * LS + li] = (li < 4 * g + i) ? -x[i] : 0.0f;
+            }
+            f32x4 zs = zero4, aqv = zero4, aev = zero4;
+            float dgc = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const int o = li * LDR + 32 * kb + 4 * g;
+                zs = mfma_k32(cat8(ld_b4(&sm.b.Z[o]), ld_b4(&sm.b.Z[o + 16])), sfn[kb], zs);
+                aqv = mfma_k32(cat8(ld_b4(&sm.b.dO[o]), ld_b4(&sm.b.dO[o + 16])), sfn[kb], aqv);
+                const int ox = ch * LDR + 32 * kb + 4 * g;   // dS' row ch, the k-slots of this lane
+                const bf16x8 xb = cat8(ld_b4(&sm.u.Xs[ox]), ld_b4(&sm.u.Xs[ox + 16]));
+                aev = mfma_k32(cat8(ld_b4(&sm.U[o]), ld_b4(&sm.U[o + 16])), xb, aev);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) dgc += (float)xb[i] * (float)sfn[kb][i];
+            }
+            dgc += __shfl_xor(dgc, 16);
+            dgc += __shfl_xor(dgc, 32);
+            // this chunk's saved operands are used up: the previous chunk's load while the
+            // rest of this one runs
+            if (n > n_lo) load_saved(n - 1);
+            lds_barrier();
+
+            // ---- the rest of the row products and the chain rule; lane (g, li): channel ch, tokens 4g+i
+            const bf16x4 kmb = ld_b4(&sm.kmT[ch * LDK + 4 * g]);
+            f32x4 aqp;
+            {
+                const f32x4 daq = *reinterpret_cast<const f32x4*>(&sm.dAqk[li * LS + 4 * g]);
+                aqp = mfma_k16(bq(daq), kmb, zero4);                     // dA_qk K-
+            }
+            f32x4 dak;
+            {
+                const f32x4 da = *reinterpret_cast<const f32x4*>(&sm.dA[li * LS + 4 * g]);
+                dak = mfma_k16(bq(da), kmb, zero4);                      // dA K-
+            }
+            const bf16x8 qk = cat8(ld_b4(&sm.b.qpT[ch * LDK + 4 * g]), ld_b4(&sm.kpT[ch * LDK + 4 * g]));
+            f32x4 amv;
+            {
+                const bf16x4 a0 = bq4(sm.dAqk[(4 * g + 0) * LS + li], sm.dAqk[(4 * g + 1) * LS + li],
+                                      sm.dAqk[(4 * g + 2) * LS + li], sm.dAqk[(4 * g + 3) * LS + li]);
+                const bf16x4 a1 = bq4(bt[0] * sm.dA[(4 * g + 0) * LS + li], bt[1] * sm.dA[(4 * g + 1) * LS + li],
+                                      bt[2] * sm.dA[(4 * g + 2) * LS + li], bt[3] * sm.dA[(4 * g + 3) * LS + li]);
+                amv = mfma_k32(cat8(a0, a1), qk, zero4);                 // dA_qk^T Q+ + (diag(beta) dA)^T K+
+            }
+            const Rsrc rq = make_rsrc(dq + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
+            const Rsrc rk = make_rsrc(dk + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
+            const Rsrc rt_ = make_rsrc(dtheta + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
+            // The intra-chunk (pair) parts of dK+, dQ+ and dK- each reach the log-decay of
+            // two tokens with opposite signs, which cancel in its reverse prefix sum; they
+            // cancel to fp32 accuracy only when both sides use the bf16 values the products
+            // used, so those parts are multiplied by the rounded K+, K- and Q+.
+            auto rb = [](float x) { return (float)(bf16)x; };
+            float dG[4], kes = 0.0f, kzp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t off = (uint32_t)i * row4;
+                const float aks = -bt[i] * zs[i], akp = bt[i] * dak[i];   // dK+: state part, pair part
+                const float gm = G.gam[i], ig = G.igam[i];
+                buf_st32((aks + akp) * gm + amv[i] * ig + aev[i] * (G.gC * ig), rk, vo4, off);
+                buf_st32((aqv[i] + aqp[i]) * gm, rq, vo4, off);
+                const float ked = aev[i] * kev(i);
+                kes += ked;
+                const float kpb = rb(kpv(i));
+                dG[i] = aks * kpv(i) + akp * kpb - amv[i] * rb(kmv(i)) + aqv[i] * qpv(i) + aqp[i] * rb(qpv(i)) - ked;
+                kzp[i] = zs[i] * kpb;   // rowsum(K+ * (Z S^T)) with the K+ the forward's Y used
+            }
+            kes += __shfl_xor(kes, 16);
+            kes += __shfl_xor(kes, 32);
+            // the chunk's last token also carries the end decay: d(G_C) = sum_t dKend Kend + dGamma_C Gamma_C
+            if (g == 3) dG[3] += kes + dgc * G.gC;
+            float suf = 0.0f;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                suf += dG[i];
+                dG[i] = suf;
+            }
+            const float s1 = __shfl(suf, 16 + li), s2 = __shfl(suf, 32 + li), s3 = __shfl(suf, 48 + li);
+            const float later = (g < 1 ? s1 : 0.0f) + (g < 2 ? s2 : 0.0f) + (g < 3 ? s3 : 0.0f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                buf_st32((dG[i] + later) * G.dsg[i], rt_, vo4, (uint32_t)i * row4);
+            // rowsum(K+ * (Z S^T)) over this wavefront's 16 channels
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s = kzp[i];
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+                if (li == 0) sm.kz[w][4 * g + i] = s;
+            }
+            lds_barrier();
+            if (tid < CHUNK) {   // dbeta = rowsum(dA * KK) + rowsum(Z * V) - rowsum(K+ * (Z S^T))
+                const int t = tid;
+                float a = 0.0f;
+#pragma unroll
+                for (int s = 0; s < CHUNK; ++s) a = fmaf(sm.dA[t * LS + s], sm.KK[t * LS + s], a);
+#pragma unroll
+                for (int x = 0; x < C::NW; ++x) a += sm.zv[x][t] - sm.kz[x][t];
+                if (t < nv) dbeta[bb + (int64_t)(tc + t) * H] = a;
+            }
+        }
+        if constexpr (!FULL) {
+            store_map(X);
+        } else if (dS0 && seg == 0) {
+#pragma unroll
+            for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dS0[((int64_t)bh * D + 16 * rt + 4 * g + i) * D + ch] = X[rt][0][i];
+        }
+    }
+}
+
+size_t chunk_bwd2_workspace_bytes(int B, int T, int H, int d, int nseg) {
+    const size_t nchunks = ((size_t)T + CHUNK - 1) / CHUNK;
+    const size_t BH = (size_t)B * H;
+    const size_t DD = (size_t)d * d;
+    size_t n = nchunks * BH * (DD + 16 * (size_t)d + 256) * sizeof(bf16);
+    n = (n + 255) & ~(size_t)255;
+    if (nseg > 1) n += (size_t)nseg * BH * (4 * DD + 2 * DD) * sizeof(float);
+    return n;
+}
+
+hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, const void* q, const void* k,
+                             const void* v, const float* theta, const float* beta, const float* S0,
+                             const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
+                             float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int BH = B * H;
+    const size_t DD = (size_t)d * d;
+    bf16* wsb = (bf16*)workspace;
+    size_t off = (size_t)nchunks * BH * (DD + 16 * (size_t)d + 256) * sizeof(bf16);
+    off = (off + 255) & ~(size_t)255;
+    float* mapF = (float*)((char*)workspace + off);
+    float* mapB = mapF + (size_t)nseg * BH * 2 * DD;
+    float* Sst = mapB + (size_t)nseg * BH * 2 * DD;
+    float* Xen = Sst + (size_t)nseg * BH * DD;
+#define KDA_B2(D, MODE, GRID, SI, XI, MP)                                                                   \
+    hipLaunchKernelGGL((bwd2_kernel<D, MODE>), dim3((unsigned)(GRID)), dim3(B2Cfg<D>::NTHR), 0, stream, T, H, \
+                       BH, nchunks, seg_len, (const bf16*)q, (const bf16*)k, (const bf16*)v, theta, beta, SI,  \
+                       (const bf16*)dout, XI, dq, dk, dv, dtheta, dbeta, dS0, wsb, MP)
+#define KDA_B2_ALL(D)                                                                                     \
+    if (nseg == 1) {                                                                                      \
+        KDA_B2(D, B2_FULL, BH, S0, dS_T, nullptr);                                                        \
+    } else {                                                                                              \
+        KDA_B2(D, B2_FMAP, nseg * BH, nullptr, nullptr, mapF);                                            \
+        KDA_B2(D, B2_BMAP, nseg * BH, nullptr, nullptr, mapB);                                            \
+        hipError_t e = launch_bwd_combine(D, BH, nseg, 0, mapF, S0, Sst, stream);                         \
+        if (e == hipSuccess) e = launch_bwd_combine(D, BH, nseg, 1, mapB, dS_T, Xen, stream);             \
+        if (e != hipSuccess) return e;                                                                    \
+        KDA_B2(D, B2_FULL, nseg * BH, (const float*)Sst, (const float*)Xen, nullptr);                      \
+    }                                                                                                     \
+    return hipGetLastError()
+    switch (d) {
+        case 64: KDA_B2_ALL(64);
+        case 128: KDA_B2_ALL(128);
+    }
+#undef KDA_B2_ALL
+#undef KDA_B2
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

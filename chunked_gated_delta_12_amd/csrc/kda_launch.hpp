@@ -62,4 +62,19 @@ hipError_t launch_chunk_bwd(bool f32, int B, int T, int H, int d, const void* q,
                             const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
                             float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream);
 
+// The same backward pass for bf16 inputs at d = 64 and 128 on the bf16 matrix
+// cores (kda_bwd2.hip), with nseg segments of seg_len chunks per sequence; its
+// workspace (every chunk's start state, U and T^T in bf16, and the segment maps
+// and boundary values) takes chunk_bwd2_workspace_bytes.
+size_t chunk_bwd2_workspace_bytes(int B, int T, int H, int d, int nseg);
+hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, const void* q, const void* k,
+                             const void* v, const float* theta, const float* beta, const float* S0,
+                             const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
+                             float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream);
+// Chains the backward segment maps of every head (kda_bwd.hip): the state at
+// every segment's start (reverse = 0) or the carried gradient at every
+// segment's end (reverse = 1).
+hipError_t launch_bwd_combine(int d, int BH, int nseg, int reverse, const float* maps, const float* init,
+                              float* out, hipStream_t stream);
+
 }  // namespace kda
