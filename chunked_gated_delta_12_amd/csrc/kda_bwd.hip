@@ -954,21 +954,6 @@ static int bwd_segments(int BH, int nchunks, int d, int* seg_len) {
     return (nchunks + L - 1) / L;
 }
 
-hipError_t launch_bwd_combine(int d, int BH, int nseg, int reverse, const float* maps, const float* init,
-                              float* out, hipStream_t stream) {
-    switch (d) {
-        case 64:
-            hipLaunchKernelGGL((bwd_combine_kernel<64>), dim3((unsigned)(BH * 4)), dim3(256), 0, stream, BH, nseg,
-                               reverse, maps, init, out);
-            return hipGetLastError();
-        case 128:
-            hipLaunchKernelGGL((bwd_combine_kernel<128>), dim3((unsigned)(BH * 8)), dim3(256), 0, stream, BH, nseg,
-                               reverse, maps, init, out);
-            return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
-}
-
 // The size serves both input types: the fp32 kernels' layout (fp32 chunk states,
 // U and Y) and, for d = 64 and 128, the bf16 kernel's (kda_bwd2.hip).
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int d) {

@@ -34,8 +34,8 @@
 // FMAP / BMAP are the segment maps for few long sequences: the forward sweep
 // (FMAP, which also saves every chunk's T^T) or the carried-gradient chain
 // (BMAP) over one segment with the state widened to [0 | I] (d x 2d), whose
-// end value [N | M] is stored as the segment's affine map; bwd_combine_kernel
-// chains the maps.
+// end value [N | M] is stored as the segment's affine map; the forward pass's
+// combine kernel chains the maps (the gradient's in reverse segment order).
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -119,6 +119,24 @@ __device__ __forceinline__ void buf_st_b8(bf16x8 x, Rsrc r, uint32_t voff, uint3
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)voff, (int)soff, 0);
 }
 
+// Sum over the 16 lanes of a row (lane & 15), in every lane of the row, by DPP
+// lane swaps (xor 1, xor 2, half-row mirror, row mirror) on the vector unit.
+__device__ __forceinline__ float rowsum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+// x . y over 8 bf16 pairs, accumulated in fp32 (packed bf16 dot products)
+__device__ __forceinline__ float dot8(bf16x8 x, bf16x8 y, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bf16v2{x[2 * i], x[2 * i + 1]}, bf16v2{y[2 * i], y[2 * i + 1]}, acc, false);
+    return acc;
+}
+
 // 16x16 product P = A B^T over the D channels, A and B row-major [16][LDR] in
 // LDS: lane (g, r) gets P[4g + i][r].  k-map: block kb, slot i of group g is
 // channel 32kb + 4g + i, slot 4 + i channel 32kb + 16 + 4g + i.
@@ -187,10 +205,14 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         float th[4], bt[4];
         uint32_t k[4], q[4], x[4], o[4];   // bf16 bits: k, q, v (x), dO (o)
     };
+    // Unconditional: a chunk outside the segment (the one after the last, or before the
+    // first) reads zeros through resources of size zero, so no load sits under a branch
+    // (which would make the compiler wait for every outstanding access at the join).
     auto load_raw = [&](int m, Raw& r, auto bwd_tag) {
         constexpr bool BWD = decltype(bwd_tag)::value;
         const int tm = m * CHUNK;
-        const uint32_t nv = __builtin_amdgcn_readfirstlane(max(0, min(CHUNK, T - tm)));
+        const bool inside = m >= n_lo && m < n_hi;
+        const uint32_t nv = __builtin_amdgcn_readfirstlane(inside ? max(0, min(CHUNK, T - tm)) : 0);
         const int64_t base = hb + (int64_t)tm * tstr;
         const uint32_t span = nv * tstr;
         const Rsrc rth = make_rsrc(theta + base, span * 4u);
@@ -257,7 +279,9 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     // ------------------------------------------------------------ state registers
     // S (forward) / X = dS' (backward): tile rt holds rows 16rt + 4g + i of column
     // tile cx (the widened state's column 16 (w + NT cx) + li in the maps).
-    auto init_state = [&](f32x4 (&Wt)[NT][NCX], const float* init) {
+    auto init_state = [&](f32x4 (&Wt)[NT][NCX], const float* init, int64_t off) {
+        // the start value (zero when init is NULL: a resource of size zero)
+        const Rsrc ri = make_rsrc(init ? init + off : init, init ? (uint32_t)(D * D * 4) : 0u);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -265,19 +289,29 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 16 * rt + 4 * g + i;
-                    if constexpr (FULL) Wt[rt][cx][i] = init ? init[sb + (int64_t)row * D + ch] : 0.0f;
-                    else Wt[rt][cx][i] = (cx == 1 && row == ch) ? 1.0f : 0.0f;   // [0 | I]
+                    if constexpr (FULL)
+                        Wt[rt][cx][i] = __builtin_bit_cast(float, buf_ld32(ri, (uint32_t)(row * D + ch) * 4u, 0u));
+                    else
+                        Wt[rt][cx][i] = (cx == 1 && row == ch) ? 1.0f : 0.0f;   // [0 | I]
                 }
     };
+    // The end value [N | M] of a map sweep: N fp32 and M bf16, each [map][batch*head][d][d]
+    // (M after the nseg N blocks).  The state maps (FMAP) are stored by segment, the
+    // gradient maps (BMAP) in reverse segment order, so that both chains run forward
+    // through the same combine kernel.
+    const int nseg = (nchunks + seg_len - 1) / seg_len;
     auto store_map = [&](const f32x4 (&Wt)[NT][NCX]) {
-        float* mp = maps + ((int64_t)seg * BH + bh) * D * 2 * D;
+        const int slot = MODE == B2_BMAP ? nseg - 1 - seg : seg;
+        float* mn = maps + ((int64_t)slot * BH + bh) * D * D;
+        bf16* mm = reinterpret_cast<bf16*>(maps + (int64_t)nseg * BH * D * D) + ((int64_t)slot * BH + bh) * D * D;
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-            for (int cx = 0; cx < NCX; ++cx)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    mp[(int64_t)(16 * rt + 4 * g + i) * 2 * D + 16 * (w + NT * cx) + li] = Wt[rt][cx][i];
+            for (int i = 0; i < 4; ++i) {
+                const int64_t o = (int64_t)(16 * rt + 4 * g + i) * D + ch;
+                mn[o] = Wt[rt][0][i];
+                if constexpr (NCX == 2) mm[o] = (bf16)Wt[rt][NCX - 1][i];
+            }
     };
 
     Raw raw = {};
@@ -287,8 +321,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     // ============================================================ forward sweep
     if constexpr (MODE != B2_BMAP) {
         f32x4 St[NT][NCX];
-        init_state(St, Sinit);
+        init_state(St, Sinit, sb);
         load_raw(n_lo, raw, FWD_T);
+        // retire the first loads before the loop, so the wait counts inside it stay exact
+        __builtin_amdgcn_s_waitcnt(0);
         for (int n = n_lo; n < n_hi; ++n) {
             relane();
             const int nv = min(CHUNK, T - n * CHUNK);
@@ -301,7 +337,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 vf[i] = (float)b16_of(raw.x[i]);
                 bt[i] = raw.bt[i];
             }
-            if (n + 1 < n_hi) load_raw(n + 1, raw, FWD_T);   // in flight during this chunk
+            load_raw(n + 1, raw, FWD_T);   // in flight during this chunk
             // tiles of the chunk
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -401,8 +437,8 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                     const bf16x8 fr = cat8(ld_b4(&sm.u.Sst[o]), ld_b4(&sm.u.Sst[o + 16]));
                     buf_st_b8(fr, rws, (uint32_t)tid * 16u, (uint32_t)(jf * C::NTHR) * 16u);
                 }
-                if (tid < 2 * D) {   // U rows, 16 bytes per thread
-                    const int row = tid / (D / 8), c8 = (tid % (D / 8)) * 8;
+                {   // U rows, 16 bytes per thread; the 2D pieces are stored twice (no branch)
+                    const int p = tid % (2 * D), row = p / (D / 8), c8 = (p % (D / 8)) * 8;
                     const bf16x8 ur = cat8(ld_b4(&sm.U[row * LDR + c8]), ld_b4(&sm.U[row * LDR + c8 + 4]));
                     buf_st_b8(ur, rws, (uint32_t)(row * D + c8) * 2u, (uint32_t)C::WS_S * 2u);
                 }
@@ -418,28 +454,34 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     // ============================================================ backward sweep
     if constexpr (MODE != B2_FMAP) {
         f32x4 X[NT][NCX];                 // dS' by value-column tiles
-        init_state(X, Xinit);
+        // the carried gradient at the segment's end: the combine wrote the segments'
+        // end values in reverse order (one segment: dS_T itself)
+        init_state(X, Xinit, ((int64_t)(nseg - 1 - seg) * BH + bh) * D * D);
         // chunk-saved operands, loaded a chunk ahead with the raw inputs
         bf16x8 sfn[KB];                   // start-state fragments of this lane's channel tile
         bf16x8 ufn = {};                  // 16 bytes of U rows
         bf16x4 tfn = {};                  // 4 elements of T^T
+        // chunk m's saved operands (zeros through resources of size zero outside the segment)
         auto load_saved = [&](int m) {
-            const Rsrc rws = make_rsrc(wsh + (int64_t)m * C::WSC, (uint32_t)C::WSC * 2u);
+            const bool inside = m >= n_lo && m < n_hi;
+            const int mm = inside ? m : n_lo;   // an address inside the workspace either way
+            const bf16* wsm = wsh + (int64_t)mm * C::WSC;
             if constexpr (FULL) {
+                const Rsrc rws = make_rsrc(wsm, inside ? (uint32_t)C::WS_S * 2u : 0u);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
                     sfn[kb] = buf_ld_b8(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
-                // U rows: 16 bytes per thread of the first 2D (a resource of size zero for the rest)
-                // (wave-uniform: 2D threads are whole wavefronts)
-                const Rsrc ru = make_rsrc(wsh + (int64_t)m * C::WSC + C::WS_S, w < 2 * D / 64 ? (uint32_t)C::WS_U * 2u : 0u);
-                ufn = buf_ld_b8(ru, (uint32_t)tid * 16u, 0u);
+                // U rows: 16 bytes per thread, the 2D pieces loaded (and later written to LDS) twice
+                const Rsrc ru = make_rsrc(wsm + C::WS_S, inside ? (uint32_t)C::WS_U * 2u : 0u);
+                ufn = buf_ld_b8(ru, (uint32_t)(tid % (2 * D)) * 16u, 0u);
             }
-            // T^T: wavefront 0 only
-            const Rsrc rt = make_rsrc(wsh + (int64_t)m * C::WSC + C::WS_S + C::WS_U, w == 0 ? 512u : 0u);
+            // T^T: every wavefront loads it and writes the same values
+            const Rsrc rt = make_rsrc(wsm + C::WS_S + C::WS_U, inside ? 512u : 0u);
             tfn = buf_ld_b4(rt, (uint32_t)lane * 8u, 0u);
         };
         load_raw(n_hi - 1, raw, BWD_T);
         load_saved(n_hi - 1);
+        __builtin_amdgcn_s_waitcnt(0);   // retire the first loads before the loop
         for (int n = n_hi - 1; n >= n_lo; --n) {
             relane();
             const int tc = n * CHUNK;
@@ -454,15 +496,15 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 bt[i] = raw.bt[i];
             }
             // tiles of the chunk (the saved U rows and T^T first: their registers are reloaded next)
+            // (no branch around registers of pending loads: every thread writes, the
+            // duplicates with equal values)
             if constexpr (FULL) {
-                if (tid < 2 * D) {
-                    const int row = tid / (D / 8), c8 = (tid % (D / 8)) * 8;
-                    *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8]) = __builtin_shufflevector(ufn, ufn, 0, 1, 2, 3);
-                    *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8 + 4]) = __builtin_shufflevector(ufn, ufn, 4, 5, 6, 7);
-                }
+                const int p = tid % (2 * D), row = p / (D / 8), c8 = (p % (D / 8)) * 8;
+                *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8]) = __builtin_shufflevector(ufn, ufn, 0, 1, 2, 3);
+                *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8 + 4]) = __builtin_shufflevector(ufn, ufn, 4, 5, 6, 7);
             }
-            if (w == 0) *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
-            if (n > n_lo) load_raw(n - 1, raw, BWD_T);   // in flight during this chunk
+            *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
+            load_raw(n - 1, raw, BWD_T);   // in flight during this chunk
             // K+, K-, Q+ and Kend of this lane's channel and tokens (recomputed in the chain rule)
             auto kpv = [&](int i) { return G.kf[i] * G.gam[i]; };
             auto kmv = [&](int i) { return G.kf[i] * G.igam[i]; };
@@ -543,16 +585,14 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 }
             }
             if constexpr (!FULL) {
-                if (n > n_lo) load_saved(n - 1);
+                load_saved(n - 1);
                 lds_barrier();   // before the next chunk overwrites the tiles
                 continue;
             }
             // rowsum(Z * V) over this wavefront's 16 columns
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s = zvp[i];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+                const float s = rowsum16(zvp[i]);
                 if (li == 0) sm.zv[w][4 * g + i] = s;
             }
             lds_barrier();
@@ -580,14 +620,13 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 const int ox = ch * LDR + 32 * kb + 4 * g;   // dS' row ch, the k-slots of this lane
                 const bf16x8 xb = cat8(ld_b4(&sm.u.Xs[ox]), ld_b4(&sm.u.Xs[ox + 16]));
                 aev = mfma_k32(cat8(ld_b4(&sm.U[o]), ld_b4(&sm.U[o + 16])), xb, aev);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) dgc += (float)xb[i] * (float)sfn[kb][i];
+                dgc = dot8(xb, sfn[kb], dgc);
             }
             dgc += __shfl_xor(dgc, 16);
             dgc += __shfl_xor(dgc, 32);
             // this chunk's saved operands are used up: the previous chunk's load while the
             // rest of this one runs
-            if (n > n_lo) load_saved(n - 1);
+            load_saved(n - 1);
             lds_barrier();
 
             // ---- the rest of the row products and the chain rule; lane (g, li): channel ch, tokens 4g+i
@@ -651,20 +690,20 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             // rowsum(K+ * (Z S^T)) over this wavefront's 16 channels
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s = kzp[i];
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+                const float s = rowsum16(kzp[i]);
                 if (li == 0) sm.kz[w][4 * g + i] = s;
             }
             lds_barrier();
-            if (tid < CHUNK) {   // dbeta = rowsum(dA * KK) + rowsum(Z * V) - rowsum(K+ * (Z S^T))
-                const int t = tid;
+            {   // dbeta = rowsum(dA * KK) + rowsum(Z * V) - rowsum(K+ * (Z S^T)): every thread
+                // forms the value of token tid % 16 and stores it (equal duplicates, no branch)
+                const int t = tid & 15;
                 float a = 0.0f;
 #pragma unroll
                 for (int s = 0; s < CHUNK; ++s) a = fmaf(sm.dA[t * LS + s], sm.KK[t * LS + s], a);
 #pragma unroll
                 for (int x = 0; x < C::NW; ++x) a += sm.zv[x][t] - sm.kz[x][t];
-                if (t < nv) dbeta[bb + (int64_t)(tc + t) * H] = a;
+                const Rsrc rb = make_rsrc(dbeta + bb + (int64_t)tc * H, (uint32_t)nv * (uint32_t)H * 4u);
+                buf_st32(a, rb, (uint32_t)t * (uint32_t)H * 4u, 0u);
             }
         }
         if constexpr (!FULL) {
@@ -698,10 +737,11 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
     bf16* wsb = (bf16*)workspace;
     size_t off = (size_t)nchunks * BH * (DD + 16 * (size_t)d + 256) * sizeof(bf16);
     off = (off + 255) & ~(size_t)255;
+    // per direction: N (fp32) then M (bf16, in a region sized for fp32), [map][BH][d][d]
     float* mapF = (float*)((char*)workspace + off);
     float* mapB = mapF + (size_t)nseg * BH * 2 * DD;
-    float* Sst = mapB + (size_t)nseg * BH * 2 * DD;
-    float* Xen = Sst + (size_t)nseg * BH * DD;
+    float* Sst = mapB + (size_t)nseg * BH * 2 * DD;    // state at every segment's start
+    float* Xen = Sst + (size_t)nseg * BH * DD;         // carried gradient at the segments' ends, reversed
 #define KDA_B2(D, MODE, GRID, SI, XI, MP)                                                                   \
     hipLaunchKernelGGL((bwd2_kernel<D, MODE>), dim3((unsigned)(GRID)), dim3(B2Cfg<D>::NTHR), 0, stream, T, H, \
                        BH, nchunks, seg_len, (const bf16*)q, (const bf16*)k, (const bf16*)v, theta, beta, SI,  \
@@ -712,8 +752,9 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
     } else {                                                                                              \
         KDA_B2(D, B2_FMAP, nseg * BH, nullptr, nullptr, mapF);                                            \
         KDA_B2(D, B2_BMAP, nseg * BH, nullptr, nullptr, mapB);                                            \
-        hipError_t e = launch_bwd_combine(D, BH, nseg, 0, mapF, S0, Sst, stream);                         \
-        if (e == hipSuccess) e = launch_bwd_combine(D, BH, nseg, 1, mapB, dS_T, Xen, stream);             \
+        hipError_t e = launch_state_combine(D, BH, nseg, S0, mapF, mapF + (size_t)nseg * BH * DD, Sst, stream); \
+        if (e == hipSuccess)                                                                              \
+            e = launch_state_combine(D, BH, nseg, dS_T, mapB, mapB + (size_t)nseg * BH * DD, Xen, stream);  \
         if (e != hipSuccess) return e;                                                                    \
         KDA_B2(D, B2_FULL, nseg * BH, (const float*)Sst, (const float*)Xen, nullptr);                      \
     }                                                                                                     \

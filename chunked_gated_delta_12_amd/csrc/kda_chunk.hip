@@ -848,6 +848,21 @@ static hipError_t launch_chunk_t(int B, int T, int H, const SegPlan& p, const vo
     return hipGetLastError();
 }
 
+hipError_t launch_state_combine(int d, int BH, int nseg, const float* init, const float* ws_n, const void* ws_m,
+                                float* out, hipStream_t stream) {
+    const int heads_per_xcd = (BH + COMBINE_XCDS - 1) / COMBINE_XCDS;
+#define KDA_COMB(D)                                                                                          \
+    hipLaunchKernelGGL((combine_kernel<bf16, D>), dim3((unsigned)(COMBINE_XCDS * heads_per_xcd * (D / 16))),   \
+                       dim3(64 * (D / 16)), 0, stream, BH, nseg, init, ws_n, (const bf16*)ws_m, out);         \
+    return hipGetLastError()
+    switch (d) {
+        case 64: KDA_COMB(64);
+        case 128: KDA_COMB(128);
+    }
+#undef KDA_COMB
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_chunk_fwd(bool f32, int B, int T, int H, int d, const SegPlan& plan,
                             const void* q, const void* k, const void* v, const float* theta,
                             const float* beta, const float* S0, const void* z, void* o, float* S_T,

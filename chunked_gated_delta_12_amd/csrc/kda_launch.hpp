@@ -71,10 +71,11 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
                              const void* v, const float* theta, const float* beta, const float* S0,
                              const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
                              float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream);
-// Chains the backward segment maps of every head (kda_bwd.hip): the state at
-// every segment's start (reverse = 0) or the carried gradient at every
-// segment's end (reverse = 1).
-hipError_t launch_bwd_combine(int d, int BH, int nseg, int reverse, const float* maps, const float* init,
-                              float* out, hipStream_t stream);
+// Chains affine segment maps X_{s+1} = M_s X_s + N_s of every head on the bf16
+// matrix cores (the forward's combine kernel, kda_chunk.hip): N fp32 and M bf16,
+// both [segment][batch*head][d][d]; writes X_s for every segment to out (X_0 =
+// init, or zero when NULL).  d = 64 or 128.
+hipError_t launch_state_combine(int d, int BH, int nseg, const float* init, const float* ws_n, const void* ws_m,
+                                float* out, hipStream_t stream);
 
 }  // namespace kda
