@@ -24,11 +24,18 @@
 // accumulator registers), and channels 16w.. in the row products.  Products
 // that contract over the state's columns (dO S^T, Z S^T, U dS'^T) need the
 // state and the carried gradient with the columns as the contraction index:
-// the forward sweep saves every chunk's start state in bf16, laid out as the
-// operand fragments the row products load (16 bytes per lane, coalesced); the
+// the forward sweep saves the start state in bf16, laid out as the operand
+// fragments the row products load (16 bytes per lane, coalesced), at every
+// other chunk of the segment (the even ones, counted from its first chunk); the
 // carried gradient is copied to LDS in bf16, row-major, at every chunk.
-// The forward sweep also saves U (bf16 rows) and T^T (bf16), so the backward
-// sweep neither recomputes the state chain nor solves the triangular system.
+// The forward sweep also saves U (bf16 rows) and T^T (bf16) of every chunk, so
+// the backward sweep neither runs the state chain nor solves the triangular
+// system, and, for an even chunk followed by an odd one, Kend (bf16) and Gamma_C
+// (fp32) in the odd chunk's unused state area.  The backward sweep forms an odd
+// chunk's start state from the even one before it by one step of the chain,
+//     S_m = Diag(Gamma_C) S_{m-1} + Kend^T U_{m-1}   (chunk m-1's operands),
+// from the very bf16 operands the forward chain used, and keeps S_{m-1} in LDS
+// for the next chunk: half the state traffic, the largest item of the sweep's.
 //
 // MODE FULL runs both sweeps over one segment and writes the gradients.  MODE
 // FMAP / BMAP are the segment maps for few long sequences: the forward sweep
@@ -57,6 +64,12 @@ struct B2Cfg {
     static constexpr int64_t WS_S = (int64_t)D * D;
     static constexpr int64_t WS_U = 16 * (int64_t)D;
     static constexpr int64_t WSC = WS_S + WS_U + 256;
+    // in the state area of an odd chunk: the previous chunk's Kend as the operand
+    // fragments of the step above ([wavefront][lane], 4 tokens of one channel,
+    // 8 bytes), then its Gamma_C (fp32 per channel), byte offsets
+    static constexpr uint32_t KE_BYTES = (uint32_t)NW * 64u * 8u;
+    static constexpr uint32_t GC_OFF = KE_BYTES;
+    static_assert(KE_BYTES + 4 * D <= 2 * WS_S, "Kend and Gamma_C fit in a state area");
     static_assert(D == 64 || D == 128, "d = 64 or 128");
 };
 
@@ -80,6 +93,8 @@ struct B2Smem {
         alignas(16) bf16 dO[16 * C::LDR];    // dO [token][column]
         alignas(16) bf16 Z[16 * C::LDR];     // Z = T^T dU [token][column]
     } b;
+    alignas(16) bf16 stash[D * D];       // backward: an even chunk's start-state fragments [w][kb][lane]
+    alignas(16) bf16 upT[D * C::LDK];    // backward: U^T of the chunk before an odd chunk [column][token]
     alignas(16) bf16 tp[16 * C::LDK];    // forward: T diag(beta) [row][col]
     alignas(16) bf16 ttT[16 * C::LDK];   // backward: T^T
     alignas(16) float KK[16 * C::LS];    // K+ K-^T [t][s]
@@ -114,6 +129,9 @@ __device__ __forceinline__ bf16x8 buf_ld_b8(Rsrc r, uint32_t voff, uint32_t soff
 }
 __device__ __forceinline__ bf16x4 buf_ld_b4(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_st_b4(bf16x4 x, Rsrc r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ void buf_st_b8(bf16x8 x, Rsrc r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)voff, (int)soff, 0);
@@ -329,6 +347,11 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             relane();
             const int nv = min(CHUNK, T - n * CHUNK);
             const Rsrc rws = make_rsrc(wsh + (int64_t)n * C::WSC, (uint32_t)C::WSC * 2u);   // this chunk's saved operands
+            // even chunks of the segment save their start state; an even chunk followed
+            // by an odd one also leaves its Kend and Gamma_C in the odd one's state area
+            const bool save_s = ((n - n_lo) & 1) == 0;
+            const Rsrc rnx = make_rsrc(wsh + (int64_t)(n + 1) * C::WSC,
+                                      FULL && save_s && n + 1 < n_hi ? C::KE_BYTES + 4u * D : 0u);
             Gate G;
             gate(raw, nv, G, false);
             float vf[4], bt[4];
@@ -347,9 +370,15 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             }
             *reinterpret_cast<bf16x4*>(&sm.kpT[ch * LDK + 4 * g]) =
                 bq4(G.kf[0] * G.gam[0], G.kf[1] * G.gam[1], G.kf[2] * G.gam[2], G.kf[3] * G.gam[3]);
-            *reinterpret_cast<bf16x4*>(&sm.keT[ch * LDK + 4 * g]) =
-                bq4(G.kf[0] * (G.gC * G.igam[0]), G.kf[1] * (G.gC * G.igam[1]), G.kf[2] * (G.gC * G.igam[2]),
-                    G.kf[3] * (G.gC * G.igam[3]));
+            {
+                const bf16x4 ke = bq4(G.kf[0] * (G.gC * G.igam[0]), G.kf[1] * (G.gC * G.igam[1]),
+                                      G.kf[2] * (G.gC * G.igam[2]), G.kf[3] * (G.gC * G.igam[3]));
+                *reinterpret_cast<bf16x4*>(&sm.keT[ch * LDK + 4 * g]) = ke;
+                if constexpr (FULL) {   // dropped (a resource of size zero) unless the next chunk is odd
+                    buf_st_b4(ke, rnx, (uint32_t)lane * 8u, (uint32_t)w * 512u);
+                    buf_st32(G.gC, rnx, (uint32_t)ch * 4u, C::GC_OFF);   // the lane groups store equal values
+                }
+            }
             if (g == 0) sm.gc[ch] = G.gC;
             if (w == 0 && li == 0) {
 #pragma unroll
@@ -408,11 +437,13 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 for (int i = 0; i < 4; ++i) y[i] = (cx == 0 ? vf[i] : 0.0f) - p[i];   // the M part has V = 0
                 const f32x4 uu = mfma_k16(ld_b4(&sm.tp[li * LDK + 4 * g]), bq(y), zero4);
                 if constexpr (FULL) {
-                    // the chunk's start state and U, staged for the workspace
+                    // the chunk's start state (even chunks) and U, staged for the workspace
+                    if (save_s) {
 #pragma unroll
-                    for (int rt = 0; rt < NT; ++rt)
+                        for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sm.u.Sst[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)St[rt][cx][i];
+                            for (int i = 0; i < 4; ++i) sm.u.Sst[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)St[rt][cx][i];
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = (bf16)uu[i];
                 }
@@ -429,6 +460,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             if constexpr (FULL) {
                 // start state as row-product fragments: fragment f = (channel tile c, block kb,
                 // lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3] and S[16c + rl][32kb + 16 + 4gl ..+3]
+                if (save_s) {
 #pragma unroll
                 for (int jf = 0; jf < NT * KB * 64 / C::NTHR; ++jf) {
                     const int f = tid + jf * C::NTHR;
@@ -436,6 +468,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                     const int o = (16 * c + (l & 15)) * LDR + 32 * kb + 4 * (l >> 4);
                     const bf16x8 fr = cat8(ld_b4(&sm.u.Sst[o]), ld_b4(&sm.u.Sst[o + 16]));
                     buf_st_b8(fr, rws, (uint32_t)tid * 16u, (uint32_t)(jf * C::NTHR) * 16u);
+                }
                 }
                 {   // U rows, 16 bytes per thread; the 2D pieces are stored twice (no branch)
                     const int p = tid % (2 * D), row = p / (D / 8), c8 = (p % (D / 8)) * 8;
@@ -459,21 +492,33 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         init_state(X, Xinit, ((int64_t)(nseg - 1 - seg) * BH + bh) * D * D);
         // chunk-saved operands, loaded a chunk ahead with the raw inputs
         bf16x8 sfn[KB];                   // start-state fragments of this lane's channel tile
-        bf16x8 ufn = {};                  // 16 bytes of U rows
+        bf16x8 ufn = {}, ufp = {};        // 16 bytes of U rows (of the chunk; of the one before)
         bf16x4 tfn = {};                  // 4 elements of T^T
-        // chunk m's saved operands (zeros through resources of size zero outside the segment)
+        bf16x4 kep = {};                  // Kend of the chunk before (tokens 4g.., channel ch)
+        float gcp = 0.0f;                 // its Gamma_C of channel ch
+        // chunk m's saved operands (zeros through resources of size zero outside the
+        // segment).  An odd chunk loads the state fragments of the chunk before it, that
+        // chunk's U and the Kend and Gamma_C stored in its own state area; an even chunk
+        // loads no state (the odd chunk after it leaves it in LDS).
         auto load_saved = [&](int m) {
             const bool inside = m >= n_lo && m < n_hi;
             const int mm = inside ? m : n_lo;   // an address inside the workspace either way
             const bf16* wsm = wsh + (int64_t)mm * C::WSC;
             if constexpr (FULL) {
-                const Rsrc rws = make_rsrc(wsm, inside ? (uint32_t)C::WS_S * 2u : 0u);
+                const bool odd = inside && ((m - n_lo) & 1);
+                const bf16* wsp = odd ? wsm - C::WSC : wsm;
+                const Rsrc rws = make_rsrc(wsp, odd ? (uint32_t)C::WS_S * 2u : 0u);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
                     sfn[kb] = buf_ld_b8(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
                 // U rows: 16 bytes per thread, the 2D pieces loaded (and later written to LDS) twice
                 const Rsrc ru = make_rsrc(wsm + C::WS_S, inside ? (uint32_t)C::WS_U * 2u : 0u);
                 ufn = buf_ld_b8(ru, (uint32_t)(tid % (2 * D)) * 16u, 0u);
+                const Rsrc rup = make_rsrc(wsp + C::WS_S, odd ? (uint32_t)C::WS_U * 2u : 0u);
+                ufp = buf_ld_b8(rup, (uint32_t)(tid % (2 * D)) * 16u, 0u);
+                const Rsrc rke = make_rsrc(wsm, odd ? C::KE_BYTES + 4u * D : 0u);
+                kep = buf_ld_b4(rke, (uint32_t)lane * 8u, (uint32_t)w * 512u);
+                gcp = __builtin_bit_cast(float, buf_ld32(rke, (uint32_t)ch * 4u, C::GC_OFF));
             }
             // T^T: every wavefront loads it and writes the same values
             const Rsrc rt = make_rsrc(wsm + C::WS_S + C::WS_U, inside ? 512u : 0u);
@@ -481,6 +526,16 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         };
         load_raw(n_hi - 1, raw, BWD_T);
         load_saved(n_hi - 1);
+        if constexpr (FULL) {
+            // an even last chunk has no odd chunk after it to leave its state in LDS:
+            // fetch it here (zeros through a resource of size zero otherwise)
+            const bool even_last = ((n_hi - 1 - n_lo) & 1) == 0;
+            const Rsrc rls = make_rsrc(wsh + (int64_t)(n_hi - 1) * C::WSC, even_last ? (uint32_t)C::WS_S * 2u : 0u);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+                *reinterpret_cast<bf16x8*>(&sm.stash[((w * KB + kb) * 64 + lane) * 8]) =
+                    buf_ld_b8(rls, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
+        }
         __builtin_amdgcn_s_waitcnt(0);   // retire the first loads before the loop
         for (int n = n_hi - 1; n >= n_lo; --n) {
             relane();
@@ -502,6 +557,9 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 const int p = tid % (2 * D), row = p / (D / 8), c8 = (p % (D / 8)) * 8;
                 *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8]) = __builtin_shufflevector(ufn, ufn, 0, 1, 2, 3);
                 *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8 + 4]) = __builtin_shufflevector(ufn, ufn, 4, 5, 6, 7);
+                // U^T of the chunk before (zeros before an even chunk, unused there)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm.upT[(c8 + e) * LDK + row] = ufp[e];
             }
             *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
             load_raw(n - 1, raw, BWD_T);   // in flight during this chunk
@@ -530,6 +588,32 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                     for (int i = 0; i < 4; ++i) sm.u.Xs[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)X[rt][0][i];
             }
             lds_barrier();
+
+            if constexpr (FULL) {
+                // ---- the chunk's start state as row-product fragments
+                bf16* stw = &sm.stash[(w * KB * 64 + lane) * 8];   // this lane's fragments, block kb at +512 kb
+                if ((n - n_lo) & 1) {
+                    // odd chunk: keep the even chunk's state for the next chunk, then step it,
+                    // S_n = Diag(Gamma_C) S_{n-1} + Kend^T U_{n-1}, with the state transposed:
+                    // tile jt of S^T holds value columns 16jt + 4g + i of channel ch
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        *reinterpret_cast<bf16x8*>(stw + kb * 512) = sfn[kb];
+                        f32x4 hv[2];
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            f32x4 c;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) c[i] = gcp * (float)sfn[kb][4 * hh + i];
+                            hv[hh] = mfma_k16(ld_b4(&sm.upT[(16 * (2 * kb + hh) + li) * LDK + 4 * g]), kep, c);
+                        }
+                        sfn[kb] = cat8(bq(hv[0]), bq(hv[1]));
+                    }
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) sfn[kb] = *reinterpret_cast<const bf16x8*>(stw + kb * 512);
+                }
+            }
 
             // ---- KK = K+ K-^T (wave 0), A_qk = LowerIncl(Q+ K-^T) (wave 1)
             if (w == 0 && FULL) {

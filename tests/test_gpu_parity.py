@@ -78,6 +78,11 @@ CHUNK_CASES = [
     ("decay_stress", dict(H=4, T=1024), None, 8),
     ("decay_stress", dict(H=2, T=512), "f32", 4),                 # fp32 re-run of the stress case
     ("prefill_64k", dict(H=2, T=2048 + 9), None, 0),
+    # slow decay: the state and the segment maps carry information across many chunks
+    ("long_memory", dict(H=4, T=1024), None, 1),
+    ("long_memory", dict(H=4, T=4096 + 5), None, 8),
+    ("long_memory", dict(H=2, T=1024), "f32", 4),
+    ("long_memory", dict(H=2, T=1500, dk=64, dv=64), None, 6),
     # several segments with a ragged tail: the map kernel publishes T for the
     # partial chunk and the out kernel reads it
     ("tiny", dict(T=61), None, 3),
@@ -359,6 +364,10 @@ BWD_CASES = [
     ("small", dict(B=1, H=1, T=1500), "f32", True),       # fp32, d = 64; 6 segments
     ("decay_stress", dict(H=2, T=2048 + 3), None, True),  # d = 128 at the decay bound; 9 segments
     ("decay_stress", dict(B=1, H=1, T=1100), "f32", True),  # fp32, d = 128; 5 segments
+    ("long_memory", dict(H=2, T=512), None, True),        # slow decay, one segment
+    ("long_memory", dict(H=2, T=2048 + 3), None, True),   # slow decay; segment maps carry the state
+    ("long_memory", dict(H=2, T=1500, dk=64, dv=64), None, True),
+    ("long_memory", dict(B=1, H=1, T=1100), "f32", True),
     ("tiny", dict(T=77), "bf16", True),                   # bf16 at d = 16 (vector-unit kernel)
     ("small", dict(dk=32, dv=32, H=3, T=333), None, True),  # bf16 at d = 32 (vector-unit kernel)
 ]
@@ -459,6 +468,10 @@ def test_decay_stress_full_size_whole_tensor(oracle_mod):
     _whole_chunk_check(oracle_mod, "decay_stress")
 
 
+def test_long_memory_full_size_whole_tensor(oracle_mod):
+    _whole_chunk_check(oracle_mod, "long_memory")
+
+
 @pytest.mark.slow
 def test_prefill_1m_two_heads_every_column(oracle_mod):
     _whole_chunk_check(oracle_mod, "prefill_1m", heads=[3, 12])
@@ -493,7 +506,7 @@ def test_decode_b256_1024_steps_every_sequence(oracle_mod):
 
 
 # ----------------------------------------------------------------------------- decode replays
-@pytest.mark.parametrize("name", ["tiny", "small", "decay_stress", "prefill_64k"])
+@pytest.mark.parametrize("name", ["tiny", "small", "decay_stress", "prefill_64k", "long_memory"])
 def test_decode_replay_matches_oracle(oracle_mod, name):
     """kda_decode_step replayed token by token from S0 over a whole prefill workload
     (the 64K one included: 65,536 consecutive steps of 16 heads), every o_t and the

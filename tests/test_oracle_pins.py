@@ -389,7 +389,7 @@ def test_bf16_bound_on_16_token_inverse_decay():
     assert torch.isfinite(torch.tensor(e80, dtype=torch.float32).to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "prefill_64k", "decay_stress"])
+@pytest.mark.parametrize("name", ["tiny", "small", "prefill_64k", "decay_stress", "long_memory"])
 def test_workload_chunk_decay_within_bound(oracle_mod, name):
     w = kin.scaled(kin.WORKLOADS[name], T=min(kin.WORKLOADS[name].T, 512), B=1)
     th = kin.chunk_inputs(w)["theta"]
@@ -397,6 +397,8 @@ def test_workload_chunk_decay_within_bound(oracle_mod, name):
     assert G.min() >= -80.0
     if name == "decay_stress":   # sigma(8 +- 1): most chunks come within 1% of the bound
         assert G.min() < -79.0
+    if name == "long_memory":    # most channels keep more than 90% of the state over a chunk
+        assert float((G[:, 15::16] > -0.1).mean()) > 0.9
 
 
 # ----------------------------------------------------------------------------- brute force
