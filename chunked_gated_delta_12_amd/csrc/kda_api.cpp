@@ -70,6 +70,17 @@ bool sizes_fit(int64_t a, int64_t b, int64_t c, int64_t d) {
     return x < 4.0e18;
 }
 
+// The size limits every entry point and size query applies (after check_common).
+int check_sizes(int B, int T, int H, int dk) {
+    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
+    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*d too large");
+    // a chunk of one fp32 [B, T, H, d] tensor, 16*H*d*4 bytes, is addressed with
+    // 32-bit offsets
+    if ((int64_t)H * dk * KDA_CHUNK * 4 >= (1LL << 32))
+        return fail(KDA_ERR_SHAPE, "H*d=%lld too large (64*H*d must stay below 2^32)", (long long)H * dk);
+    return KDA_OK;
+}
+
 int check_common(int dtype, int B, int H, int dk, int dv) {
     if (dtype != KDA_BF16 && dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "unknown dtype %d", dtype);
     if (B < 1 || H < 1) return fail(KDA_ERR_SHAPE, "B=%d H=%d must be >= 1", B, H);
@@ -102,6 +113,7 @@ int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 int kda_chunk_fwd_auto_segments(int B, int T, int H, int dk, int dv) {
     if (B < 1 || T < 1 || H < 1 || !supported_d(dk) || dk != dv) return 0;
+    if (check_sizes(B, T, H, dk) != KDA_OK) return 0;
     // The map and output passes run one workgroup per compute unit: aim for one
     // resident round of 256 workgroups (every head of a run of segments at once;
     // at least two segments below 512 sequences, where the single-segment kernel,
@@ -122,8 +134,8 @@ int kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int segmen
     if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
     int st = check_common(KDA_BF16, B, H, dk, dv);
     if (st) return st;
-    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
-    const int nchunks = (T + KDA_CHUNK - 1) / KDA_CHUNK;
+    if ((st = check_sizes(B, T, H, dk))) return st;
+    const int nchunks = (int)(((int64_t)T + KDA_CHUNK - 1) / KDA_CHUNK);
     if (segments < 0 || segments > nchunks)
         return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);
     const int req = segments ? segments : kda_chunk_fwd_auto_segments(B, T, H, dk, dv);
@@ -163,11 +175,8 @@ static int chunk_fwd_impl(int dtype, int B, int T, int H, int dk, int dv, int se
                           bool noalloc = false) {
     int st = check_common(dtype, B, H, dk, dv);
     if (st) return st;
-    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
-    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*d too large");
-    if ((int64_t)H * dk * KDA_CHUNK >= (1LL << 31))
-        return fail(KDA_ERR_SHAPE, "H*d=%lld too large (16*H*d must stay below 2^31)", (long long)H * dk);
-    const int nchunks = (T + KDA_CHUNK - 1) / KDA_CHUNK;
+    if ((st = check_sizes(B, T, H, dk))) return st;
+    const int nchunks = (int)(((int64_t)T + KDA_CHUNK - 1) / KDA_CHUNK);
     if (segments < 0 || segments > nchunks)
         return fail(KDA_ERR_SHAPE, "segments=%d outside [0, %d]", segments, nchunks);
     if (!q || !k || !v || !theta || !beta || !o)
@@ -256,7 +265,7 @@ int kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, size_t* by
     if (!bytes) return fail(KDA_ERR_NULL, "bytes is NULL");
     int st = check_common(KDA_BF16, B, H, dk, dv);
     if (st) return st;
-    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
+    if ((st = check_sizes(B, T, H, dk))) return st;
     *bytes = kda::chunk_bwd_workspace_bytes(B, T, H, dk);
     return ok();
 }
@@ -267,8 +276,7 @@ int kda_chunk_bwd(int dtype, int B, int T, int H, int dk, int dv, const void* q,
                   float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_common(dtype, B, H, dk, dv);
     if (st) return st;
-    if (T < 1) return fail(KDA_ERR_SHAPE, "T=%d must be >= 1", T);
-    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*d too large");
+    if ((st = check_sizes(B, T, H, dk))) return st;
     if (!q || !k || !v || !theta || !beta || !dout || !dq || !dkk || !dvv || !dtheta || !dbeta)
         return fail(KDA_ERR_NULL, "q, k, v, theta, beta, do and every gradient but dS0 must be non-NULL");
     const void* all[] = {q, k, v, theta, beta, S0, dout, dS_T, dq, dkk, dvv, dtheta, dbeta, dS0, workspace};
@@ -352,7 +360,7 @@ int kda_decode_step_gated(int dtype, int B, int H, int dk, int dv, const void* q
 int kda_gate(int B, int T, int H, int dk, const float* theta, float* g, float* g_cum, void* stream) {
     if (B < 1 || T < 1 || H < 1) return fail(KDA_ERR_SHAPE, "B=%d T=%d H=%d must be >= 1", B, T, H);
     if (!supported_d(dk)) return fail(KDA_ERR_SHAPE, "dk=%d not in {16, 32, 64, 128}", dk);
-    if (!sizes_fit(B, T, H, dk)) return fail(KDA_ERR_SHAPE, "B*T*H*dk too large");
+    if (int st = check_sizes(B, T, H, dk)) return st;
     if (!theta) return fail(KDA_ERR_NULL, "theta is NULL");
     if (!g && !g_cum) return fail(KDA_ERR_NULL, "both g and g_cum are NULL");
     const void* all[] = {theta, g, g_cum};

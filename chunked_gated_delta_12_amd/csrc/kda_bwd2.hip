@@ -815,7 +815,7 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
                              const void* v, const float* theta, const float* beta, const float* S0,
                              const void* dout, const float* dS_T, float* dq, float* dk, float* dv,
                              float* dtheta, float* dbeta, float* dS0, void* workspace, hipStream_t stream) {
-    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int nchunks = (int)(((int64_t)T + CHUNK - 1) / CHUNK);
     const int BH = B * H;
     const size_t DD = (size_t)d * d;
     bf16* wsb = (bf16*)workspace;

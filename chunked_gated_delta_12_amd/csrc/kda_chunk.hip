@@ -776,7 +776,7 @@ combine_kernel(int BH, int nseg, const float* S0, const float* __restrict__ ws_n
 // ----------------------------------------------------------------------------- host side
 SegPlan plan_segments(int T, int requested) {
     SegPlan p;
-    p.nchunks = (T + CHUNK - 1) / CHUNK;
+    p.nchunks = (int)(((int64_t)T + CHUNK - 1) / CHUNK);
     int want = requested < 1 ? 1 : requested;
     if (want > p.nchunks) want = p.nchunks;
     p.seg_len = (p.nchunks + want - 1) / want;

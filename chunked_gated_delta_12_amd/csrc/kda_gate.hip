@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(256) gate_kernel(int B, int T, int H, int dk, 
 
 hipError_t launch_gate(int B, int T, int H, int dk, const float* theta, float* g, float* gcum,
                        hipStream_t stream) {
-    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int nchunks = (int)(((int64_t)T + CHUNK - 1) / CHUNK);
     const int64_t n = (int64_t)B * nchunks * H * dk;
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, B, T, H, dk,
