@@ -37,12 +37,14 @@
 // from the very bf16 operands the forward chain used, and keeps S_{m-1} in LDS
 // for the next chunk: half the state traffic, the largest item of the sweep's.
 //
-// MODE FULL runs both sweeps over one segment and writes the gradients.  MODE
-// FMAP / BMAP are the segment maps for few long sequences: the forward sweep
-// (FMAP, which also saves every chunk's T^T) or the carried-gradient chain
-// (BMAP) over one segment with the state widened to [0 | I] (d x 2d), whose
-// end value [N | M] is stored as the segment's affine map; the forward pass's
-// combine kernel chains the maps (the gradient's in reverse segment order).
+// MODE FULL runs both sweeps over one segment and writes the gradients.  For
+// few long sequences the segments' start states and end gradients come from
+// affine segment maps: the state maps from the forward pass's map kernel
+// (kda_map.hip, which also publishes every chunk's T' = T diag(beta)), the
+// gradient maps from MODE BMAP, the carried-gradient chain over one segment
+// with the gradient widened to [0 | I] (d x 2d) and T' read from there, whose
+// end value [N | M] is stored as the segment's map; the forward pass's combine
+// kernel chains both (the gradient's in reverse segment order).
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -108,7 +110,7 @@ struct B2Smem {
     float kz[C::NW][16];                 // rowsum(K+ * (Z S^T)) over each wavefront's channels
 };
 
-enum { B2_FULL = 0, B2_FMAP = 1, B2_BMAP = 2 };
+enum { B2_FULL = 0, B2_BMAP = 1 };
 
 __device__ __forceinline__ bf16x4 bq(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
 __device__ __forceinline__ bf16x4 bq4(float a, float b, float c, float d) {
@@ -313,13 +315,13 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                         Wt[rt][cx][i] = (cx == 1 && row == ch) ? 1.0f : 0.0f;   // [0 | I]
                 }
     };
-    // The end value [N | M] of a map sweep: N fp32 and M bf16, each [map][batch*head][d][d]
-    // (M after the nseg N blocks).  The state maps (FMAP) are stored by segment, the
-    // gradient maps (BMAP) in reverse segment order, so that both chains run forward
-    // through the same combine kernel.
+    // The end value [N | M] of the gradient's map sweep: N fp32 and M bf16, each
+    // [map][batch*head][d][d] (M after the nseg N blocks), stored in reverse segment
+    // order, so that the chain runs forward through the combine kernel as the state
+    // maps' does.
     const int nseg = (nchunks + seg_len - 1) / seg_len;
     auto store_map = [&](const f32x4 (&Wt)[NT][NCX]) {
-        const int slot = MODE == B2_BMAP ? nseg - 1 - seg : seg;
+        const int slot = nseg - 1 - seg;
         float* mn = maps + ((int64_t)slot * BH + bh) * D * D;
         bf16* mm = reinterpret_cast<bf16*>(maps + (int64_t)nseg * BH * D * D) + ((int64_t)slot * BH + bh) * D * D;
 #pragma unroll
@@ -337,7 +339,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     const std::integral_constant<bool, true> BWD_T{};
 
     // ============================================================ forward sweep
-    if constexpr (MODE != B2_BMAP) {
+    if constexpr (FULL) {
         f32x4 St[NT][NCX];
         init_state(St, Sinit, sb);
         load_raw(n_lo, raw, FWD_T);
@@ -477,15 +479,11 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 }
             }
         }
-        if constexpr (MODE == B2_FMAP) {
-            store_map(St);
-            return;
-        }
     }
     if constexpr (FULL) __syncthreads();   // the saved chunks are in memory; LDS free for the backward tiles
 
     // ============================================================ backward sweep
-    if constexpr (MODE != B2_FMAP) {
+    {
         f32x4 X[NT][NCX];                 // dS' by value-column tiles
         // the carried gradient at the segment's end: the combine wrote the segments'
         // end values in reverse order (one segment: dS_T itself)
@@ -520,8 +518,11 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 kep = buf_ld_b4(rke, (uint32_t)lane * 8u, (uint32_t)w * 512u);
                 gcp = __builtin_bit_cast(float, buf_ld32(rke, (uint32_t)ch * 4u, C::GC_OFF));
             }
-            // T^T: every wavefront loads it and writes the same values
-            const Rsrc rt = make_rsrc(wsm + C::WS_S + C::WS_U, inside ? 512u : 0u);
+            // FULL: T^T, saved by the forward sweep; BMAP: T' = T diag(beta), [batch*head][chunk]
+            // [16][16] as the forward pass's map kernel publishes it.  Lane l loads row l/4,
+            // columns 4(l%4) .. +3; every wavefront loads it and writes the same values.
+            const bf16* tsrc = FULL ? wsm + C::WS_S + C::WS_U : ws + ((int64_t)bh * nchunks + mm) * 256;
+            const Rsrc rt = make_rsrc(tsrc, inside ? 512u : 0u);
             tfn = buf_ld_b4(rt, (uint32_t)lane * 8u, 0u);
         };
         load_raw(n_hi - 1, raw, BWD_T);
@@ -561,7 +562,12 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sm.upT[(c8 + e) * LDK + row] = ufp[e];
             }
-            *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
+            if constexpr (FULL) {
+                *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
+            } else {   // T'^T = diag(beta) T^T
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.ttT[(4 * (lane & 3) + i) * LDK + (lane >> 2)] = tfn[i];
+            }
             load_raw(n - 1, raw, BWD_T);   // in flight during this chunk
             // K+, K-, Q+ and Kend of this lane's channel and tokens (recomputed in the chain rule)
             auto kpv = [&](int i) { return G.kf[i] * G.gam[i]; };
@@ -644,10 +650,11 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                     du = mfma_k32(cat8(ld_b4(&sm.ke[o]), ld_b4(&sm.ke[o + 16])),
                                   cat8(bq(X[2 * kb][cx]), bq(X[2 * kb + 1][cx])), du);
                 }
+                // FULL: Z = T^T dU and -dY = -diag(beta) Z; BMAP: -dY = -T'^T dU directly
                 const f32x4 z = mfma_k16(ld_b4(&sm.ttT[li * LDK + 4 * g]), bq(du), zero4);
                 f32x4 ndy;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ndy[i] = -bt[i] * z[i];
+                for (int i = 0; i < 4; ++i) ndy[i] = FULL ? -bt[i] * z[i] : -z[i];
                 if constexpr (FULL) {
                     const Rsrc rdv = make_rsrc(dv + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
 #pragma unroll
@@ -834,9 +841,17 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
     if (nseg == 1) {                                                                                      \
         KDA_B2(D, B2_FULL, BH, S0, dS_T, nullptr);                                                        \
     } else {                                                                                              \
-        KDA_B2(D, B2_FMAP, nseg * BH, nullptr, nullptr, mapF);                                            \
+        /* the state maps and every chunk's T' (into the chunk area, which the full pass */               \
+        /* overwrites only later) from the forward pass's map kernel */                                   \
+        SegPlan plan;                                                                                     \
+        plan.nchunks = nchunks;                                                                           \
+        plan.seg_len = seg_len;                                                                           \
+        plan.nseg = nseg;                                                                                 \
+        hipError_t e = launch_chunk_map(false, B, T, H, D, plan, k, v, theta, beta, mapF,                  \
+                                        mapF + (size_t)nseg * BH * DD, wsb, stream);                      \
+        if (e != hipSuccess) return e;                                                                    \
         KDA_B2(D, B2_BMAP, nseg * BH, nullptr, nullptr, mapB);                                            \
-        hipError_t e = launch_state_combine(D, BH, nseg, S0, mapF, mapF + (size_t)nseg * BH * DD, Sst, stream); \
+        e = launch_state_combine(D, BH, nseg, S0, mapF, mapF + (size_t)nseg * BH * DD, Sst, stream);      \
         if (e == hipSuccess)                                                                              \
             e = launch_state_combine(D, BH, nseg, dS_T, mapB, mapB + (size_t)nseg * BH * DD, Xen, stream);  \
         if (e != hipSuccess) return e;                                                                    \
