@@ -101,7 +101,6 @@ struct B2Smem {
     alignas(16) bf16 ttT[16 * C::LDK];   // backward: T^T
     alignas(16) float KK[16 * C::LS];    // K+ K-^T [t][s]
     alignas(16) float AmT[16 * C::LS];   // forward: A^T, A = StrictLower(diag(beta) KK)
-    alignas(16) float Aqk[16 * C::LS];   // LowerIncl(Q+ K-^T) [t][s]
     alignas(16) float dAqk[16 * C::LS];
     alignas(16) float dA[16 * C::LS];
     alignas(16) float gc[D];             // Gamma_C per channel
@@ -621,29 +620,22 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 }
             }
 
-            // ---- KK = K+ K-^T (wave 0), A_qk = LowerIncl(Q+ K-^T) (wave 1)
-            if (w == 0 && FULL) {
-                const f32x4 kk = small_abt<D>(sm.kp, sm.km, li, g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.KK[(4 * g + i) * LS + li] = kk[i];
-            }
-            if (w == (FULL ? 1 : 0)) {
+            // ---- A_qk = LowerIncl(Q+ K-^T), formed by every wavefront: lane (g, li) holds
+            // A_qk[4g + i][li], which is its A_qk^T operand fragment (row li, k = 4g + i)
+            bf16x4 aqT;
+            {
                 const f32x4 aq = small_abt<D>(sm.b.qp, sm.km, li, g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.Aqk[(4 * g + i) * LS + li] = (li <= 4 * g + i) ? aq[i] : 0.0f;
+                aqT = bq4(li <= 4 * g ? aq[0] : 0.0f, li <= 4 * g + 1 ? aq[1] : 0.0f,
+                          li <= 4 * g + 2 ? aq[2] : 0.0f, li <= 4 * g + 3 ? aq[3] : 0.0f);
             }
-            lds_barrier();
 
             // ---- column products: dU, Z, dY = dV, and dS' <- Diag(Gamma_C) dS' + Q+^T dO - K+^T dY
             float zvp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int cx = 0; cx < NCX; ++cx) {
                 f32x4 du = zero4;
-                if (cx == 0) {   // A_qk^T dO (the M part of the widened gradient has dO = 0)
-                    const bf16x4 at = bq4(sm.Aqk[(4 * g + 0) * LS + li], sm.Aqk[(4 * g + 1) * LS + li],
-                                          sm.Aqk[(4 * g + 2) * LS + li], sm.Aqk[(4 * g + 3) * LS + li]);
-                    du = mfma_k16(at, bq4(of[0], of[1], of[2], of[3]), du);
-                }
+                if (cx == 0)   // A_qk^T dO (the M part of the widened gradient has dO = 0)
+                    du = mfma_k16(aqT, bq4(of[0], of[1], of[2], of[3]), du);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
                     const int o = li * LDR + 32 * kb + 4 * g;
@@ -688,9 +680,14 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             }
             lds_barrier();
 
-            // ---- dA_qk = LowerIncl(dO U^T) (wave 0), dA = StrictLower(-Z U^T) (wave 1);
-            // everyone: the row products over the state's columns, dO S^T, U dS'^T and
-            // Z S^T, and dGamma_C = rowsum(dS' * S)
+            // ---- dA_qk = LowerIncl(dO U^T) (wave 0), dA = StrictLower(-Z U^T) (wave 1),
+            // KK = K+ K-^T (wave 2, for dbeta); everyone: the row products over the state's
+            // columns, dO S^T, U dS'^T and Z S^T, and dGamma_C = rowsum(dS' * S)
+            if (w == 2) {
+                const f32x4 kk = small_abt<D>(sm.kp, sm.km, li, g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.KK[(4 * g + i) * LS + li] = kk[i];
+            }
             if (w == 0) {
                 const f32x4 x = small_abt<D>(sm.b.dO, sm.U, li, g);
 #pragma unroll
