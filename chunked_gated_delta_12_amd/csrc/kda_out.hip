@@ -58,19 +58,21 @@ struct OutCfg {
     static_assert(NT % NCW == 0 && NTG * PPH == 64 && TPL * NTG == CHUNK, "lane mappings");
 };
 
-// What the consumers read for one chunk.  The consumer of column tile jt stages
-// its o tile, [token][16 columns], in the first 256 elements of rows 16jt ..
-// 16jt+15 of v_col -- rows only it reads -- after it has read them.
+// What the consumers read for one chunk, and the o tiles they stage for the
+// producers to write out: o_st, [token][column] with a row of D + 4 elements (a
+// stride of 2 (mod 32) dwords), on which the consumers' 8-byte writes of
+// 16 rows and the producers' reads of whole token rows meet no bank conflict.
 template <int D>
 struct OutSlot {
     typedef OutCfg<D> C;
     alignas(16) bf16 kn_row[16 * C::LDR];            // -K+ = -K*Gamma             [token][ch]
     alignas(16) bf16 qp_row[16 * C::LDR];            // Q+ = Q*Gamma               [token][ch]
     alignas(16) bf16 ke_col[D * C::LDK];             // Kend^T = (K*Gamma_C/Gamma)^T [ch][token]
-    alignas(16) bf16 v_col[D * C::LDK];              // V^T, then the staged o     [ch][token]
+    alignas(16) bf16 v_col[D * C::LDK];              // V^T                        [ch][token]
     alignas(16) bf16 t_row[16 * C::LDK];             // T' = (I + A)^-1 diag(beta) [row][k]
     alignas(16) bf16 aqk[C::NSP][16 * C::LDK];       // A_qk over each channel half [token][token]
     alignas(16) float gc[D];                         // Gamma_C per channel
+    alignas(16) bf16 o_st[16 * (D + 4)];             // the staged o               [token][column]
 };
 template <int D>
 struct OutSmem {
@@ -201,9 +203,8 @@ out_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg, int smul, c
             tl = BufQuad<bf16>::ld(rt, (uint32_t)(r * 16 + 4 * g) * 2u, 0u);
         };
 
-        // o tiles.  Each producer writes out the columns of its own channel half:
-        // their staging lives in the v_col rows that only it overwrites with the
-        // next chunk's V, so neither producer of a chunk waits for the other.
+        // o tiles.  Each producer writes out the columns of its own channel half of
+        // the chunk staged in its slot, so neither producer of a chunk waits for the other.
         // Units of UE elements, UPH per token row of the half, one per lane and pass.
         constexpr int UE = D / 2 >= 64 ? 8 : 4;          // elements per unit (16 or 8 bytes)
         constexpr int UPH = (D / 2) / UE;                // units per token row of a half
@@ -244,7 +245,16 @@ out_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg, int smul, c
             for (int jj = 0; jj < NUH; ++jj) {
                 int t, col;
                 unit_tc(jj, t, col);
-                Unit val = *reinterpret_cast<const Unit*>(&sl.v_col[(col / 16) * 16 * C::LDK + t * 16 + col % 16]);
+                // 8-byte halves: the staged rows are 8-byte aligned
+                const bf16* sp = &sl.o_st[t * (D + 4) + col];
+                Unit val;
+                if constexpr (UE == 8) {
+                    typedef uint32_t U2 __attribute__((__vector_size__(8)));
+                    const U2 lo = *reinterpret_cast<const U2*>(sp), hi = *reinterpret_cast<const U2*>(sp + 4);
+                    val = Unit{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    val = *reinterpret_cast<const Unit*>(sp);
+                }
                 if constexpr (GATE) val = out_gate<Unit>(val, zl[jj]);
                 if constexpr (UE == 8)
                     __builtin_amdgcn_raw_buffer_store_b128(val, ro, unit_off(jj), 0, 0);
@@ -401,14 +411,14 @@ out_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg, int smul, c
 #pragma unroll
             for (int jj = 0; jj < C::TPW; ++jj) up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(y[jj]), f32x4{0, 0, 0, 0}));
             // O^T = O1^T + U^T A_qk^T over both channel halves: lane (g, r) holds
-            // o[token r][16jt + 4g + i], staged in the rows of v_col only this tile reads
+            // o[token r][16jt + 4g + i], staged for the producers
             const PFrag qf0 = out_ldk16(&sl.aqk[0][r * C::LDK + 4 * g]);
             const PFrag qf1 = out_ldk16(&sl.aqk[1][r * C::LDK + 4 * g]);
 #pragma unroll
             for (int jj = 0; jj < C::TPW; ++jj) {
                 const int jt = wave + C::NCW * jj;
                 const f32x4 ot = MM::mm16(up[jj], qf1, MM::mm16(up[jj], qf0, o1[jj]));
-                out_store4(&sl.v_col[jt * 16 * C::LDK + r * 16 + 4 * g], ot);
+                out_store4(&sl.o_st[r * (D + 4) + 16 * jt + 4 * g], ot);
             }
             // S <- Diag(Gamma_C) S + Kend^T U
 #pragma unroll
