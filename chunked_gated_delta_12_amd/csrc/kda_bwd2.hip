@@ -61,16 +61,15 @@ struct B2Cfg {
     static constexpr int LDR = D + 4;        // bf16 row stride of [16][D] tiles
     static constexpr int LDK = 20;           // bf16 row stride of [.][16] tiles
     static constexpr int LS = 20;            // fp32 row stride of 16x16 tiles
-    // workspace of one chunk of one sequence, in bf16 elements: the start state
-    // as row-product operand fragments, U rows [16][D], and T^T [16][16]
-    static constexpr int64_t WS_S = (int64_t)D * D;
-    static constexpr int64_t WS_U = 16 * (int64_t)D;
-    static constexpr int64_t WSC = WS_S + WS_U + 256;
-    // in the state area of an odd chunk: the previous chunk's Kend as the operand
-    // fragments of the step above ([wavefront][lane], 4 tokens of one channel,
-    // 8 bytes), then its Gamma_C (fp32 per channel), byte offsets
-    static constexpr uint32_t KE_BYTES = (uint32_t)NW * 64u * 8u;
-    static constexpr uint32_t GC_OFF = KE_BYTES;
+    // workspace of one chunk of one sequence (kda_launch.hpp): the start state as
+    // row-product operand fragments, U rows [16][D], and T^T [16][16]; in the state
+    // area of an odd chunk the previous chunk's Kend as the operand fragments of the
+    // reconstruction step ([wavefront][lane], 4 tokens of one channel, 8 bytes), then
+    // its Gamma_C (fp32 per channel)
+    typedef BwdChunkWs<D> W;
+    static constexpr int64_t WS_S = W::WS_S, WS_U = W::WS_U, WSC = W::WSC;
+    static constexpr uint32_t KE_BYTES = W::KE_BYTES, GC_OFF = W::GC_OFF;
+    static_assert(KE_BYTES == (uint32_t)NW * 64u * 8u, "one 8-byte Kend fragment per lane");
     static_assert(KE_BYTES + 4 * D <= 2 * WS_S, "Kend and Gamma_C fit in a state area");
     static_assert(D == 64 || D == 128, "d = 64 or 128");
 };
@@ -80,14 +79,12 @@ struct B2Smem {
     typedef B2Cfg<D> C;
     alignas(16) bf16 kp[16 * C::LDR];    // K+   [token][channel]
     alignas(16) bf16 km[16 * C::LDR];    // K-
-    alignas(16) bf16 ke[16 * C::LDR];    // Kend (backward)
+    alignas(16) bf16 ke[16 * C::LDR];    // Kend
     alignas(16) bf16 kpT[D * C::LDK];    // K+^T [channel][token]
-    alignas(16) bf16 kmT[D * C::LDK];    // K-^T (backward)
-    alignas(16) bf16 keT[D * C::LDK];    // Kend^T (forward)
+    alignas(16) bf16 kmT[D * C::LDK];    // K-^T
     alignas(16) bf16 U[16 * C::LDR];     // U [token][value column]
-    union {
-        alignas(16) bf16 Sst[D * C::LDR];   // forward: the chunk's start state [channel][column]
-        alignas(16) bf16 Xs[D * C::LDR];    // backward: dS' of the chunk's end [channel][column]
+    struct {
+        alignas(16) bf16 Xs[D * C::LDR];    // dS' of the chunk's end [channel][column]
     } u;
     struct {
         alignas(16) bf16 qp[16 * C::LDR];    // Q+
@@ -95,21 +92,20 @@ struct B2Smem {
         alignas(16) bf16 dO[16 * C::LDR];    // dO [token][column]
         alignas(16) bf16 Z[16 * C::LDR];     // Z = T^T dU [token][column]
     } b;
-    alignas(16) bf16 stash[D * D];       // backward: an even chunk's start-state fragments [w][kb][lane]
-    alignas(16) bf16 upT[D * C::LDK];    // backward: U^T of the chunk before an odd chunk [column][token]
-    alignas(16) bf16 tp[16 * C::LDK];    // forward: T diag(beta) [row][col]
-    alignas(16) bf16 ttT[16 * C::LDK];   // backward: T^T
+    alignas(16) bf16 stash[D * D];       // an even chunk's start-state fragments [w][kb][lane]
+    alignas(16) bf16 upT[D * C::LDK];    // U^T of the chunk before an odd chunk [column][token]
+    alignas(16) bf16 ttT[16 * C::LDK];   // T^T (BMAP: T'^T)
     alignas(16) float KK[16 * C::LS];    // K+ K-^T [t][s]
-    alignas(16) float AmT[16 * C::LS];   // forward: A^T, A = StrictLower(diag(beta) KK)
     alignas(16) float dAqk[16 * C::LS];
     alignas(16) float dA[16 * C::LS];
     alignas(16) float gc[D];             // Gamma_C per channel
-    float beta[16];
     float zv[C::NW][16];                 // rowsum(Z * V) over each wavefront's columns
     float kz[C::NW][16];                 // rowsum(K+ * (Z S^T)) over each wavefront's channels
 };
 
-enum { B2_FULL = 0, B2_BMAP = 1 };
+// BMAP: the gradient map of a segment; BWD: the backward sweep over a segment, from
+// the operands the map kernel's SAVE mode wrote.
+enum { B2_BMAP = 1, B2_BWD = 2 };
 
 __device__ __forceinline__ bf16x4 bq(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
 __device__ __forceinline__ bf16x4 bq4(float a, float b, float c, float d) {
@@ -175,12 +171,12 @@ template <int D, int MODE>
 __global__ void __launch_bounds__(B2Cfg<D>::NTHR)
 bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restrict__ q,
             const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ theta,
-            const float* __restrict__ beta, const float* __restrict__ Sinit, const bf16* __restrict__ dout,
+            const float* __restrict__ beta, const bf16* __restrict__ dout,
             const float* __restrict__ Xinit, float* __restrict__ dq, float* __restrict__ dk,
             float* __restrict__ dv, float* __restrict__ dtheta, float* __restrict__ dbeta,
             float* __restrict__ dS0, bf16* __restrict__ ws, float* __restrict__ maps) {
     typedef B2Cfg<D> C;
-    constexpr bool FULL = MODE == B2_FULL;
+    constexpr bool FULL = MODE != B2_BMAP;   // writes the gradients
     constexpr int NCX = FULL ? 1 : 2;   // column tiles per wavefront (the widened state in the maps)
     constexpr int NT = C::NT, KB = C::KB, LDR = C::LDR, LDK = C::LDK, LS = C::LS;
     constexpr float LOG2E = 1.4426950408889634f;
@@ -196,7 +192,6 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     int g = lane >> 4, li = lane & 15;
     const int bh = blockIdx.x % BH, seg = blockIdx.x / BH, b = bh / H, h = bh % H;
     const int n_lo = seg * seg_len, n_hi = min(nchunks, n_lo + seg_len);
-    const int64_t sb = ((int64_t)seg * BH + bh) * D * D;             // this segment's start / end matrix
     const uint32_t tstr = (uint32_t)(H * D);                          // elements between tokens
     const int64_t hb = (int64_t)b * T * H * D + (int64_t)h * D;      // token 0 of this head
     const int64_t bb = (int64_t)b * T * H + h;                       // beta of token 0
@@ -227,8 +222,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     // Unconditional: a chunk outside the segment (the one after the last, or before the
     // first) reads zeros through resources of size zero, so no load sits under a branch
     // (which would make the compiler wait for every outstanding access at the join).
-    auto load_raw = [&](int m, Raw& r, auto bwd_tag) {
-        constexpr bool BWD = decltype(bwd_tag)::value;
+    auto load_raw = [&](int m, Raw& r) {
         const int tm = m * CHUNK;
         const bool inside = m >= n_lo && m < n_hi;
         const uint32_t nv = __builtin_amdgcn_readfirstlane(inside ? max(0, min(CHUNK, T - tm)) : 0);
@@ -244,7 +238,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             r.k[i] = buf_ld16(rk, vo2, (uint32_t)i * row2);
             r.bt[i] = __builtin_bit_cast(float, buf_ld32(rb, vb, (uint32_t)i * hrow));
         }
-        if constexpr (BWD) {
+        {
             const Rsrc rq = make_rsrc(q + base, span * 2u);
             const Rsrc ro = make_rsrc(dout + base, span * 2u);
 #pragma unroll
@@ -253,7 +247,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 r.o[i] = buf_ld16(ro, vo2, (uint32_t)i * row2);
             }
         }
-        if constexpr (!BWD || FULL) {   // v: the forward sweep's Y, the backward sweep's rowsum(Z * V)
+        if constexpr (FULL) {   // v: rowsum(Z * V) in dbeta
             const Rsrc rv = make_rsrc(v + base, span * 2u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) r.x[i] = buf_ld16(rv, vo2, (uint32_t)i * row2);
@@ -334,152 +328,6 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     };
 
     Raw raw = {};
-    const std::integral_constant<bool, false> FWD_T{};
-    const std::integral_constant<bool, true> BWD_T{};
-
-    // ============================================================ forward sweep
-    if constexpr (FULL) {
-        f32x4 St[NT][NCX];
-        init_state(St, Sinit, sb);
-        load_raw(n_lo, raw, FWD_T);
-        // retire the first loads before the loop, so the wait counts inside it stay exact
-        __builtin_amdgcn_s_waitcnt(0);
-        for (int n = n_lo; n < n_hi; ++n) {
-            relane();
-            const int nv = min(CHUNK, T - n * CHUNK);
-            const Rsrc rws = make_rsrc(wsh + (int64_t)n * C::WSC, (uint32_t)C::WSC * 2u);   // this chunk's saved operands
-            // even chunks of the segment save their start state; an even chunk followed
-            // by an odd one also leaves its Kend and Gamma_C in the odd one's state area
-            const bool save_s = ((n - n_lo) & 1) == 0;
-            const Rsrc rnx = make_rsrc(wsh + (int64_t)(n + 1) * C::WSC,
-                                      FULL && save_s && n + 1 < n_hi ? C::KE_BYTES + 4u * D : 0u);
-            Gate G;
-            gate(raw, nv, G, false);
-            float vf[4], bt[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vf[i] = (float)b16_of(raw.x[i]);
-                bt[i] = raw.bt[i];
-            }
-            load_raw(n + 1, raw, FWD_T);   // in flight during this chunk
-            // tiles of the chunk
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * g + i;
-                sm.kp[t * LDR + ch] = (bf16)(G.kf[i] * G.gam[i]);
-                sm.km[t * LDR + ch] = (bf16)(G.kf[i] * G.igam[i]);
-            }
-            *reinterpret_cast<bf16x4*>(&sm.kpT[ch * LDK + 4 * g]) =
-                bq4(G.kf[0] * G.gam[0], G.kf[1] * G.gam[1], G.kf[2] * G.gam[2], G.kf[3] * G.gam[3]);
-            {
-                const bf16x4 ke = bq4(G.kf[0] * (G.gC * G.igam[0]), G.kf[1] * (G.gC * G.igam[1]),
-                                      G.kf[2] * (G.gC * G.igam[2]), G.kf[3] * (G.gC * G.igam[3]));
-                *reinterpret_cast<bf16x4*>(&sm.keT[ch * LDK + 4 * g]) = ke;
-                if constexpr (FULL) {   // dropped (a resource of size zero) unless the next chunk is odd
-                    buf_st_b4(ke, rnx, (uint32_t)lane * 8u, (uint32_t)w * 512u);
-                    buf_st32(G.gC, rnx, (uint32_t)ch * 4u, C::GC_OFF);   // the lane groups store equal values
-                }
-            }
-            if (g == 0) sm.gc[ch] = G.gC;
-            if (w == 0 && li == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.beta[4 * g + i] = bt[i];
-            }
-            lds_barrier();
-            // A = StrictLower(diag(beta) K+ K-^T), stored transposed for the solve
-            if (w == 0) {
-                const f32x4 kk = small_abt<D>(sm.kp, sm.km, li, g);
-                f32x4 a;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = (li < 4 * g + i) ? bt[i] * kk[i] : 0.0f;
-                *reinterpret_cast<f32x4*>(&sm.AmT[li * LS + 4 * g]) = a;
-            }
-            lds_barrier();
-            // T = (I + A)^-1: lane (g, r) solves column r (the four lane groups hold
-            // copies) right-looking; group g keeps rows 4g .. 4g+3
-            if (w == 0) {
-                const int j = li;
-                float x[16];
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.0f : 0.0f;
-#pragma unroll
-                for (int s = 0; s < 15; ++s) {
-                    f32x4 col[4];
-#pragma unroll
-                    for (int c = s / 4; c < 4; ++c) col[c] = *reinterpret_cast<const f32x4*>(&sm.AmT[s * LS + 4 * c]);
-                    const float xs = x[s];
-#pragma unroll
-                    for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
-                }
-                if (g == 0) {   // the first lane group writes column j
-                    const float bj = sm.beta[j];
-#pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) sm.tp[rr * LDK + j] = (bf16)(x[rr] * bj);   // T diag(beta)
-                    // T^T row j, for the backward sweep
-                    buf_st_b8(cat8(bq4(x[0], x[1], x[2], x[3]), bq4(x[4], x[5], x[6], x[7])), rws, (uint32_t)j * 32u,
-                              (uint32_t)(C::WS_S + C::WS_U) * 2u);
-                    buf_st_b8(cat8(bq4(x[8], x[9], x[10], x[11]), bq4(x[12], x[13], x[14], x[15])), rws,
-                              (uint32_t)j * 32u, (uint32_t)(C::WS_S + C::WS_U) * 2u + 16u);
-                }
-            }
-            lds_barrier();
-            // column products: Y = V - K+ S, U = T diag(beta) Y, S <- Diag(Gamma_C) S + Kend^T U
-#pragma unroll
-            for (int cx = 0; cx < NCX; ++cx) {
-                f32x4 p = zero4;
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const int o = li * LDR + 32 * kb + 4 * g;
-                    p = mfma_k32(cat8(ld_b4(&sm.kp[o]), ld_b4(&sm.kp[o + 16])),
-                                 cat8(bq(St[2 * kb][cx]), bq(St[2 * kb + 1][cx])), p);
-                }
-                f32x4 y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = (cx == 0 ? vf[i] : 0.0f) - p[i];   // the M part has V = 0
-                const f32x4 uu = mfma_k16(ld_b4(&sm.tp[li * LDK + 4 * g]), bq(y), zero4);
-                if constexpr (FULL) {
-                    // the chunk's start state (even chunks) and U, staged for the workspace
-                    if (save_s) {
-#pragma unroll
-                        for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) sm.u.Sst[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)St[rt][cx][i];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = (bf16)uu[i];
-                }
-                const bf16x4 ub = bq(uu);
-#pragma unroll
-                for (int rt = 0; rt < NT; ++rt) {
-                    const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sm.gc[16 * rt + 4 * g]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) St[rt][cx][i] *= gcv[i];
-                    St[rt][cx] = mfma_k16(ld_b4(&sm.keT[(16 * rt + li) * LDK + 4 * g]), ub, St[rt][cx]);
-                }
-            }
-            lds_barrier();
-            if constexpr (FULL) {
-                // start state as row-product fragments: fragment f = (channel tile c, block kb,
-                // lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3] and S[16c + rl][32kb + 16 + 4gl ..+3]
-                if (save_s) {
-#pragma unroll
-                for (int jf = 0; jf < NT * KB * 64 / C::NTHR; ++jf) {
-                    const int f = tid + jf * C::NTHR;
-                    const int c = f / (KB * 64), kb = (f / 64) % KB, l = f % 64;
-                    const int o = (16 * c + (l & 15)) * LDR + 32 * kb + 4 * (l >> 4);
-                    const bf16x8 fr = cat8(ld_b4(&sm.u.Sst[o]), ld_b4(&sm.u.Sst[o + 16]));
-                    buf_st_b8(fr, rws, (uint32_t)tid * 16u, (uint32_t)(jf * C::NTHR) * 16u);
-                }
-                }
-                {   // U rows, 16 bytes per thread; the 2D pieces are stored twice (no branch)
-                    const int p = tid % (2 * D), row = p / (D / 8), c8 = (p % (D / 8)) * 8;
-                    const bf16x8 ur = cat8(ld_b4(&sm.U[row * LDR + c8]), ld_b4(&sm.U[row * LDR + c8 + 4]));
-                    buf_st_b8(ur, rws, (uint32_t)(row * D + c8) * 2u, (uint32_t)C::WS_S * 2u);
-                }
-            }
-        }
-    }
-    if constexpr (FULL) __syncthreads();   // the saved chunks are in memory; LDS free for the backward tiles
 
     // ============================================================ backward sweep
     {
@@ -489,7 +337,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         init_state(X, Xinit, ((int64_t)(nseg - 1 - seg) * BH + bh) * D * D);
         // chunk-saved operands, loaded a chunk ahead with the raw inputs
         bf16x8 sfn[KB];                   // start-state fragments of this lane's channel tile
-        bf16x8 ufn = {}, ufp = {};        // 16 bytes of U rows (of the chunk; of the one before)
+        bf16x4 ufn = {}, ufp = {};        // U of tile w, tokens 4g.., column 16w + li (of the chunk; of the one before)
         bf16x4 tfn = {};                  // 4 elements of T^T
         bf16x4 kep = {};                  // Kend of the chunk before (tokens 4g.., channel ch)
         float gcp = 0.0f;                 // its Gamma_C of channel ch
@@ -508,11 +356,11 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
                     sfn[kb] = buf_ld_b8(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
-                // U rows: 16 bytes per thread, the 2D pieces loaded (and later written to LDS) twice
+                // U, stored by column tiles: [tile][lane (g, li)][tokens 4g .. 4g+3], 8 bytes per lane
                 const Rsrc ru = make_rsrc(wsm + C::WS_S, inside ? (uint32_t)C::WS_U * 2u : 0u);
-                ufn = buf_ld_b8(ru, (uint32_t)(tid % (2 * D)) * 16u, 0u);
+                ufn = buf_ld_b4(ru, (uint32_t)lane * 8u, (uint32_t)w * 512u);
                 const Rsrc rup = make_rsrc(wsp + C::WS_S, odd ? (uint32_t)C::WS_U * 2u : 0u);
-                ufp = buf_ld_b8(rup, (uint32_t)(tid % (2 * D)) * 16u, 0u);
+                ufp = buf_ld_b4(rup, (uint32_t)lane * 8u, (uint32_t)w * 512u);
                 const Rsrc rke = make_rsrc(wsm, odd ? C::KE_BYTES + 4u * D : 0u);
                 kep = buf_ld_b4(rke, (uint32_t)lane * 8u, (uint32_t)w * 512u);
                 gcp = __builtin_bit_cast(float, buf_ld32(rke, (uint32_t)ch * 4u, C::GC_OFF));
@@ -524,7 +372,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             const Rsrc rt = make_rsrc(tsrc, inside ? 512u : 0u);
             tfn = buf_ld_b4(rt, (uint32_t)lane * 8u, 0u);
         };
-        load_raw(n_hi - 1, raw, BWD_T);
+        load_raw(n_hi - 1, raw);
         load_saved(n_hi - 1);
         if constexpr (FULL) {
             // an even last chunk has no odd chunk after it to leave its state in LDS:
@@ -554,12 +402,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             // (no branch around registers of pending loads: every thread writes, the
             // duplicates with equal values)
             if constexpr (FULL) {
-                const int p = tid % (2 * D), row = p / (D / 8), c8 = (p % (D / 8)) * 8;
-                *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8]) = __builtin_shufflevector(ufn, ufn, 0, 1, 2, 3);
-                *reinterpret_cast<bf16x4*>(&sm.U[row * LDR + c8 + 4]) = __builtin_shufflevector(ufn, ufn, 4, 5, 6, 7);
-                // U^T of the chunk before (zeros before an even chunk, unused there)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sm.upT[(c8 + e) * LDK + row] = ufp[e];
+                for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = ufn[i];
+                // U^T of the chunk before (zeros before an even chunk, unused there)
+                *reinterpret_cast<bf16x4*>(&sm.upT[ch * LDK + 4 * g]) = ufp;
             }
             if constexpr (FULL) {
                 *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
@@ -567,7 +413,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.ttT[(4 * (lane & 3) + i) * LDK + (lane >> 2)] = tfn[i];
             }
-            load_raw(n - 1, raw, BWD_T);   // in flight during this chunk
+            load_raw(n - 1, raw);   // in flight during this chunk
             // K+, K-, Q+ and Kend of this lane's channel and tokens (recomputed in the chain rule)
             auto kpv = [&](int i) { return G.kf[i] * G.gam[i]; };
             auto kmv = [&](int i) { return G.kf[i] * G.igam[i]; };
@@ -830,29 +676,35 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
     float* mapB = mapF + (size_t)nseg * BH * 2 * DD;
     float* Sst = mapB + (size_t)nseg * BH * 2 * DD;    // state at every segment's start
     float* Xen = Sst + (size_t)nseg * BH * DD;         // carried gradient at the segments' ends, reversed
-#define KDA_B2(D, MODE, GRID, SI, XI, MP)                                                                   \
+#define KDA_B2(D, MODE, GRID, XI, MP)                                                                   \
     hipLaunchKernelGGL((bwd2_kernel<D, MODE>), dim3((unsigned)(GRID)), dim3(B2Cfg<D>::NTHR), 0, stream, T, H, \
-                       BH, nchunks, seg_len, (const bf16*)q, (const bf16*)k, (const bf16*)v, theta, beta, SI,  \
+                       BH, nchunks, seg_len, (const bf16*)q, (const bf16*)k, (const bf16*)v, theta, beta,      \
                        (const bf16*)dout, XI, dq, dk, dv, dtheta, dbeta, dS0, wsb, MP)
+    SegPlan plan;
+    plan.nchunks = nchunks;
+    plan.seg_len = seg_len;
+    plan.nseg = nseg;
+    // One segment: the forward chain's saved operands from the map kernel's SAVE mode,
+    // then the backward sweep.  Several: the state maps and every chunk's T' (into the
+    // chunk area, which the SAVE pass overwrites only later) from the prefill's map
+    // kernel, the gradient maps, both chains combined, then SAVE and the backward sweep
+    // from the segments' boundary values.
 #define KDA_B2_ALL(D)                                                                                     \
     if (nseg == 1) {                                                                                      \
-        KDA_B2(D, B2_FULL, BH, S0, dS_T, nullptr);                                                        \
+        hipError_t e = launch_chunk_save(B, T, H, D, plan, k, v, theta, beta, S0, wsb, stream);           \
+        if (e != hipSuccess) return e;                                                                    \
+        KDA_B2(D, B2_BWD, BH, dS_T, nullptr);                                                             \
     } else {                                                                                              \
-        /* the state maps and every chunk's T' (into the chunk area, which the full pass */               \
-        /* overwrites only later) from the forward pass's map kernel */                                   \
-        SegPlan plan;                                                                                     \
-        plan.nchunks = nchunks;                                                                           \
-        plan.seg_len = seg_len;                                                                           \
-        plan.nseg = nseg;                                                                                 \
         hipError_t e = launch_chunk_map(false, B, T, H, D, plan, k, v, theta, beta, mapF,                  \
                                         mapF + (size_t)nseg * BH * DD, wsb, stream);                      \
         if (e != hipSuccess) return e;                                                                    \
-        KDA_B2(D, B2_BMAP, nseg * BH, nullptr, nullptr, mapB);                                            \
+        KDA_B2(D, B2_BMAP, nseg * BH, nullptr, mapB);                                                     \
         e = launch_state_combine(D, BH, nseg, S0, mapF, mapF + (size_t)nseg * BH * DD, Sst, stream);      \
         if (e == hipSuccess)                                                                              \
             e = launch_state_combine(D, BH, nseg, dS_T, mapB, mapB + (size_t)nseg * BH * DD, Xen, stream);  \
+        if (e == hipSuccess) e = launch_chunk_save(B, T, H, D, plan, k, v, theta, beta, Sst, wsb, stream); \
         if (e != hipSuccess) return e;                                                                    \
-        KDA_B2(D, B2_FULL, nseg * BH, (const float*)Sst, (const float*)Xen, nullptr);                      \
+        KDA_B2(D, B2_BWD, nseg * BH, (const float*)Xen, nullptr);                                         \
     }                                                                                                     \
     return hipGetLastError()
     switch (d) {

@@ -36,6 +36,30 @@ hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan&
                             const void* v, const float* theta, const float* beta, float* ws_n,
                             void* ws_m, void* ws_t, hipStream_t stream);
 
+// Per-chunk workspace of the bf16 backward pass (one chunk of one sequence), in bf16
+// elements: the start state as row-product operand fragments (even chunks of a
+// segment only), U by 16-column tiles ([d/16][64 lanes (g, li)][tokens 4g ..
+// 4g+3 of column 16 tile + li]), T^T [16][16].  An odd chunk's state area holds the
+// previous chunk's Kend (operand fragments [d/16][64 lanes] x 8 bytes) and Gamma_C
+// (fp32 per channel) instead, at the byte offsets below.
+template <int D>
+struct BwdChunkWs {
+    static constexpr int64_t WS_S = (int64_t)D * D;
+    static constexpr int64_t WS_U = 16 * (int64_t)D;
+    static constexpr int64_t WSC = WS_S + WS_U + 256;
+    static constexpr uint32_t KE_BYTES = (uint32_t)(D / 16) * 64u * 8u;
+    static constexpr uint32_t GC_OFF = KE_BYTES;
+};
+
+// The forward chain of the bf16 backward pass on the map kernel's producer and
+// consumer wavefronts (d = 64 or 128): from each segment's start state (s_start,
+// [segment][batch*head][d][d] fp32, or NULL for zero), it writes every chunk's
+// saved operands into the backward workspace's chunk area ws_b
+// ([batch*head][chunk] of BwdChunkWs<d>::WSC elements).
+hipError_t launch_chunk_save(int B, int T, int H, int d, const SegPlan& plan, const void* k, const void* v,
+                             const float* theta, const float* beta, const float* s_start, void* ws_b,
+                             hipStream_t stream);
+
 // Output pass of a segmented bf16 prefill with producer and consumer
 // wavefronts (d = 32, 64 or 128: chunk_out_supported): o from each segment's
 // start state in ws_start and each chunk's T' in ws_t, scaled by the output gate

@@ -20,14 +20,20 @@
 // barriers.  A producer lane owns one channel pair of its chunk for all its
 // tokens (all 16 when d_k = 128), so the in-chunk prefix of the log-decay stays
 // inside the lane; its next chunk's inputs are loaded while it forms A and T'.
+//
+// SAVE mode (bf16, d = 64 and 128) serves the backward pass: the same chain, not
+// widened, from each segment's given start state, writing for every chunk the
+// operands the backward sweep reads (kda_launch.hpp, BwdChunkWs): the start state
+// of every even chunk of the segment as row-product operand fragments, U, T^T,
+// and the Kend and Gamma_C an odd chunk's state is formed from.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
-template <typename E, int D>
+template <typename E, int D, bool SAVE = false>
 struct MapCfg {
-    static constexpr int NT = D / 8;                      // 16-column tiles of [N | M]
+    static constexpr int NT = SAVE ? D / 16 : D / 8;      // 16-column tiles of [N | M] (SAVE: of S)
     // consumer wavefronts: eight for bf16; four for fp32 (the validation type),
     // whose wider operands need two wavefronts' registers per SIMD
     static constexpr int NCWMAX = sizeof(E) == 2 ? 8 : 4;
@@ -64,10 +70,14 @@ struct MapScratch {
     alignas(16) E km_row[16 * MapCfg<E, D>::LDR];   // K- = K/Gamma     [token][ch]
     alignas(16) float akk_t[16 * 20];               // A^T, fp32        [col][row]
 };
-template <typename E, int D>
+// SAVE: each consumer stages one 16x16 block of its state tile at a time ([row][20],
+// 8-byte aligned rows), to store it as row-product fragments.
+constexpr int SAVE_STG = 4 * 256;   // four 16x16 blocks
+template <typename E, int D, bool SAVE = false>
 struct MapSmem {
-    MapSlot<E, D> slot[2 * MapCfg<E, D>::NPW];
-    MapScratch<E, D> scr[MapCfg<E, D>::NPW];
+    MapSlot<E, D> slot[2 * MapCfg<E, D, SAVE>::NPW];
+    MapScratch<E, D> scr[MapCfg<E, D, SAVE>::NPW];
+    alignas(16) bf16 stg[SAVE ? MapCfg<E, D, SAVE>::NCW * SAVE_STG : 8];
 };
 
 // N elements as 8-byte stores (4-byte when the run is shorter).
@@ -94,18 +104,21 @@ __device__ __forceinline__ void store_run8(E* p, const E* x) {
 __device__ __forceinline__ bf16x8 ld_k16(const bf16* p) { return cat8(ld_b4(p), ld_b4(p + 4)); }
 __device__ __forceinline__ f32x4 ld_k16(const float* p) { return ld_quad(p); }
 
-template <typename E, int D>
-__global__ void __launch_bounds__((64 * MapCfg<E, D>::NW))
+template <typename E, int D, bool SAVE = false>
+__global__ void __launch_bounds__((64 * MapCfg<E, D, SAVE>::NW))
 map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
            const E* __restrict__ k, const E* __restrict__ v, const float* __restrict__ theta,
            const float* __restrict__ beta, float* __restrict__ ws_n, E* __restrict__ ws_m,
-           E* __restrict__ ws_t) {
-    typedef MapCfg<E, D> C;
+           E* __restrict__ ws_t, const float* __restrict__ s_start, bf16* __restrict__ ws_b) {
+    typedef MapCfg<E, D, SAVE> C;
+    typedef BwdChunkWs<D> BW;
+    static_assert(!SAVE || (sizeof(E) == 2 && (D == 64 || D == 128) && C::TPW == 1),
+                  "SAVE: bf16 at d = 64 and 128, one state tile per consumer");
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
     typedef typename MM::PFrag PFrag;
     typedef MapSlot<E, D> Slot;
-    __shared__ MapSmem<E, D> sm;
+    __shared__ MapSmem<E, D, SAVE> sm;
 
     // wave index as a scalar, so that branches on it stay scalar branches
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,7 +131,13 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     const int c1 = min(nchunks, c0 + seg_len);
     const int nsteps = (c1 - c0 + C::NPW - 1) / C::NPW;
     const int tend = min(T, c1 * CHUNK);            // the segment's tokens end here
-    const bool last = seg == nseg - 1;              // publishes T' only
+    const bool last = !SAVE && seg == nseg - 1;     // publishes T' only
+    // SAVE: the backward workspace of chunk m of this sequence, and the resource of its
+    // first `bytes` (none outside the segment: stores through it are dropped)
+    auto bws = [&](int m) { return ws_b + ((int64_t)bh * nchunks + m) * BW::WSC; };
+    auto bws_rsrc = [&](int m, bool on, uint32_t bytes) {
+        return make_rsrc(bws(on ? m : c0), on ? bytes : 0u);
+    };
 
     // zero the padding columns 16 .. LDK-1 of the [.][16] tiles read by ld_k16
     for (int i = tid; i < 2 * C::NPW * (D + 16); i += 64 * C::NW) {
@@ -295,6 +314,23 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 store_run8<E, C::TPL>(&sl.v_col[(ch + 1) * C::LDK + tok0], vb);
             }
             *reinterpret_cast<f32x2*>(&sl.gc[ch]) = f32x2{eCa, eCb};   // token groups write equal values
+            if constexpr (SAVE) {
+                // an even chunk followed by an odd one leaves its Kend (fragments: wavefront
+                // c/16, lane 16 (token group) + c%16, 4 tokens of channel c) and Gamma_C in the
+                // odd chunk's state area
+                const Rsrc rk = bws_rsrc(m + 1, ((m - c0) & 1) == 0 && m + 1 < c1, BW::KE_BYTES + 4u * D);
+#pragma unroll
+                for (int q4 = 0; q4 < C::TPL / 4; ++q4) {
+                    const int gq = tok0 / 4 + q4;
+                    buf_st_quad(bf16x4{kea[4 * q4], kea[4 * q4 + 1], kea[4 * q4 + 2], kea[4 * q4 + 3]}, rk,
+                                (uint32_t)(((ch >> 4) * 64 + gq * 16 + (ch & 15)) * 8));
+                    buf_st_quad(bf16x4{keb[4 * q4], keb[4 * q4 + 1], keb[4 * q4 + 2], keb[4 * q4 + 3]}, rk,
+                                (uint32_t)((((ch + 1) >> 4) * 64 + gq * 16 + ((ch + 1) & 15)) * 8));
+                }
+                typedef uint32_t U2 __attribute__((__vector_size__(8)));
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(U2, f32x2{eCa, eCb}), rk,
+                                                      (int)(BW::GC_OFF + (uint32_t)ch * 4u), 0, 0);
+            }
             load(m + C::NPW);   // in flight while A and T' are formed
             wave_lds_sync();
 
@@ -328,11 +364,25 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             for (int rr = 0; rr < 16; ++rr) sl.t_row[rr * C::LDK + r] = from_f<E>(x[rr] * br);
             load_beta(m + C::NPW);
             wave_lds_sync();
-            // publish T' of chunks inside the segment: lane (g, r) stores T'[r][4g .. 4g+3]
-            const Quad tq = ld_quad(&sl.t_row[r * C::LDK + 4 * g]);
-            const Rsrc rt = make_rsrc(ws_t + ((int64_t)bh * nchunks + m) * 256,
-                                      m < c1 ? 256u * (uint32_t)sizeof(E) : 0u);
-            buf_st_quad(tq, rt, (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E));
+            if constexpr (SAVE) {
+                // T^T row r (column r of T) for the backward sweep; the four lane groups
+                // store equal values
+                typedef uint32_t U4 __attribute__((__vector_size__(16)));
+                const Rsrc rt = bws_rsrc(m, m < c1, (uint32_t)BW::WSC * 2u);
+                const uint32_t o = (uint32_t)(BW::WS_S + BW::WS_U) * 2u + (uint32_t)r * 32u;
+                const bf16x8 t0 = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3],
+                                   (bf16)x[4], (bf16)x[5], (bf16)x[6], (bf16)x[7]};
+                const bf16x8 t1 = {(bf16)x[8], (bf16)x[9], (bf16)x[10], (bf16)x[11],
+                                   (bf16)x[12], (bf16)x[13], (bf16)x[14], (bf16)x[15]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, t0), rt, (int)o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, t1), rt, (int)(o + 16u), 0, 0);
+            } else {
+                // publish T' of chunks inside the segment: lane (g, r) stores T'[r][4g .. 4g+3]
+                const Quad tq = ld_quad(&sl.t_row[r * C::LDK + 4 * g]);
+                const Rsrc rt = make_rsrc(ws_t + ((int64_t)bh * nchunks + m) * 256,
+                                          m < c1 ? 256u * (uint32_t)sizeof(E) : 0u);
+                buf_st_quad(tq, rt, (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E));
+            }
         };
 
         load(c0 + pw);
@@ -349,6 +399,7 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     } else {
         // =================================================================== consumer
         // state tiles: S[jj][t] = rows 16t.., columns 16*(wave + NCW*jj).. of [N | M]
+        // (SAVE: of S, from the segment's start state)
         f32x4 S[C::TPW][C::KT];
 #pragma unroll
         for (int jj = 0; jj < C::TPW; ++jj) {
@@ -356,11 +407,44 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 #pragma unroll
             for (int t = 0; t < C::KT; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    S[jj][t][i] = (jt >= D / 16 && jt - D / 16 == t && 4 * g + i == r) ? 1.0f : 0.0f;
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (SAVE)
+                        S[jj][t][i] = s_start ? s_start[(((int64_t)seg * BH + bh) * D + 16 * t + 4 * g + i) * D + 16 * jt + r]
+                                              : 0.0f;
+                    else
+                        S[jj][t][i] = (jt >= D / 16 && jt - D / 16 == t && 4 * g + i == r) ? 1.0f : 0.0f;
+                }
         }
+        bf16* stg = &sm.stg[SAVE ? wave * SAVE_STG : 0];   // SAVE: this wavefront's staging block
 
-        auto chain = [&](const Slot& sl) {
+        auto chain = [&](const Slot& sl, int m) {
+            if constexpr (SAVE) {
+                // the start state of an even chunk, as row-product fragments: fragment
+                // (channel tile c, block kb, lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3]
+                // and S[16c + rl][32kb + 16 + 4gl ..+3]; this tile fills the 8-byte half
+                // (jt & 1) of the fragments of block jt / 2, one 16x16 block at a time
+                // Blocks go through LDS four at a time; element (row, col) of a block sits at
+                // row * 16 + (col ^ 4 (row / 4)), so that the 8-byte row reads of 16 lanes
+                // meet all 32 banks once.
+                const Rsrc rs = bws_rsrc(m, m < c1 && ((m - c0) & 1) == 0, (uint32_t)BW::WS_S * 2u);
+                const int jt = wave;
+#pragma unroll
+                for (int t0 = 0; t0 < C::KT; t0 += 4) {
+#pragma unroll
+                    for (int t = t0; t < t0 + 4 && t < C::KT; ++t)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            stg[(t - t0) * 256 + (4 * g + i) * 16 + (r ^ (4 * g))] = (bf16)S[0][t][i];
+                    wave_lds_sync();
+#pragma unroll
+                    for (int t = t0; t < t0 + 4 && t < C::KT; ++t) {
+                        // S[16t + r][16jt + 4g ..+3]
+                        const bf16x4 piece = ld_b4(&stg[(t - t0) * 256 + r * 16 + 4 * (g ^ (r >> 2))]);
+                        buf_st_quad(piece, rs, (uint32_t)((((t * (D / 32) + (jt >> 1)) * 64 + g * 16 + r) * 16) + 8 * (jt & 1)));
+                    }
+                    wave_lds_sync();
+                }
+            }
             // Y = V - K+ S   (the M part of the widened state has V = 0)
             f32x4 y[C::TPW];
             BFrag sb[C::TPW * C::KT];
@@ -382,7 +466,15 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             const PFrag tf = ld_k16(&sl.t_row[r * C::LDK + 4 * g]);
             PFrag up[C::TPW];
 #pragma unroll
-            for (int jj = 0; jj < C::TPW; ++jj) up[jj] = MM::to_p(MM::mm16(tf, MM::to_p(y[jj]), f32x4{0, 0, 0, 0}));
+            for (int jj = 0; jj < C::TPW; ++jj) {
+                const f32x4 ua = MM::mm16(tf, MM::to_p(y[jj]), f32x4{0, 0, 0, 0});
+                up[jj] = MM::to_p(ua);
+                if constexpr (SAVE) {   // U of this column tile: [tile][lane][tokens 4g ..], 8 bytes per lane
+                    const Rsrc ru = bws_rsrc(m, m < c1, (uint32_t)BW::WSC * 2u);
+                    buf_st_quad(bf16x4{(bf16)ua[0], (bf16)ua[1], (bf16)ua[2], (bf16)ua[3]}, ru,
+                                (uint32_t)(BW::WS_S * 2 + (wave * 64 + lane) * 8));
+                }
+            }
             // fp32 operands are the state registers themselves: keep the update
             // below from being scheduled into the products above, which would
             // need a second copy of the state
@@ -408,12 +500,12 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 // compiler has been seen to under-count matrix-core wait states
                 // across back-edges
 #pragma unroll
-                for (int pp = 0; pp < C::NPW; ++pp) chain(sm.slot[((s - 1) & 1) * C::NPW + pp]);
+                for (int pp = 0; pp < C::NPW; ++pp) chain(sm.slot[((s - 1) & 1) * C::NPW + pp], c0 + (s - 1) * C::NPW + pp);
             }
             lds_barrier();
         }
 
-        if (!last) {
+        if (!last && !SAVE) {
 #pragma unroll
             for (int jj = 0; jj < C::TPW; ++jj) {
                 const int jt = wave + C::NCW * jj;
@@ -440,8 +532,26 @@ static hipError_t launch_map_t(int B, int H, int T, const SegPlan& p, const void
     const int BH = B * H;
     hipLaunchKernelGGL((map_kernel<E, D>), dim3((unsigned)(BH * p.nseg)), dim3(64 * C::NW), 0, stream,
                        T, H, BH, p.nchunks, p.seg_len, p.nseg, (const E*)k, (const E*)v, theta, beta,
-                       ws_n, (E*)ws_m, (E*)ws_t);
+                       ws_n, (E*)ws_m, (E*)ws_t, (const float*)nullptr, (bf16*)nullptr);
     return hipGetLastError();
+}
+
+hipError_t launch_chunk_save(int B, int T, int H, int d, const SegPlan& p, const void* k, const void* v,
+                             const float* theta, const float* beta, const float* s_start, void* ws_b,
+                             hipStream_t stream) {
+    const int BH = B * H;
+#define KDA_SAVE(D)                                                                                        \
+    hipLaunchKernelGGL((map_kernel<bf16, D, true>), dim3((unsigned)(BH * p.nseg)),                         \
+                       dim3(64 * MapCfg<bf16, D, true>::NW), 0, stream, T, H, BH, p.nchunks, p.seg_len, p.nseg, \
+                       (const bf16*)k, (const bf16*)v, theta, beta, (float*)nullptr, (bf16*)nullptr,        \
+                       (bf16*)nullptr, s_start, (bf16*)ws_b);                                              \
+    return hipGetLastError()
+    switch (d) {
+        case 64: KDA_SAVE(64);
+        case 128: KDA_SAVE(128);
+    }
+#undef KDA_SAVE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan& plan, const void* k,
