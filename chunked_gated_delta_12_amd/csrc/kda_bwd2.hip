@@ -18,33 +18,35 @@
 // need not be kept), then the chain through the decay scalings to K, Q and the
 // chunk-local cumulative log-decay as in kda_bwd.hip.
 //
-// Layout of the work.  One workgroup per (segment, batch, head), D/16
-// wavefronts; wavefront w owns state tile w: columns 16w.. of the state in the
-// column products (the forward state S and the carried gradient dS', rows in
-// accumulator registers), and channels 16w.. in the row products.  Products
-// that contract over the state's columns (dO S^T, Z S^T, U dS'^T) need the
-// state and the carried gradient with the columns as the contraction index:
-// the forward sweep saves the start state in bf16, laid out as the operand
-// fragments the row products load (16 bytes per lane, coalesced), at every
-// other chunk of the segment (the even ones, counted from its first chunk); the
-// carried gradient is copied to LDS in bf16, row-major, at every chunk.
-// The forward sweep also saves U (bf16 rows) and T^T (bf16) of every chunk, so
-// the backward sweep neither runs the state chain nor solves the triangular
-// system, and, for an even chunk followed by an odd one, Kend (bf16) and Gamma_C
-// (fp32) in the odd chunk's unused state area.  The backward sweep forms an odd
-// chunk's start state from the even one before it by one step of the chain,
-//     S_m = Diag(Gamma_C) S_{m-1} + Kend^T U_{m-1}   (chunk m-1's operands),
-// from the very bf16 operands the forward chain used, and keeps S_{m-1} in LDS
-// for the next chunk: half the state traffic, the largest item of the sweep's.
+// Layout of the work.  The forward chain runs first, on the map kernel's
+// producer and consumer wavefronts (kda_map.hip, SAVE mode), and writes for
+// every chunk the operands this kernel reads: the start state in bf16 at every
+// other chunk of the segment (the even ones, counted from its first chunk), laid
+// out as the operand fragments the row products load (16 bytes per lane,
+// coalesced); U (by column tiles) and T^T (bf16) of every chunk; and, for an
+// even chunk followed by an odd one, Kend (bf16) and Gamma_C (fp32) in the odd
+// chunk's unused state area.  So this kernel neither runs the state chain nor
+// solves the triangular system.
 //
-// MODE FULL runs both sweeps over one segment and writes the gradients.  For
-// few long sequences the segments' start states and end gradients come from
-// affine segment maps: the state maps from the forward pass's map kernel
-// (kda_map.hip, which also publishes every chunk's T' = T diag(beta)), the
-// gradient maps from MODE BMAP, the carried-gradient chain over one segment
-// with the gradient widened to [0 | I] (d x 2d) and T' read from there, whose
-// end value [N | M] is stored as the segment's map; the forward pass's combine
-// kernel chains both (the gradient's in reverse segment order).
+// Here one workgroup per (segment, batch, head) runs the backward sweep, D/16
+// wavefronts; wavefront w owns state tile w: columns 16w.. of the carried
+// gradient dS' in the column products (rows in accumulator registers), and
+// channels 16w.. in the row products.  Products that contract over the state's
+// columns (dO S^T, Z S^T, U dS'^T) take the saved state fragments and an LDS copy
+// of dS' (bf16, row-major, every chunk).  An odd chunk's start state is formed
+// from the even one before it by one step of the chain,
+//     S_m = Diag(Gamma_C) S_{m-1} + Kend^T U_{m-1}   (chunk m-1's operands),
+// from the very bf16 operands the forward chain used, and S_{m-1} is kept in LDS
+// for the next chunk: half the state traffic, the largest item of the pass's.
+//
+// MODE BWD is that sweep.  For few long sequences the segments' start states
+// and end gradients come from affine segment maps: the state maps from the
+// forward pass's map kernel (kda_map.hip, which also publishes every chunk's
+// T' = T diag(beta)), the gradient maps from MODE BMAP, the carried-gradient
+// chain over one segment with the gradient widened to [0 | I] (d x 2d) and T'
+// read from there, whose end value [N | M] is stored as the segment's map; the
+// forward pass's combine kernel chains both (the gradient's in reverse segment
+// order).
 #include <type_traits>
 
 #include "kda_device.hpp"
