@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 PEAKS_LIB = os.path.join(HERE, "libkda_peaks.so")
 PEAKS_SOURCES = ["kda_peaks.hip"]
-SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_decode.hip", "kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_bwd.hip", "kda_bwd2.hip"]
+SOURCES = ["kda_api.cpp", "kda_gate.hip", "kda_decode.hip", "kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_bwd.hip", "kda_bwd2.hip", "kda_gmap.hip"]
 ARCH = "gfx950"
 
 

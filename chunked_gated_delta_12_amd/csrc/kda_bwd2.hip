@@ -39,14 +39,11 @@
 // from the very bf16 operands the forward chain used, and S_{m-1} is kept in LDS
 // for the next chunk: half the state traffic, the largest item of the pass's.
 //
-// MODE BWD is that sweep.  For few long sequences the segments' start states
-// and end gradients come from affine segment maps: the state maps from the
-// forward pass's map kernel (kda_map.hip, which also publishes every chunk's
-// T' = T diag(beta)), the gradient maps from MODE BMAP, the carried-gradient
-// chain over one segment with the gradient widened to [0 | I] (d x 2d) and T'
-// read from there, whose end value [N | M] is stored as the segment's map; the
-// forward pass's combine kernel chains both (the gradient's in reverse segment
-// order).
+// For few long sequences the segments' start states and end gradients come from
+// affine segment maps: the state maps from the forward pass's map kernel
+// (kda_map.hip, which also publishes every chunk's T' = T diag(beta)), the
+// gradient maps from kda_gmap.hip; the forward pass's combine kernel chains both
+// (the gradient's in reverse segment order).
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -105,9 +102,6 @@ struct B2Smem {
     float kz[C::NW][16];                 // rowsum(K+ * (Z S^T)) over each wavefront's channels
 };
 
-// BMAP: the gradient map of a segment; BWD: the backward sweep over a segment, from
-// the operands the map kernel's SAVE mode wrote.
-enum { B2_BMAP = 1, B2_BWD = 2 };
 
 __device__ __forceinline__ bf16x4 bq(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
 __device__ __forceinline__ bf16x4 bq4(float a, float b, float c, float d) {
@@ -169,17 +163,16 @@ __device__ __forceinline__ f32x4 small_abt(const bf16* A, const bf16* B, int r, 
     return acc;
 }
 
-template <int D, int MODE>
+template <int D>
 __global__ void __launch_bounds__(B2Cfg<D>::NTHR)
 bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restrict__ q,
             const bf16* __restrict__ k, const bf16* __restrict__ v, const float* __restrict__ theta,
             const float* __restrict__ beta, const bf16* __restrict__ dout,
             const float* __restrict__ Xinit, float* __restrict__ dq, float* __restrict__ dk,
             float* __restrict__ dv, float* __restrict__ dtheta, float* __restrict__ dbeta,
-            float* __restrict__ dS0, bf16* __restrict__ ws, float* __restrict__ maps) {
+            float* __restrict__ dS0, bf16* __restrict__ ws) {
     typedef B2Cfg<D> C;
-    constexpr bool FULL = MODE != B2_BMAP;   // writes the gradients
-    constexpr int NCX = FULL ? 1 : 2;   // column tiles per wavefront (the widened state in the maps)
+    constexpr int NCX = 1;   // column tiles of dS' per wavefront
     constexpr int NT = C::NT, KB = C::KB, LDR = C::LDR, LDK = C::LDK, LS = C::LS;
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr float GMIN2 = G_MIN * LOG2E;
@@ -213,7 +206,6 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         vo2 = vo4 >> 1;
     };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    const bf16x4 zb4 = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
 
     // ------------------------------------------------------------ raw inputs of a chunk
     // lane (g, li) holds tokens 4g .. 4g+3 of element ch; padding tokens read zero
@@ -249,7 +241,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 r.o[i] = buf_ld16(ro, vo2, (uint32_t)i * row2);
             }
         }
-        if constexpr (FULL) {   // v: rowsum(Z * V) in dbeta
+        {   // v: rowsum(Z * V) in dbeta
             const Rsrc rv = make_rsrc(v + base, span * 2u);
 #pragma unroll
             for (int i = 0; i < 4; ++i) r.x[i] = buf_ld16(rv, vo2, (uint32_t)i * row2);
@@ -291,42 +283,17 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         }
     };
 
-    // ------------------------------------------------------------ state registers
-    // S (forward) / X = dS' (backward): tile rt holds rows 16rt + 4g + i of column
-    // tile cx (the widened state's column 16 (w + NT cx) + li in the maps).
+    // ------------------------------------------------------------ carried gradient
+    // X = dS': tile rt holds rows 16rt + 4g + i of column 16w + li.  Its start value
+    // (zero when init is NULL: a resource of size zero).
+    const int nseg = (nchunks + seg_len - 1) / seg_len;
     auto init_state = [&](f32x4 (&Wt)[NT][NCX], const float* init, int64_t off) {
-        // the start value (zero when init is NULL: a resource of size zero)
         const Rsrc ri = make_rsrc(init ? init + off : init, init ? (uint32_t)(D * D * 4) : 0u);
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-            for (int cx = 0; cx < NCX; ++cx)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rt + 4 * g + i;
-                    if constexpr (FULL)
-                        Wt[rt][cx][i] = __builtin_bit_cast(float, buf_ld32(ri, (uint32_t)(row * D + ch) * 4u, 0u));
-                    else
-                        Wt[rt][cx][i] = (cx == 1 && row == ch) ? 1.0f : 0.0f;   // [0 | I]
-                }
-    };
-    // The end value [N | M] of the gradient's map sweep: N fp32 and M bf16, each
-    // [map][batch*head][d][d] (M after the nseg N blocks), stored in reverse segment
-    // order, so that the chain runs forward through the combine kernel as the state
-    // maps' does.
-    const int nseg = (nchunks + seg_len - 1) / seg_len;
-    auto store_map = [&](const f32x4 (&Wt)[NT][NCX]) {
-        const int slot = nseg - 1 - seg;
-        float* mn = maps + ((int64_t)slot * BH + bh) * D * D;
-        bf16* mm = reinterpret_cast<bf16*>(maps + (int64_t)nseg * BH * D * D) + ((int64_t)slot * BH + bh) * D * D;
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t o = (int64_t)(16 * rt + 4 * g + i) * D + ch;
-                mn[o] = Wt[rt][0][i];
-                if constexpr (NCX == 2) mm[o] = (bf16)Wt[rt][NCX - 1][i];
-            }
+            for (int i = 0; i < 4; ++i)
+                Wt[rt][0][i] = __builtin_bit_cast(float, buf_ld32(ri, (uint32_t)((16 * rt + 4 * g + i) * D + ch) * 4u, 0u));
     };
 
     Raw raw = {};
@@ -351,7 +318,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             const bool inside = m >= n_lo && m < n_hi;
             const int mm = inside ? m : n_lo;   // an address inside the workspace either way
             const bf16* wsm = wsh + (int64_t)mm * C::WSC;
-            if constexpr (FULL) {
+            {
                 const bool odd = inside && ((m - n_lo) & 1);
                 const bf16* wsp = odd ? wsm - C::WSC : wsm;
                 const Rsrc rws = make_rsrc(wsp, odd ? (uint32_t)C::WS_S * 2u : 0u);
@@ -367,16 +334,14 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 kep = buf_ld_b4(rke, (uint32_t)lane * 8u, (uint32_t)w * 512u);
                 gcp = __builtin_bit_cast(float, buf_ld32(rke, (uint32_t)ch * 4u, C::GC_OFF));
             }
-            // FULL: T^T, saved by the forward sweep; BMAP: T' = T diag(beta), [batch*head][chunk]
-            // [16][16] as the forward pass's map kernel publishes it.  Lane l loads row l/4,
-            // columns 4(l%4) .. +3; every wavefront loads it and writes the same values.
-            const bf16* tsrc = FULL ? wsm + C::WS_S + C::WS_U : ws + ((int64_t)bh * nchunks + mm) * 256;
-            const Rsrc rt = make_rsrc(tsrc, inside ? 512u : 0u);
+            // T^T, saved by the forward chain: lane l loads row l/4, columns 4(l%4) .. +3;
+            // every wavefront loads it and writes the same values
+            const Rsrc rt = make_rsrc(wsm + C::WS_S + C::WS_U, inside ? 512u : 0u);
             tfn = buf_ld_b4(rt, (uint32_t)lane * 8u, 0u);
         };
         load_raw(n_hi - 1, raw);
         load_saved(n_hi - 1);
-        if constexpr (FULL) {
+        {
             // an even last chunk has no odd chunk after it to leave its state in LDS:
             // fetch it here (zeros through a resource of size zero otherwise)
             const bool even_last = ((n_hi - 1 - n_lo) & 1) == 0;
@@ -397,24 +362,19 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 of[i] = (float)b16_of(raw.o[i]);
-                vf[i] = FULL ? (float)b16_of(raw.x[i]) : 0.0f;
+                vf[i] = (float)b16_of(raw.x[i]);
                 bt[i] = raw.bt[i];
             }
             // tiles of the chunk (the saved U rows and T^T first: their registers are reloaded next)
             // (no branch around registers of pending loads: every thread writes, the
             // duplicates with equal values)
-            if constexpr (FULL) {
+            {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = ufn[i];
                 // U^T of the chunk before (zeros before an even chunk, unused there)
                 *reinterpret_cast<bf16x4*>(&sm.upT[ch * LDK + 4 * g]) = ufp;
             }
-            if constexpr (FULL) {
-                *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
-            } else {   // T'^T = diag(beta) T^T
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.ttT[(4 * (lane & 3) + i) * LDK + (lane >> 2)] = tfn[i];
-            }
+            *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
             load_raw(n - 1, raw);   // in flight during this chunk
             // K+, K-, Q+ and Kend of this lane's channel and tokens (recomputed in the chain rule)
             auto kpv = [&](int i) { return G.kf[i] * G.gam[i]; };
@@ -434,7 +394,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             *reinterpret_cast<bf16x4*>(&sm.kmT[ch * LDK + 4 * g]) = bq4(kmv(0), kmv(1), kmv(2), kmv(3));
             *reinterpret_cast<bf16x4*>(&sm.b.qpT[ch * LDK + 4 * g]) = bq4(qpv(0), qpv(1), qpv(2), qpv(3));
             if (g == 0) sm.gc[ch] = G.gC;
-            if constexpr (FULL) {   // dS' of the chunk's end, row-major, for the products over its columns
+            {   // dS' of the chunk's end, row-major, for the products over its columns
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -442,7 +402,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             }
             lds_barrier();
 
-            if constexpr (FULL) {
+            {
                 // ---- the chunk's start state as row-product fragments
                 bf16* stw = &sm.stash[(w * KB * 64 + lane) * 8];   // this lane's fragments, block kb at +512 kb
                 if ((n - n_lo) & 1) {
@@ -482,7 +442,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 #pragma unroll
             for (int cx = 0; cx < NCX; ++cx) {
                 f32x4 du = zero4;
-                if (cx == 0)   // A_qk^T dO (the M part of the widened gradient has dO = 0)
+                // A_qk^T dO
                     du = mfma_k16(aqT, bq4(of[0], of[1], of[2], of[3]), du);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
@@ -490,12 +450,12 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                     du = mfma_k32(cat8(ld_b4(&sm.ke[o]), ld_b4(&sm.ke[o + 16])),
                                   cat8(bq(X[2 * kb][cx]), bq(X[2 * kb + 1][cx])), du);
                 }
-                // FULL: Z = T^T dU and -dY = -diag(beta) Z; BMAP: -dY = -T'^T dU directly
+                // Z = T^T dU and -dY = -diag(beta) Z
                 const f32x4 z = mfma_k16(ld_b4(&sm.ttT[li * LDK + 4 * g]), bq(du), zero4);
                 f32x4 ndy;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ndy[i] = FULL ? -bt[i] * z[i] : -z[i];
-                if constexpr (FULL) {
+                for (int i = 0; i < 4; ++i) ndy[i] = -bt[i] * z[i];
+                {
                     const Rsrc rdv = make_rsrc(dv + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -504,7 +464,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                         zvp[i] = z[i] * vf[i];
                     }
                 }
-                const bf16x4 ob = cx == 0 ? bq4(of[0], of[1], of[2], of[3]) : zb4;
+                const bf16x4 ob = bq4(of[0], of[1], of[2], of[3]);
                 const bf16x8 bop = cat8(ob, bq(ndy));
 #pragma unroll
                 for (int rt = 0; rt < NT; ++rt) {
@@ -514,11 +474,6 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                     const int o = (16 * rt + li) * LDK + 4 * g;
                     X[rt][cx] = mfma_k32(cat8(ld_b4(&sm.b.qpT[o]), ld_b4(&sm.kpT[o])), bop, X[rt][cx]);
                 }
-            }
-            if constexpr (!FULL) {
-                load_saved(n - 1);
-                lds_barrier();   // before the next chunk overwrites the tiles
-                continue;
             }
             // rowsum(Z * V) over this wavefront's 16 columns
 #pragma unroll
@@ -642,9 +597,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 buf_st32(a, rb, (uint32_t)t * (uint32_t)H * 4u, 0u);
             }
         }
-        if constexpr (!FULL) {
-            store_map(X);
-        } else if (dS0 && seg == 0) {
+        if (dS0 && seg == 0) {
 #pragma unroll
             for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
@@ -678,10 +631,10 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
     float* mapB = mapF + (size_t)nseg * BH * 2 * DD;
     float* Sst = mapB + (size_t)nseg * BH * 2 * DD;    // state at every segment's start
     float* Xen = Sst + (size_t)nseg * BH * DD;         // carried gradient at the segments' ends, reversed
-#define KDA_B2(D, MODE, GRID, XI, MP)                                                                   \
-    hipLaunchKernelGGL((bwd2_kernel<D, MODE>), dim3((unsigned)(GRID)), dim3(B2Cfg<D>::NTHR), 0, stream, T, H, \
+#define KDA_B2(D, GRID, XI)                                                                             \
+    hipLaunchKernelGGL((bwd2_kernel<D>), dim3((unsigned)(GRID)), dim3(B2Cfg<D>::NTHR), 0, stream, T, H,      \
                        BH, nchunks, seg_len, (const bf16*)q, (const bf16*)k, (const bf16*)v, theta, beta,      \
-                       (const bf16*)dout, XI, dq, dk, dv, dtheta, dbeta, dS0, wsb, MP)
+                       (const bf16*)dout, XI, dq, dk, dv, dtheta, dbeta, dS0, wsb)
     SegPlan plan;
     plan.nchunks = nchunks;
     plan.seg_len = seg_len;
@@ -695,18 +648,19 @@ hipError_t launch_chunk_bwd2(int B, int T, int H, int d, int nseg, int seg_len, 
     if (nseg == 1) {                                                                                      \
         hipError_t e = launch_chunk_save(B, T, H, D, plan, k, v, theta, beta, S0, wsb, stream);           \
         if (e != hipSuccess) return e;                                                                    \
-        KDA_B2(D, B2_BWD, BH, dS_T, nullptr);                                                             \
+        KDA_B2(D, BH, dS_T);                                                                              \
     } else {                                                                                              \
         hipError_t e = launch_chunk_map(false, B, T, H, D, plan, k, v, theta, beta, mapF,                  \
                                         mapF + (size_t)nseg * BH * DD, wsb, stream);                      \
         if (e != hipSuccess) return e;                                                                    \
-        KDA_B2(D, B2_BMAP, nseg * BH, nullptr, mapB);                                                     \
+        e = launch_grad_map(B, T, H, D, plan, q, k, theta, dout, wsb, mapB, stream);                    \
+        if (e != hipSuccess) return e;                                                                    \
         e = launch_state_combine(D, BH, nseg, S0, mapF, mapF + (size_t)nseg * BH * DD, Sst, stream);      \
         if (e == hipSuccess)                                                                              \
             e = launch_state_combine(D, BH, nseg, dS_T, mapB, mapB + (size_t)nseg * BH * DD, Xen, stream);  \
         if (e == hipSuccess) e = launch_chunk_save(B, T, H, D, plan, k, v, theta, beta, Sst, wsb, stream); \
         if (e != hipSuccess) return e;                                                                    \
-        KDA_B2(D, B2_BWD, nseg * BH, (const float*)Xen, nullptr);                                         \
+        KDA_B2(D, nseg * BH, (const float*)Xen);                                                          \
     }                                                                                                     \
     return hipGetLastError()
     switch (d) {

@@ -60,6 +60,14 @@ hipError_t launch_chunk_save(int B, int T, int H, int d, const SegPlan& plan, co
                              const float* theta, const float* beta, const float* s_start, void* ws_b,
                              hipStream_t stream);
 
+// Gradient segment maps of the bf16 backward pass (d = 64 or 128): for every segment
+// but the first, the end value [N | M] of the carried-gradient chain over it from
+// [0 | I], in reverse segment order (N fp32, then M bf16 after the nseg N blocks,
+// [map][batch*head][d][d]); T' of every chunk from ws_t ([batch*head][chunk][16][16]).
+hipError_t launch_grad_map(int B, int T, int H, int d, const SegPlan& plan, const void* q, const void* k,
+                           const float* theta, const void* dout, const void* ws_t, float* maps,
+                           hipStream_t stream);
+
 // Output pass of a segmented bf16 prefill with producer and consumer
 // wavefronts (d = 32, 64 or 128: chunk_out_supported): o from each segment's
 // start state in ws_start and each chunk's T' in ws_t, scaled by the output gate

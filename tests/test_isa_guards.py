@@ -51,7 +51,7 @@ def test_no_legacy_16x16x16_bf16_mfma(assembly, src):
 def test_matrix_cores_used_where_expected(assembly, src):
     text, _ = assembly[src]
     n = len(re.findall(r"^\s*v_mfma_f32_16x16x32_bf16", text, flags=re.M))
-    if src in ("kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_bwd2.hip"):
+    if src in ("kda_chunk.hip", "kda_map.hip", "kda_out.hip", "kda_bwd2.hip", "kda_gmap.hip"):
         assert n > 0
     elif src == "kda_bwd.hip":
         # the fp32 backward (fp32 inputs; bf16 at d = 16 and 32) runs on the fp32 matrix cores
