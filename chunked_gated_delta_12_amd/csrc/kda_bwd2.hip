@@ -21,23 +21,27 @@
 // Layout of the work.  The forward chain runs first, on the map kernel's
 // producer and consumer wavefronts (kda_map.hip, SAVE mode), and writes for
 // every chunk the operands this kernel reads: the start state in bf16 at every
-// other chunk of the segment (the even ones, counted from its first chunk), laid
-// out as the operand fragments the row products load (16 bytes per lane,
-// coalesced); U (by column tiles) and T^T (bf16) of every chunk; and, for an
-// even chunk followed by an odd one, Kend (bf16) and Gamma_C (fp32) in the odd
-// chunk's unused state area.  So this kernel neither runs the state chain nor
-// solves the triangular system.
+// CKPT-th chunk of the segment (the checkpoints, counted from its first chunk),
+// laid out as the operand fragments the row products load (16 bytes per lane,
+// coalesced); U (by column tiles) and T^T (bf16) of every chunk; and, in the
+// unused state area of every other chunk, the previous chunk's Kend (bf16) and
+// Gamma_C (fp32).  So this kernel neither runs the state chain over whole
+// segments nor solves the triangular system.
 //
 // Here one workgroup per (segment, batch, head) runs the backward sweep, D/16
 // wavefronts; wavefront w owns state tile w: columns 16w.. of the carried
 // gradient dS' in the column products (rows in accumulator registers), and
 // channels 16w.. in the row products.  Products that contract over the state's
 // columns (dO S^T, Z S^T, U dS'^T) take the saved state fragments and an LDS copy
-// of dS' (bf16, row-major, every chunk).  An odd chunk's start state is formed
-// from the even one before it by one step of the chain,
-//     S_m = Diag(Gamma_C) S_{m-1} + Kend^T U_{m-1}   (chunk m-1's operands),
-// from the very bf16 operands the forward chain used, and S_{m-1} is kept in LDS
-// for the next chunk: half the state traffic, the largest item of the pass's.
+// of dS' (bf16, row-major, every chunk).  The start state of chunk c + r (c a
+// checkpoint, r < CKPT) is rebuilt from the checkpoint's by r steps of the chain,
+//     S_{m+1} = Diag(Gamma_C) S_m + Kend^T U_m   (chunk m's operands),
+// from the very bf16 operands the forward chain used; the checkpoint's state is
+// loaded once per run of CKPT chunks and kept in LDS.  CKPT = 2 halves the state
+// traffic of saving every chunk's (the largest item of the pass's) for one step
+// per two chunks.  The steps sit on the sweep's critical path: with CKPT = 4 (six
+// steps per four chunks) the sweep lost more time than the forward chain's
+// fewer stores saved.
 //
 // For few long sequences the segments' start states and end gradients come from
 // affine segment maps: the state maps from the forward pass's map kernel
@@ -61,12 +65,14 @@ struct B2Cfg {
     static constexpr int LDK = 20;           // bf16 row stride of [.][16] tiles
     static constexpr int LS = 20;            // fp32 row stride of 16x16 tiles
     // workspace of one chunk of one sequence (kda_launch.hpp): the start state as
-    // row-product operand fragments, U rows [16][D], and T^T [16][16]; in the state
-    // area of an odd chunk the previous chunk's Kend as the operand fragments of the
-    // reconstruction step ([wavefront][lane], 4 tokens of one channel, 8 bytes), then
-    // its Gamma_C (fp32 per channel)
+    // row-product operand fragments (checkpoints), U by column tiles, and T^T
+    // [16][16]; in the state area of every other chunk the previous chunk's Kend as
+    // the operand fragments of a rebuild step ([wavefront][lane], 4 tokens of one
+    // channel, 8 bytes), then its Gamma_C (fp32 per channel)
     typedef BwdChunkWs<D> W;
     static constexpr int64_t WS_S = W::WS_S, WS_U = W::WS_U, WSC = W::WSC;
+    static constexpr int CKPT = W::CKPT;      // chunks per saved start state
+    static constexpr int NRB = CKPT - 1;      // most rebuild steps of one chunk
     static constexpr uint32_t KE_BYTES = W::KE_BYTES, GC_OFF = W::GC_OFF;
     static_assert(KE_BYTES == (uint32_t)NW * 64u * 8u, "one 8-byte Kend fragment per lane");
     static_assert(KE_BYTES + 4 * D <= 2 * WS_S, "Kend and Gamma_C fit in a state area");
@@ -91,8 +97,8 @@ struct B2Smem {
         alignas(16) bf16 dO[16 * C::LDR];    // dO [token][column]
         alignas(16) bf16 Z[16 * C::LDR];     // Z = T^T dU [token][column]
     } b;
-    alignas(16) bf16 stash[D * D];       // an even chunk's start-state fragments [w][kb][lane]
-    alignas(16) bf16 upT[D * C::LDK];    // U^T of the chunk before an odd chunk [column][token]
+    alignas(16) bf16 stash[D * D];       // the checkpoint's start-state fragments [w][kb][lane]
+    alignas(16) bf16 upT[C::NRB][D * C::LDK];   // U^T of the chunks a start state is rebuilt from [column][token]
     alignas(16) bf16 ttT[16 * C::LDK];   // T^T (BMAP: T'^T)
     alignas(16) float KK[16 * C::LS];    // K+ K-^T [t][s]
     alignas(16) float dAqk[16 * C::LS];
@@ -306,33 +312,44 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         init_state(X, Xinit, ((int64_t)(nseg - 1 - seg) * BH + bh) * D * D);
         // chunk-saved operands, loaded a chunk ahead with the raw inputs
         bf16x8 sfn[KB];                   // start-state fragments of this lane's channel tile
-        bf16x4 ufn = {}, ufp = {};        // U of tile w, tokens 4g.., column 16w + li (of the chunk; of the one before)
+        bf16x4 ufn = {};                  // U of tile w, tokens 4g.., column 16w + li
         bf16x4 tfn = {};                  // 4 elements of T^T
-        bf16x4 kep = {};                  // Kend of the chunk before (tokens 4g.., channel ch)
-        float gcp = 0.0f;                 // its Gamma_C of channel ch
+        // operands of the rebuild steps of the chunk's start state: step j goes from
+        // chunk c + j to c + j + 1 (c the checkpoint) with chunk c + j's U (tile w, as
+        // ufn), Kend (tokens 4g.., channel ch) and Gamma_C of channel ch
+        bf16x4 ufp[C::NRB], kep[C::NRB];
+        float gcp[C::NRB];
         // chunk m's saved operands (zeros through resources of size zero outside the
-        // segment).  An odd chunk loads the state fragments of the chunk before it, that
-        // chunk's U and the Kend and Gamma_C stored in its own state area; an even chunk
-        // loads no state (the odd chunk after it leaves it in LDS).
+        // segment).  Chunk m = c + r (r < CKPT) needs r rebuild steps from the checkpoint
+        // c.  The first chunk the sweep meets in a run c .. c + CKPT - 1 (its last one,
+        // or the segment's last chunk) loads the checkpoint's state and keeps it in LDS
+        // for the rest of the run; the others load no state.
         auto load_saved = [&](int m) {
             const bool inside = m >= n_lo && m < n_hi;
             const int mm = inside ? m : n_lo;   // an address inside the workspace either way
+            const int r = (mm - n_lo) % C::CKPT;
+            const bool top = inside && (m == n_hi - 1 || r == C::CKPT - 1);
             const bf16* wsm = wsh + (int64_t)mm * C::WSC;
+            const bf16* wsc = wsm - (int64_t)r * C::WSC;   // the checkpoint chunk
             {
-                const bool odd = inside && ((m - n_lo) & 1);
-                const bf16* wsp = odd ? wsm - C::WSC : wsm;
-                const Rsrc rws = make_rsrc(wsp, odd ? (uint32_t)C::WS_S * 2u : 0u);
+                const Rsrc rws = make_rsrc(wsc, top ? (uint32_t)C::WS_S * 2u : 0u);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
                     sfn[kb] = buf_ld_b8(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
                 // U, stored by column tiles: [tile][lane (g, li)][tokens 4g .. 4g+3], 8 bytes per lane
                 const Rsrc ru = make_rsrc(wsm + C::WS_S, inside ? (uint32_t)C::WS_U * 2u : 0u);
                 ufn = buf_ld_b4(ru, (uint32_t)lane * 8u, (uint32_t)w * 512u);
-                const Rsrc rup = make_rsrc(wsp + C::WS_S, odd ? (uint32_t)C::WS_U * 2u : 0u);
-                ufp = buf_ld_b4(rup, (uint32_t)lane * 8u, (uint32_t)w * 512u);
-                const Rsrc rke = make_rsrc(wsm, odd ? C::KE_BYTES + 4u * D : 0u);
-                kep = buf_ld_b4(rke, (uint32_t)lane * 8u, (uint32_t)w * 512u);
-                gcp = __builtin_bit_cast(float, buf_ld32(rke, (uint32_t)ch * 4u, C::GC_OFF));
+#pragma unroll
+                for (int j = 0; j < C::NRB; ++j) {
+                    const bool on = inside && j < r;
+                    // chunk c + j's U; its Kend and Gamma_C in chunk c + j + 1's state area
+                    const bf16* wj = on ? wsc + (int64_t)j * C::WSC : wsc;
+                    const Rsrc rup = make_rsrc(wj + C::WS_S, on ? (uint32_t)C::WS_U * 2u : 0u);
+                    ufp[j] = buf_ld_b4(rup, (uint32_t)lane * 8u, (uint32_t)w * 512u);
+                    const Rsrc rke = make_rsrc(on ? wj + C::WSC : wsc, on ? C::KE_BYTES + 4u * D : 0u);
+                    kep[j] = buf_ld_b4(rke, (uint32_t)lane * 8u, (uint32_t)w * 512u);
+                    gcp[j] = __builtin_bit_cast(float, buf_ld32(rke, (uint32_t)ch * 4u, C::GC_OFF));
+                }
             }
             // T^T, saved by the forward chain: lane l loads row l/4, columns 4(l%4) .. +3;
             // every wavefront loads it and writes the same values
@@ -341,16 +358,6 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         };
         load_raw(n_hi - 1, raw);
         load_saved(n_hi - 1);
-        {
-            // an even last chunk has no odd chunk after it to leave its state in LDS:
-            // fetch it here (zeros through a resource of size zero otherwise)
-            const bool even_last = ((n_hi - 1 - n_lo) & 1) == 0;
-            const Rsrc rls = make_rsrc(wsh + (int64_t)(n_hi - 1) * C::WSC, even_last ? (uint32_t)C::WS_S * 2u : 0u);
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-                *reinterpret_cast<bf16x8*>(&sm.stash[((w * KB + kb) * 64 + lane) * 8]) =
-                    buf_ld_b8(rls, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
-        }
         __builtin_amdgcn_s_waitcnt(0);   // retire the first loads before the loop
         for (int n = n_hi - 1; n >= n_lo; --n) {
             relane();
@@ -371,8 +378,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = ufn[i];
-                // U^T of the chunk before (zeros before an even chunk, unused there)
-                *reinterpret_cast<bf16x4*>(&sm.upT[ch * LDK + 4 * g]) = ufp;
+                // U^T of the chunks of the rebuild steps (zeros for steps the chunk has not)
+#pragma unroll
+                for (int j = 0; j < C::NRB; ++j)
+                    *reinterpret_cast<bf16x4*>(&sm.upT[j][ch * LDK + 4 * g]) = ufp[j];
             }
             *reinterpret_cast<bf16x4*>(&sm.ttT[(lane >> 2) * LDK + 4 * (lane & 3)]) = tfn;
             load_raw(n - 1, raw);   // in flight during this chunk
@@ -403,28 +412,36 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             lds_barrier();
 
             {
-                // ---- the chunk's start state as row-product fragments
+                // ---- the chunk's start state as row-product fragments: the checkpoint's
+                // (loaded by the first chunk of its run to be met, kept in LDS for the rest),
+                // then r steps S_{m+1} = Diag(Gamma_C) S_m + Kend^T U_m (chunk m's operands),
+                // with the state transposed: tile jt of S^T holds value columns
+                // 16jt + 4g + i of channel ch
                 bf16* stw = &sm.stash[(w * KB * 64 + lane) * 8];   // this lane's fragments, block kb at +512 kb
-                if ((n - n_lo) & 1) {
-                    // odd chunk: keep the even chunk's state for the next chunk, then step it,
-                    // S_n = Diag(Gamma_C) S_{n-1} + Kend^T U_{n-1}, with the state transposed:
-                    // tile jt of S^T holds value columns 16jt + 4g + i of channel ch
+                const int r = (n - n_lo) % C::CKPT;
+                if (n == n_hi - 1 || r == C::CKPT - 1) {
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        *reinterpret_cast<bf16x8*>(stw + kb * 512) = sfn[kb];
-                        f32x4 hv[2];
-#pragma unroll
-                        for (int hh = 0; hh < 2; ++hh) {
-                            f32x4 c;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) c[i] = gcp * (float)sfn[kb][4 * hh + i];
-                            hv[hh] = mfma_k16(ld_b4(&sm.upT[(16 * (2 * kb + hh) + li) * LDK + 4 * g]), kep, c);
-                        }
-                        sfn[kb] = cat8(bq(hv[0]), bq(hv[1]));
-                    }
+                    for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<bf16x8*>(stw + kb * 512) = sfn[kb];
                 } else {
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) sfn[kb] = *reinterpret_cast<const bf16x8*>(stw + kb * 512);
+                }
+#pragma unroll
+                for (int j = 0; j < C::NRB; ++j) {
+                    if (j < r) {
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb) {
+                            f32x4 hv[2];
+#pragma unroll
+                            for (int hh = 0; hh < 2; ++hh) {
+                                f32x4 c;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) c[i] = gcp[j] * (float)sfn[kb][4 * hh + i];
+                                hv[hh] = mfma_k16(ld_b4(&sm.upT[j][(16 * (2 * kb + hh) + li) * LDK + 4 * g]), kep[j], c);
+                            }
+                            sfn[kb] = cat8(bq(hv[0]), bq(hv[1]));
+                        }
+                    }
                 }
             }
 
@@ -585,14 +602,17 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 if (li == 0) sm.kz[w][4 * g + i] = s;
             }
             lds_barrier();
-            {   // dbeta = rowsum(dA * KK) + rowsum(Z * V) - rowsum(K+ * (Z S^T)): every thread
-                // forms the value of token tid % 16 and stores it (equal duplicates, no branch)
-                const int t = tid & 15;
-                float a = 0.0f;
-#pragma unroll
-                for (int s = 0; s < CHUNK; ++s) a = fmaf(sm.dA[t * LS + s], sm.KK[t * LS + s], a);
-#pragma unroll
-                for (int x = 0; x < C::NW; ++x) a += sm.zv[x][t] - sm.kz[x][t];
+            if (w < 4) {
+                // dbeta = rowsum(dA * KK) + rowsum(Z * V) - rowsum(K+ * (Z S^T)), on the first
+                // four wavefronts only: they reach the next chunk's first barrier well before
+                // the others, which start that chunk's tiles at once.  Wavefront w forms tokens
+                // 4w .. 4w+3, one per lane group; lane li takes term s = li of each sum, and
+                // the 16 lanes of the group add them up and store the value (equal duplicates).
+                // The next writes of dA, KK, zv and kz follow the next chunk's first barrier.
+                const int t = 4 * w + g;
+                float a = sm.dA[t * LS + li] * sm.KK[t * LS + li];
+                if (li < C::NW) a += sm.zv[li][t] - sm.kz[li][t];
+                a = rowsum16(a);
                 const Rsrc rb = make_rsrc(dbeta + bb + (int64_t)tc * H, (uint32_t)nv * (uint32_t)H * 4u);
                 buf_st32(a, rb, (uint32_t)t * (uint32_t)H * 4u, 0u);
             }

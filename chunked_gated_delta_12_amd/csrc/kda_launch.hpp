@@ -37,13 +37,16 @@ hipError_t launch_chunk_map(bool f32, int B, int T, int H, int d, const SegPlan&
                             void* ws_m, void* ws_t, hipStream_t stream);
 
 // Per-chunk workspace of the bf16 backward pass (one chunk of one sequence), in bf16
-// elements: the start state as row-product operand fragments (even chunks of a
-// segment only), U by 16-column tiles ([d/16][64 lanes (g, li)][tokens 4g ..
-// 4g+3 of column 16 tile + li]), T^T [16][16].  An odd chunk's state area holds the
-// previous chunk's Kend (operand fragments [d/16][64 lanes] x 8 bytes) and Gamma_C
-// (fp32 per channel) instead, at the byte offsets below.
+// elements: the start state as row-product operand fragments (checkpoint chunks
+// only: every CKPT-th chunk of a segment, counted from its first), U by 16-column
+// tiles ([d/16][64 lanes (g, li)][tokens 4g .. 4g+3 of column 16 tile + li]),
+// T^T [16][16].  The state area of every other chunk holds the previous chunk's
+// Kend (operand fragments [d/16][64 lanes] x 8 bytes) and Gamma_C (fp32 per
+// channel) instead, at the byte offsets below: the backward sweep rebuilds a
+// chunk's start state from the checkpoint before it with those and the U's.
 template <int D>
 struct BwdChunkWs {
+    static constexpr int CKPT = 2;
     static constexpr int64_t WS_S = (int64_t)D * D;
     static constexpr int64_t WS_U = 16 * (int64_t)D;
     static constexpr int64_t WSC = WS_S + WS_U + 256;

@@ -24,8 +24,9 @@
 // SAVE mode (bf16, d = 64 and 128) serves the backward pass: the same chain, not
 // widened, from each segment's given start state, writing for every chunk the
 // operands the backward sweep reads (kda_launch.hpp, BwdChunkWs): the start state
-// of every even chunk of the segment as row-product operand fragments, U, T^T,
-// and the Kend and Gamma_C an odd chunk's state is formed from.
+// of every CKPT-th chunk of the segment (the checkpoints) as row-product operand
+// fragments, U and T^T of every chunk, and the Kend and Gamma_C the other chunks'
+// states are rebuilt from.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -315,10 +316,11 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             }
             *reinterpret_cast<f32x2*>(&sl.gc[ch]) = f32x2{eCa, eCb};   // token groups write equal values
             if constexpr (SAVE) {
-                // an even chunk followed by an odd one leaves its Kend (fragments: wavefront
-                // c/16, lane 16 (token group) + c%16, 4 tokens of channel c) and Gamma_C in the
-                // odd chunk's state area
-                const Rsrc rk = bws_rsrc(m + 1, ((m - c0) & 1) == 0 && m + 1 < c1, BW::KE_BYTES + 4u * D);
+                // a chunk whose successor is no checkpoint leaves its Kend (fragments:
+                // wavefront c/16, lane 16 (token group) + c%16, 4 tokens of channel c) and
+                // Gamma_C in that successor's state area
+                const Rsrc rk = bws_rsrc(m + 1, (m - c0) % BW::CKPT != BW::CKPT - 1 && m + 1 < c1,
+                                         BW::KE_BYTES + 4u * D);
 #pragma unroll
                 for (int q4 = 0; q4 < C::TPL / 4; ++q4) {
                     const int gq = tok0 / 4 + q4;
@@ -419,14 +421,14 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
         auto chain = [&](const Slot& sl, int m) {
             if constexpr (SAVE) {
-                // the start state of an even chunk, as row-product fragments: fragment
+                // the start state of a checkpoint chunk, as row-product fragments: fragment
                 // (channel tile c, block kb, lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3]
                 // and S[16c + rl][32kb + 16 + 4gl ..+3]; this tile fills the 8-byte half
                 // (jt & 1) of the fragments of block jt / 2, one 16x16 block at a time
                 // Blocks go through LDS four at a time; element (row, col) of a block sits at
                 // row * 16 + (col ^ 4 (row / 4)), so that the 8-byte row reads of 16 lanes
                 // meet all 32 banks once.
-                const Rsrc rs = bws_rsrc(m, m < c1 && ((m - c0) & 1) == 0, (uint32_t)BW::WS_S * 2u);
+                const Rsrc rs = bws_rsrc(m, m < c1 && (m - c0) % BW::CKPT == 0, (uint32_t)BW::WS_S * 2u);
                 const int jt = wave;
 #pragma unroll
                 for (int t0 = 0; t0 < C::KT; t0 += 4) {
