@@ -425,9 +425,11 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 // (channel tile c, block kb, lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3]
                 // and S[16c + rl][32kb + 16 + 4gl ..+3]; this tile fills the 8-byte half
                 // (jt & 1) of the fragments of block jt / 2, one 16x16 block at a time
-                // Blocks go through LDS four at a time; element (row, col) of a block sits at
-                // row * 16 + (col ^ 4 (row / 4)), so that the 8-byte row reads of 16 lanes
-                // meet all 32 banks once.
+                // Blocks go through LDS four at a time.  Element (row, col) of a block sits
+                // at 16 p(row) + 4 ((col / 4) ^ (row % 4)) + col % 4, p(row) = 4 (row % 4) +
+                // row / 4: the 2-byte writes of lane group g (rows 4g + i) meet banks
+                // 8g .. 8g+7 only, and the 8-byte row reads of 16 lanes meet all 32 banks
+                // once.
                 const Rsrc rs = bws_rsrc(m, m < c1 && (m - c0) % BW::CKPT == 0, (uint32_t)BW::WS_S * 2u);
                 const int jt = wave;
 #pragma unroll
@@ -436,12 +438,12 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                     for (int t = t0; t < t0 + 4 && t < C::KT; ++t)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            stg[(t - t0) * 256 + (4 * g + i) * 16 + (r ^ (4 * g))] = (bf16)S[0][t][i];
+                            stg[(t - t0) * 256 + (4 * i + g) * 16 + (((r >> 2) ^ i) << 2) + (r & 3)] = (bf16)S[0][t][i];
                     wave_lds_sync();
 #pragma unroll
                     for (int t = t0; t < t0 + 4 && t < C::KT; ++t) {
                         // S[16t + r][16jt + 4g ..+3]
-                        const bf16x4 piece = ld_b4(&stg[(t - t0) * 256 + r * 16 + 4 * (g ^ (r >> 2))]);
+                        const bf16x4 piece = ld_b4(&stg[(t - t0) * 256 + (4 * (r & 3) + (r >> 2)) * 16 + ((g ^ (r & 3)) << 2)]);
                         buf_st_quad(piece, rs, (uint32_t)((((t * (D / 32) + (jt >> 1)) * 64 + g * 16 + r) * 16) + 8 * (jt & 1)));
                     }
                     wave_lds_sync();
