@@ -505,6 +505,37 @@ def test_decode_b256_1024_steps_every_sequence(oracle_mod):
     assert worst_o <= 2e-2 and worst_s <= 2e-2
 
 
+def test_decode_streamed_state_b512(oracle_mod):
+    """A state above the last-level cache (B=512, H=16, d=128: 512 MiB) is read and
+    written with the streaming hint.  Four steps of it equal, bit for bit, the same steps
+    run as two calls of B=256 on its halves (plain accesses: the two differ in cache hints
+    only), and match the oracle on 64 sampled sequences."""
+    w = kin.scaled(kin.DECODE_WORKLOADS["decode_b256"], B=512)
+    steps, half = 4, 256
+    note(f"decode streamed state {w}")
+    S, gen = kin.decode_state(w, device=DEV)
+    S_start = S.cpu()
+    tok = kin.decode_token(w, gen, device=DEV, steps=steps)
+    S_halves = [S[:half].clone(), S[half:].clone()]
+    o_all = torch.full((steps, w.B, w.H, w.dv), float("nan"), device=DEV, dtype=torch.bfloat16)
+    o_halves = torch.full_like(o_all, float("nan"))
+    names = ("q", "k", "v", "theta", "beta")
+    for t in range(steps):
+        kda.kda_decode_step(*(tok[n][t] for n in names), S, o=o_all[t])
+        for j in range(2):
+            rows = slice(j * half, (j + 1) * half)
+            kda.kda_decode_step(*(tok[n][t][rows] for n in names), S_halves[j], o=o_halves[t, rows])
+    torch.cuda.synchronize()
+    assert torch.equal(o_all, o_halves)
+    assert torch.equal(S[:half], S_halves[0]) and torch.equal(S[half:], S_halves[1])
+    pick = torch.arange(0, w.B, 8, device=DEV)
+    seq = lambda x: x[:, pick].transpose(0, 1).contiguous().cpu()
+    o_ref, s_ref = oracle_mod.chunk_fwd(*(seq(tok[n]) for n in names), S_start[pick.cpu()])
+    eo, es = rel_err(seq(o_all), o_ref), rel_err(S[pick], s_ref)
+    note(f"  64 sequences: err_o={eo:.3e} err_S={es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
 # ----------------------------------------------------------------------------- decode replays
 @pytest.mark.parametrize("name", ["tiny", "small", "decay_stress", "prefill_64k", "long_memory"])
 def test_decode_replay_matches_oracle(oracle_mod, name):
