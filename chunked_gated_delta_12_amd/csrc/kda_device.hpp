@@ -119,11 +119,16 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes = 0xf
     // dword3 0x00020000: 32-bit data format, the raw-buffer setting for gfx9 parts.
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Cache policy of a buffer access (the builtins' last operand): kCpStream sets the
+// non-temporal ("nt") bit, for data a kernel touches once and nothing reads soon after.
+constexpr int kCpStream = 2;
+template <int CP = 0>
 __device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, CP);
 }
+template <int CP = 0>
 __device__ __forceinline__ f32x2 buf_ld_f2(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+    return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, CP));
 }
 // Four adjacent storage elements as one load.
 template <typename E> struct BufQuad;
@@ -143,13 +148,15 @@ template <> struct BufQuad<float> {
 // Two adjacent storage elements as one load.
 template <typename E> struct BufPair;
 template <> struct BufPair<bf16> {
+    template <int CP = 0>
     static __device__ __forceinline__ bf16x2 ld(Rsrc r, uint32_t voff, uint32_t soff) {
-        return __builtin_bit_cast(bf16x2, buf_ld32(r, voff, soff));
+        return __builtin_bit_cast(bf16x2, buf_ld32<CP>(r, voff, soff));
     }
 };
 template <> struct BufPair<float> {
+    template <int CP = 0>
     static __device__ __forceinline__ f32x2 ld(Rsrc r, uint32_t voff, uint32_t soff) {
-        return buf_ld_f2(r, voff, soff);
+        return buf_ld_f2<CP>(r, voff, soff);
     }
 };
 

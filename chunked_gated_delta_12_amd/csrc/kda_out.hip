@@ -194,10 +194,11 @@ out_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg, int smul, c
 #pragma unroll
             for (int t = 0; t < C::TPL; ++t) {
                 const uint32_t el = (uint32_t)(tok0 + t) * tstr + (uint32_t)ch;
-                th[t] = buf_ld_f2(rth, el * 4u, 0u);
-                kr[t] = BufPair<bf16>::ld(rk, el * 2u, 0u);
-                vr[t] = BufPair<bf16>::ld(rv, el * 2u, 0u);
-                qr[t] = BufPair<bf16>::ld(rq, el * 2u, 0u);
+                // the inputs' last reads: non-temporal
+                th[t] = buf_ld_f2<kCpStream>(rth, el * 4u, 0u);
+                kr[t] = BufPair<bf16>::ld<kCpStream>(rk, el * 2u, 0u);
+                vr[t] = BufPair<bf16>::ld<kCpStream>(rv, el * 2u, 0u);
+                qr[t] = BufPair<bf16>::ld<kCpStream>(rq, el * 2u, 0u);
             }
             const Rsrc rt = make_rsrc(ws_t + ((int64_t)bh * nchunks + m) * 256, m < c1 ? 512u : 0u);
             tl = BufQuad<bf16>::ld(rt, (uint32_t)(r * 16 + 4 * g) * 2u, 0u);
@@ -234,9 +235,9 @@ out_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg, int smul, c
 #pragma unroll
             for (int jj = 0; jj < NUH; ++jj) {
                 if constexpr (UE == 8)
-                    zl[jj] = __builtin_bit_cast(Unit, __builtin_amdgcn_raw_buffer_load_b128(rz, unit_off(jj), 0, 0));
+                    zl[jj] = __builtin_bit_cast(Unit, __builtin_amdgcn_raw_buffer_load_b128(rz, unit_off(jj), 0, kCpStream));
                 else
-                    zl[jj] = __builtin_bit_cast(Unit, __builtin_amdgcn_raw_buffer_load_b64(rz, unit_off(jj), 0, 0));
+                    zl[jj] = __builtin_bit_cast(Unit, __builtin_amdgcn_raw_buffer_load_b64(rz, unit_off(jj), 0, kCpStream));
             }
         };
         auto store_o = [&](int mo, const Slot& sl, bool valid) {
@@ -256,10 +257,11 @@ out_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg, int smul, c
                     val = *reinterpret_cast<const Unit*>(sp);
                 }
                 if constexpr (GATE) val = out_gate<Unit>(val, zl[jj]);
+                // o is written once and not read back here: non-temporal
                 if constexpr (UE == 8)
-                    __builtin_amdgcn_raw_buffer_store_b128(val, ro, unit_off(jj), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(val, ro, unit_off(jj), 0, kCpStream);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b64(val, ro, unit_off(jj), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(val, ro, unit_off(jj), 0, kCpStream);
             }
         };
 
