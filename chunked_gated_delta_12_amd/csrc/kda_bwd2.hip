@@ -118,13 +118,16 @@ __device__ __forceinline__ bf16 b16_of(uint32_t raw) { return __builtin_bit_cast
 __device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
+// the gradients: written once, not read back by this pass (non-temporal)
 __device__ __forceinline__ void buf_st32(float x, Rsrc r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)voff, (int)soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)voff, (int)soff, kCpStream);
 }
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+// CP = kCpStream for the checkpoint states: each lane's own 16 bytes, read once
+template <int CP = 0>
 __device__ __forceinline__ bf16x8 buf_ld_b8(Rsrc r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, CP));
 }
 __device__ __forceinline__ bf16x4 buf_ld_b4(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
@@ -335,7 +338,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 const Rsrc rws = make_rsrc(wsc, top ? (uint32_t)C::WS_S * 2u : 0u);
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
-                    sfn[kb] = buf_ld_b8(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
+                    sfn[kb] = buf_ld_b8<kCpStream>(rws, (uint32_t)lane * 16u, (uint32_t)((w * KB + kb) * 64) * 16u);
                 // U, stored by column tiles: [tile][lane (g, li)][tokens 4g .. 4g+3], 8 bytes per lane
                 const Rsrc ru = make_rsrc(wsm + C::WS_S, inside ? (uint32_t)C::WS_U * 2u : 0u);
                 ufn = buf_ld_b4(ru, (uint32_t)lane * 8u, (uint32_t)w * 512u);
