@@ -9,6 +9,14 @@
 //     T' = (I + A)^-1 diag(beta),   A = StrictLower(diag(beta) K+ K-^T),
 // so that the out kernel forms U = T' (V - K+ S) without a triangular solve.
 //
+// bf16 at d = 128 (the prefill's shape) builds the same map by walking each
+// segment backward: with F_m the chunk's linear part and Z the product of the F's
+// of the chunks already walked (I at the start), N <- N + Z Kend^T T' V and
+// Z <- Z F_m, M = Z at the segment's start.  Only Z is rescaled by the decay and
+// the update of N is 16 deep, so a chunk costs the consumers about half the
+// widened forward chain; and the walk ends on each segment's first chunks, which
+// the out kernel reads first.  The other types and sizes run the forward chain.
+//
 // Wavefront roles.  Everything a chunk needs apart from the state -- the
 // gate, the decay-scaled tiles, A and T' -- is formed by NPW producer
 // wavefronts, one chunk each, into LDS slots.  NCW consumer wavefronts hold
@@ -53,10 +61,15 @@ struct MapCfg {
     static constexpr int TPL = CHUNK / NTG;               // tokens per producer lane
     static_assert(NT % NCW == 0, "state tiles split evenly");
     static_assert(PPL * 2 == D, "one producer wavefront covers all channels");
+    // The map by a backward walk (bf16 at d = 128, not SAVE): see the kernel.  Consumer w
+    // holds rows 16w.. of Z and N; the fp32 A^T tile takes a row stride of 16 (20 otherwise).
+    static constexpr bool REV = !SAVE && sizeof(E) == 2 && D == 128;
+    static constexpr int AKS = REV ? 16 : 20;
+    static_assert(!REV || (NCW == D / 16 && NTG == 1), "backward walk: one row slab per consumer");
 };
 
 // What the consumers read for one chunk.
-template <typename E, int D>
+template <typename E, int D, bool REV = false>
 struct MapSlot {
     typedef MapCfg<E, D> C;
     alignas(16) E kn_row[16 * C::LDR];   // -K+ = -K*Gamma            [token][ch]
@@ -65,19 +78,37 @@ struct MapSlot {
     alignas(16) E t_row[16 * C::LDK];    // T' = (I + A)^-1 diag(beta) [row][k]
     alignas(16) float gc[D];             // Gamma_C per channel
 };
-// Private to one producer wavefront.
+// The backward walk's operands: Kend rows, -K+^T and V^T columns, T'^T.
 template <typename E, int D>
+struct MapSlot<E, D, true> {
+    typedef MapCfg<E, D> C;
+    alignas(16) E ke_row[16 * C::LDR];   // Kend = K*Gamma_C/Gamma     [token][ch]
+    alignas(16) E kn_col[D * C::LDK];    // -K+^T                     [ch][token]
+    alignas(16) E v_col[D * C::LDK];     // V^T                       [ch][token]
+    alignas(16) E tt_row[16 * C::LDK];   // T'^T                      [col][row]
+    alignas(16) float gc[D];             // Gamma_C per channel
+};
+// Private to one producer wavefront.
+template <typename E, int D, bool REV = false>
 struct MapScratch {
     alignas(16) E km_row[16 * MapCfg<E, D>::LDR];   // K- = K/Gamma     [token][ch]
     alignas(16) float akk_t[16 * 20];               // A^T, fp32        [col][row]
+};
+template <typename E, int D>
+struct MapScratch<E, D, true> {
+    alignas(16) E km_row[16 * MapCfg<E, D>::LDR];   // K- = K/Gamma     [token][ch]
+    alignas(16) E kn_row[16 * MapCfg<E, D>::LDR];   // -K+ = -K*Gamma   [token][ch]
+    // A^T, fp32 [col][row]; once T is solved, T' row-major ([row][20] of E) for its publication
+    alignas(16) float akk_t[16 * 16];
 };
 // SAVE: each consumer stages one 16x16 block of its state tile at a time ([row][20],
 // 8-byte aligned rows), to store it as row-product fragments.
 constexpr int SAVE_STG = 4 * 256;   // four 16x16 blocks
 template <typename E, int D, bool SAVE = false>
 struct MapSmem {
-    MapSlot<E, D> slot[2 * MapCfg<E, D, SAVE>::NPW];
-    MapScratch<E, D> scr[MapCfg<E, D, SAVE>::NPW];
+    static constexpr bool REV = MapCfg<E, D, SAVE>::REV;
+    MapSlot<E, D, REV> slot[2 * MapCfg<E, D, SAVE>::NPW];
+    MapScratch<E, D, REV> scr[MapCfg<E, D, SAVE>::NPW];
     alignas(16) bf16 stg[SAVE ? MapCfg<E, D, SAVE>::NCW * SAVE_STG : 8];
 };
 
@@ -118,7 +149,8 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     typedef Ops<E> MM;
     typedef typename MM::BFrag BFrag;
     typedef typename MM::PFrag PFrag;
-    typedef MapSlot<E, D> Slot;
+    constexpr bool REV = C::REV;
+    typedef MapSlot<E, D, REV> Slot;
     __shared__ MapSmem<E, D, SAVE> sm;
 
     // wave index as a scalar, so that branches on it stay scalar branches
@@ -144,7 +176,9 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
     for (int i = tid; i < 2 * C::NPW * (D + 16); i += 64 * C::NW) {
         Slot& sl = sm.slot[i / (D + 16)];
         const int row = i % (D + 16);
-        E* pad = row < D ? &sl.ke_col[row * C::LDK + 16] : &sl.t_row[(row - D) * C::LDK + 16];
+        E* pad;
+        if constexpr (REV) pad = row < D ? &sl.kn_col[row * C::LDK + 16] : &sl.tt_row[(row - D) * C::LDK + 16];
+        else pad = row < D ? &sl.ke_col[row * C::LDK + 16] : &sl.t_row[(row - D) * C::LDK + 16];
 #pragma unroll
         for (int j = 0; j < C::LDK - 16; ++j) pad[j] = from_f<E>(0.0f);
     }
@@ -155,7 +189,7 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         // The producers' chunk is the critical path of every step: let the SIMD
         // issue their instructions first and the consumers' in the gaps.
         __builtin_amdgcn_s_setprio(3);
-        MapScratch<E, D>& scr = sm.scr[pw];
+        MapScratch<E, D, REV>& scr = sm.scr[pw];
         const int p = lane % C::PPL, tg = lane / C::PPL;
         const int ch = 2 * p, tok0 = tg * C::TPL;
         const uint32_t tstr = (uint32_t)(H * D);   // elements between tokens
@@ -170,9 +204,11 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         RawPair kr[C::TPL], vr[C::TPL];
         float bl[4], br;
         auto load = [&](int m) {
-            const int t0 = m * CHUNK;
+            // the backward walk's chunks before the segment read as padding
+            const bool before = REV && m < c0;
+            const int t0 = (before ? c0 : m) * CHUNK;
             // uniform; kept in a scalar register so the resources below stay scalar
-            const uint32_t nv = __builtin_amdgcn_readfirstlane(max(0, min(CHUNK, tend - t0)));
+            const uint32_t nv = __builtin_amdgcn_readfirstlane(before ? 0 : max(0, min(CHUNK, tend - t0)));
             const int64_t base = head_base + (int64_t)t0 * tstr;
             const uint32_t span = nv * tstr;
             const Rsrc rth = make_rsrc(theta + base, span * 4u);
@@ -188,8 +224,9 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
         };
         // beta of the chunk, loaded once the current chunk's beta is used up
         auto load_beta = [&](int m) {
-            const int t0 = m * CHUNK;
-            const uint32_t nv = __builtin_amdgcn_readfirstlane(max(0, min(CHUNK, tend - t0)));
+            const bool before = REV && m < c0;
+            const int t0 = (before ? c0 : m) * CHUNK;
+            const uint32_t nv = __builtin_amdgcn_readfirstlane(before ? 0 : max(0, min(CHUNK, tend - t0)));
             const Rsrc rb = make_rsrc(beta + ((int64_t)b * T + t0) * H + h, nv * (uint32_t)H * 4u);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -202,8 +239,9 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
 
         auto produce = [&](int m, Slot& sl) {
             const int t0 = m * CHUNK;
-            const int nv = max(0, min(CHUNK, tend - t0));
+            const int nv = (REV && m < c0) ? 0 : max(0, min(CHUNK, tend - t0));
             E kea[C::TPL], keb[C::TPL], va[C::TPL], vb[C::TPL];
+            E kna[4], knb[4];   // backward walk: -K+ of the lane's channels, four tokens at a time
             float eCa, eCb;
             if constexpr (C::NTG == 1) {
                 // The lane holds all 16 tokens of its channel pair, so the decay is
@@ -230,7 +268,19 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                     Pa *= gma[t];
                     Pb *= gmb[t];
                     const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);   // zero for padding tokens
-                    store_pair(&sl.kn_row[t * C::LDR + ch], -ka * Pa, -kb * Pb);
+                    if constexpr (REV) {
+                        kna[t & 3] = from_f<E>(-ka * Pa);
+                        knb[t & 3] = from_f<E>(-kb * Pb);
+                        store_pair(&scr.kn_row[t * C::LDR + ch], -ka * Pa, -kb * Pb);
+                        if ((t & 3) == 3) {   // -K+^T columns, tokens t-3 .. t (8-byte aligned)
+                            *reinterpret_cast<bf16x4*>(&sl.kn_col[ch * C::LDK + tok0 + t - 3]) =
+                                bf16x4{kna[0], kna[1], kna[2], kna[3]};
+                            *reinterpret_cast<bf16x4*>(&sl.kn_col[(ch + 1) * C::LDK + tok0 + t - 3]) =
+                                bf16x4{knb[0], knb[1], knb[2], knb[3]};
+                        }
+                    } else {
+                        store_pair(&sl.kn_row[t * C::LDR + ch], -ka * Pa, -kb * Pb);
+                    }
                 }
                 eCa = Pa;
                 eCb = Pb;
@@ -242,6 +292,7 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                     const float ka = to_f(kr[t][0]), kb = to_f(kr[t][1]);
                     const float xa = ka * Qa, xb = kb * Qb;   // Kend, |Kend| <= |k|
                     store_pair(&scr.km_row[t * C::LDR + ch], xa * ia, xb * ib);
+                    if constexpr (REV) store_pair(&sl.ke_row[t * C::LDR + ch], xa, xb);
                     kea[t] = from_f<E>(xa);
                     keb[t] = from_f<E>(xb);
                     va[t] = vr[t][0];
@@ -309,8 +360,10 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 }
             }
             if constexpr (sizeof(E) == 2) {   // bf16: packed runs of the lane's tokens
-                store_run8<E, C::TPL>(&sl.ke_col[ch * C::LDK + tok0], kea);
-                store_run8<E, C::TPL>(&sl.ke_col[(ch + 1) * C::LDK + tok0], keb);
+                if constexpr (!REV) {
+                    store_run8<E, C::TPL>(&sl.ke_col[ch * C::LDK + tok0], kea);
+                    store_run8<E, C::TPL>(&sl.ke_col[(ch + 1) * C::LDK + tok0], keb);
+                }
                 store_run8<E, C::TPL>(&sl.v_col[ch * C::LDK + tok0], va);
                 store_run8<E, C::TPL>(&sl.v_col[(ch + 1) * C::LDK + tok0], vb);
             }
@@ -333,16 +386,19 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(U2, f32x2{eCa, eCb}), rk,
                                                       (int)(BW::GC_OFF + (uint32_t)ch * 4u), 0, 0);
             }
-            load(m + C::NPW);   // in flight while A and T' are formed
+            load(REV ? m - C::NPW : m + C::NPW);   // in flight while A and T' are formed
             wave_lds_sync();
 
             // ---- A = StrictLower(diag(beta) K+ K-^T), transposed: akk_t[col][row]
-            const f32x4 a = MM::template mm_ll<D>(sl.kn_row, C::LDR, scr.km_row, C::LDR,
+            const E* kn_rows;
+            if constexpr (REV) kn_rows = scr.kn_row;
+            else kn_rows = sl.kn_row;
+            const f32x4 a = MM::template mm_ll<D>(kn_rows, C::LDR, scr.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
             f32x4 am;
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (r < 4 * g + i) ? -bl[i] * a[i] : 0.0f;   // beta of row 4g+i
-            *reinterpret_cast<f32x4*>(&scr.akk_t[r * 20 + 4 * g]) = am;
+            *reinterpret_cast<f32x4*>(&scr.akk_t[r * C::AKS + 4 * g]) = am;
             wave_lds_sync();
 
             // ---- T = (I + A)^-1, column j = r per lane (the four lane groups hold
@@ -356,15 +412,27 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 f32x4 col[4];
 #pragma unroll
                 for (int c = s / 4; c < 4; ++c)
-                    col[c] = *reinterpret_cast<const f32x4*>(&scr.akk_t[s * 20 + 4 * c]);
+                    col[c] = *reinterpret_cast<const f32x4*>(&scr.akk_t[s * C::AKS + 4 * c]);
                 const float xs = x[s];
 #pragma unroll
                 for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
             }
-            // T' = T diag(beta): column r scaled by beta_r
+            // T' = T diag(beta): column r scaled by beta_r.  The backward walk's consumers
+            // take T'^T, whose row r is this lane's column (lane group g stores elements
+            // 4g .. 4g+3), and T' itself goes to the publication through the scratch tile
+            // (the solve's reads of akk_t are done: x depends on all of them).
+            E* t_pub;
+            if constexpr (REV) {
+                t_pub = reinterpret_cast<E*>(scr.akk_t);
+                *reinterpret_cast<bf16x4*>(&sl.tt_row[r * C::LDK + 4 * g]) =
+                    bf16x4{(bf16)(x[4 * g] * br), (bf16)(x[4 * g + 1] * br), (bf16)(x[4 * g + 2] * br),
+                           (bf16)(x[4 * g + 3] * br)};
+            } else {
+                t_pub = sl.t_row;
+            }
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) sl.t_row[rr * C::LDK + r] = from_f<E>(x[rr] * br);
-            load_beta(m + C::NPW);
+            for (int rr = 0; rr < 16; ++rr) t_pub[rr * C::LDK + r] = from_f<E>(x[rr] * br);
+            load_beta(REV ? m - C::NPW : m + C::NPW);
             wave_lds_sync();
             if constexpr (SAVE) {
                 // T^T row r (column r of T) for the backward sweep; the four lane groups
@@ -380,24 +448,89 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, t1), rt, (int)(o + 16u), 0, 0);
             } else {
                 // publish T' of chunks inside the segment: lane (g, r) stores T'[r][4g .. 4g+3]
-                const Quad tq = ld_quad(&sl.t_row[r * C::LDK + 4 * g]);
-                const Rsrc rt = make_rsrc(ws_t + ((int64_t)bh * nchunks + m) * 256,
-                                          m < c1 ? 256u * (uint32_t)sizeof(E) : 0u);
+                const Quad tq = ld_quad(&t_pub[r * C::LDK + 4 * g]);
+                const bool inside = m >= c0 && m < c1;
+                const Rsrc rt = make_rsrc(ws_t + ((int64_t)bh * nchunks + (inside ? m : c0)) * 256,
+                                          inside ? 256u * (uint32_t)sizeof(E) : 0u);
                 buf_st_quad(tq, rt, (uint32_t)(r * 16 + 4 * g) * (uint32_t)sizeof(E));
             }
         };
 
-        load(c0 + pw);
-        load_beta(c0 + pw);
+        // step s takes chunk c0 + s NPW + pw, or c1 - 1 - (s NPW + pw) in the backward walk
+        auto chunk_at = [&](int st) { return REV ? c1 - 1 - (st * C::NPW + pw) : c0 + st * C::NPW + pw; };
+        load(chunk_at(0));
+        load_beta(chunk_at(0));
         // Retire the first chunk's loads before the loop: the compiler's
         // wait-counter analysis would otherwise merge them with the loop's own
         // prefetch and wait for everything at the top of every step.
         __builtin_amdgcn_s_waitcnt(0);
         for (int s = 0; s < nsteps; ++s) {
-            produce(c0 + s * C::NPW + pw, sm.slot[(s & 1) * C::NPW + pw]);
+            produce(chunk_at(s), sm.slot[(s & 1) * C::NPW + pw]);
             lds_barrier();
         }
         lds_barrier();   // the consumers' last step
+    } else if constexpr (REV) {
+        // ==================================================== consumer, backward walk
+        // The segment's map is F_{L-1} .. F_0 (chunk m: S -> F_m S + G_m with
+        // F_m = Diag(Gamma_C) - Kend^T T' K+ and G_m = Kend^T T' V).  Walking its chunks
+        // from the last, with Z = F_{L-1} .. F_{m+1} (I at the start) and W = Z Kend^T T':
+        //     N <- N + W V,   Z <- Z Diag(Gamma_C) - W K+,
+        // and at the segment's start M = Z.  Only Z is rescaled by the decay, and W
+        // is 16 columns wide, so a chunk costs about half the widened forward chain.
+        // Consumer w holds rows 16w.. of Z (as Z^T tiles, the operand of Kend Z^T) and
+        // of N: Zt[t], lane (g, r): Z[16w + r][16t + 4g + i]; Nt[j], lane (g, r):
+        // N[16w + 4g + i][16j + r].
+        f32x4 Zt[C::KT], Nt[C::KT];
+#pragma unroll
+        for (int t = 0; t < C::KT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Zt[t][i] = (t == wave && 4 * g + i == r) ? 1.0f : 0.0f;
+                Nt[t][i] = 0.0f;
+            }
+        auto chain_rev = [&](const Slot& sl) {
+            // P = Kend Z^T (tokens x the slab's rows of Z), over all channels
+            BFrag zb[C::KT];
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) zb[t] = MM::to_b(Zt[t]);
+            const f32x4 pz = MM::template mm_la<D>(sl.ke_row, C::LDR, zb, f32x4{0, 0, 0, 0}, r, g);
+            // W^T = T'^T P: lane (g, r) holds W[16w + r][token 4g + i], which is its
+            // operand fragment of W (row r, k = 4g + i) in the next product
+            const f32x4 wt = MM::mm16(ld_k16(&sl.tt_row[r * C::LDK + 4 * g]), MM::to_p(pz), f32x4{0, 0, 0, 0});
+            const bf16x4 wb = MM::to_b(wt);
+            // N <- N + W V
+#pragma unroll
+            for (int j = 0; j < C::KT; ++j)
+                Nt[j] = mfma_k16(wb, ld_b4(&sl.v_col[(16 * j + r) * C::LDK + 4 * g]), Nt[j]);
+            // Z^T <- Diag(Gamma_C) Z^T + (-K+^T) W^T
+            const PFrag wp = MM::pad(wb);
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) {
+                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sl.gc[16 * t + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Zt[t][i] *= gcv[i];
+                Zt[t] = MM::mm16(ld_k16(&sl.kn_col[(16 * t + r) * C::LDK + 4 * g]), wp, Zt[t]);
+            }
+        };
+        for (int s = 0; s <= nsteps; ++s) {
+            if (s > 0 && !last) {
+                // slot pp holds chunk c1 - 1 - ((s - 1) NPW + pp): descending
+#pragma unroll
+                for (int pp = 0; pp < C::NPW; ++pp) chain_rev(sm.slot[((s - 1) & 1) * C::NPW + pp]);
+            }
+            lds_barrier();
+        }
+        if (!last) {
+            // M = Z in the operand type the combine kernel uses, N in fp32,
+            // both [segment][head][row][column]
+            const int64_t rb = ((int64_t)seg * BH + bh) * D;
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) {
+                *reinterpret_cast<bf16x4*>(&ws_m[(rb + 16 * wave + r) * D + 16 * t + 4 * g]) = MM::to_b(Zt[t]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ws_n[(rb + 16 * wave + 4 * g + i) * D + 16 * t + r] = Nt[t][i];
+            }
+        }
     } else {
         // =================================================================== consumer
         // state tiles: S[jj][t] = rows 16t.., columns 16*(wave + NCW*jj).. of [N | M]
