@@ -65,6 +65,27 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---------------------------------------------------------------- lane exchange
+// A wavefront's 64 lanes as four rows of 16.
+
+// Lane N of each row, copied to every lane of that row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_lane(float v) {
+    static_assert(N >= 0 && N < 16, "lane within a row");
+    // every lane has a source lane, so the instruction's old value is never taken
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf,
+                                                              false));
+}
+
+// Row R, copied to all four rows: lane n of every row takes lane n of row R
+// (ds_bpermute: through the LDS crossbar, no memory and no VALU work).
+template <int R>
+__device__ __forceinline__ float row_to_all(float v, int lane) {
+    static_assert(R >= 0 && R < 4, "row of a wavefront");
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((R * 16 + (lane & 15)) * 4,
+                                                                  __builtin_bit_cast(int, v)));
+}
+
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float to_f(float x) { return x; }
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }

@@ -62,9 +62,8 @@ struct MapCfg {
     static_assert(NT % NCW == 0, "state tiles split evenly");
     static_assert(PPL * 2 == D, "one producer wavefront covers all channels");
     // The map by a backward walk (bf16 at d = 128, not SAVE): see the kernel.  Consumer w
-    // holds rows 16w.. of Z and N; the fp32 A^T tile takes a row stride of 16 (20 otherwise).
+    // holds rows 16w.. of Z and N.
     static constexpr bool REV = !SAVE && sizeof(E) == 2 && D == 128;
-    static constexpr int AKS = REV ? 16 : 20;
     static_assert(!REV || (NCW == D / 16 && NTG == 1), "backward walk: one row slab per consumer");
 };
 
@@ -92,14 +91,12 @@ struct MapSlot<E, D, true> {
 template <typename E, int D, bool REV = false>
 struct MapScratch {
     alignas(16) E km_row[16 * MapCfg<E, D>::LDR];   // K- = K/Gamma     [token][ch]
-    alignas(16) float akk_t[16 * 20];               // A^T, fp32        [col][row]
 };
 template <typename E, int D>
 struct MapScratch<E, D, true> {
     alignas(16) E km_row[16 * MapCfg<E, D>::LDR];   // K- = K/Gamma     [token][ch]
     alignas(16) E kn_row[16 * MapCfg<E, D>::LDR];   // -K+ = -K*Gamma   [token][ch]
-    // A^T, fp32 [col][row]; once T is solved, T' row-major ([row][20] of E) for its publication
-    alignas(16) float akk_t[16 * 16];
+    alignas(16) E t_row[16 * MapCfg<E, D>::LDK];    // T', for its publication [row][col]
 };
 // SAVE: each consumer stages one 16x16 block of its state tile at a time ([row][20],
 // 8-byte aligned rows), to store it as row-product fragments.
@@ -135,6 +132,40 @@ __device__ __forceinline__ void store_run8(E* p, const E* x) {
 // meet the zero slots of the register-side operand, so they add exact zeros.
 __device__ __forceinline__ bf16x8 ld_k16(const bf16* p) { return cat8(ld_b4(p), ld_b4(p + 4)); }
 __device__ __forceinline__ f32x4 ld_k16(const float* p) { return ld_quad(p); }
+
+// Row x[i] -= A[4B+i][4B+J] * xj: the coefficient is lane 4B+J of the lane's own row.
+template <int B, int J>
+__device__ __forceinline__ void tri_axpy(float (&x)[4], const float (&am)[4], float xj) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = fmaf(-row_lane<4 * B + J>(am[i]), xj, x[i]);
+}
+
+// One block of four rows of the unit lower triangular solve (I + A) x = e_r, one
+// right-hand side per lane column r.  Lane (g, r) holds x[i] = row 4g+i and
+// am[i] = A[4g+i][r] (zero on and above the diagonal).  Row block B is finished
+// first on its own lanes, then its four values go to every row and the rows below
+// subtract their share.
+template <int B>
+__device__ __forceinline__ void tri_block(float (&x)[4], const float (&am)[4], int g, int lane) {
+    const bool own = g == B;
+    // within the block: A[4B+i][4B+j] is zero for i <= j, so the update of rows
+    // up to j leaves them unchanged; other rows take a zero multiplier
+    tri_axpy<B, 0>(x, am, own ? x[0] : 0.0f);
+    tri_axpy<B, 1>(x, am, own ? x[1] : 0.0f);
+    tri_axpy<B, 2>(x, am, own ? x[2] : 0.0f);
+    if constexpr (B < 3) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = row_to_all<B>(x[j], lane);
+            p[j] = g > B ? p[j] : 0.0f;   // rows above B hold zero coefficients; row B is done
+        }
+        tri_axpy<B, 0>(x, am, p[0]);
+        tri_axpy<B, 1>(x, am, p[1]);
+        tri_axpy<B, 2>(x, am, p[2]);
+        tri_axpy<B, 3>(x, am, p[3]);
+    }
+}
 
 template <typename E, int D, bool SAVE = false>
 __global__ void __launch_bounds__((64 * MapCfg<E, D, SAVE>::NW))
@@ -389,63 +420,48 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
             load(REV ? m - C::NPW : m + C::NPW);   // in flight while A and T' are formed
             wave_lds_sync();
 
-            // ---- A = StrictLower(diag(beta) K+ K-^T), transposed: akk_t[col][row]
+            // ---- A = StrictLower(diag(beta) K+ K-^T): lane (g, r) holds A[4g+i][r]
             const E* kn_rows;
             if constexpr (REV) kn_rows = scr.kn_row;
             else kn_rows = sl.kn_row;
             const f32x4 a = MM::template mm_ll<D>(kn_rows, C::LDR, scr.km_row, C::LDR,
                                                   f32x4{0, 0, 0, 0}, r, g);
-            f32x4 am;
+            float am[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (r < 4 * g + i) ? -bl[i] * a[i] : 0.0f;   // beta of row 4g+i
-            *reinterpret_cast<f32x4*>(&scr.akk_t[r * C::AKS + 4 * g]) = am;
-            wave_lds_sync();
 
-            // ---- T = (I + A)^-1, column j = r per lane (the four lane groups hold
-            // copies), right-looking: once x[s] is final, every later row subtracts
-            // A[row][s] x[s].
-            float x[16];
+            // ---- T = (I + A)^-1 by forward substitution in registers: lane (g, r)
+            // holds rows 4g .. 4g+3 of column r.  A[4g+i][s] is lane s of the
+            // lane's own row; each finished block of four rows is copied to the
+            // rows below it.
+            float x[4];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == r) ? 1.0f : 0.0f;
-#pragma unroll
-            for (int s = 0; s < 15; ++s) {
-                f32x4 col[4];
-#pragma unroll
-                for (int c = s / 4; c < 4; ++c)
-                    col[c] = *reinterpret_cast<const f32x4*>(&scr.akk_t[s * C::AKS + 4 * c]);
-                const float xs = x[s];
-#pragma unroll
-                for (int rr = s + 1; rr < 16; ++rr) x[rr] = fmaf(-col[rr >> 2][rr & 3], xs, x[rr]);
-            }
+            for (int i = 0; i < 4; ++i) x[i] = (4 * g + i == r) ? 1.0f : 0.0f;
+            tri_block<0>(x, am, g, lane);
+            tri_block<1>(x, am, g, lane);
+            tri_block<2>(x, am, g, lane);
+            tri_block<3>(x, am, g, lane);
             // T' = T diag(beta): column r scaled by beta_r.  The backward walk's consumers
-            // take T'^T, whose row r is this lane's column (lane group g stores elements
-            // 4g .. 4g+3), and T' itself goes to the publication through the scratch tile
-            // (the solve's reads of akk_t are done: x depends on all of them).
+            // take T'^T, whose row r is this lane's column, and T' itself goes to the
+            // publication through a tile (rows 4g .. 4g+3 from lane group g).
             E* t_pub;
             if constexpr (REV) {
-                t_pub = reinterpret_cast<E*>(scr.akk_t);
+                t_pub = scr.t_row;
                 *reinterpret_cast<bf16x4*>(&sl.tt_row[r * C::LDK + 4 * g]) =
-                    bf16x4{(bf16)(x[4 * g] * br), (bf16)(x[4 * g + 1] * br), (bf16)(x[4 * g + 2] * br),
-                           (bf16)(x[4 * g + 3] * br)};
+                    bf16x4{(bf16)(x[0] * br), (bf16)(x[1] * br), (bf16)(x[2] * br), (bf16)(x[3] * br)};
             } else {
                 t_pub = sl.t_row;
             }
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) t_pub[rr * C::LDK + r] = from_f<E>(x[rr] * br);
+            for (int i = 0; i < 4; ++i) t_pub[(4 * g + i) * C::LDK + r] = from_f<E>(x[i] * br);
             load_beta(REV ? m - C::NPW : m + C::NPW);
             wave_lds_sync();
             if constexpr (SAVE) {
-                // T^T row r (column r of T) for the backward sweep; the four lane groups
-                // store equal values
-                typedef uint32_t U4 __attribute__((__vector_size__(16)));
+                // T^T row r (column r of T) for the backward sweep: lane group g stores
+                // elements 4g .. 4g+3
                 const Rsrc rt = bws_rsrc(m, m < c1, (uint32_t)BW::WSC * 2u);
-                const uint32_t o = (uint32_t)(BW::WS_S + BW::WS_U) * 2u + (uint32_t)r * 32u;
-                const bf16x8 t0 = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3],
-                                   (bf16)x[4], (bf16)x[5], (bf16)x[6], (bf16)x[7]};
-                const bf16x8 t1 = {(bf16)x[8], (bf16)x[9], (bf16)x[10], (bf16)x[11],
-                                   (bf16)x[12], (bf16)x[13], (bf16)x[14], (bf16)x[15]};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, t0), rt, (int)o, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U4, t1), rt, (int)(o + 16u), 0, 0);
+                const uint32_t o = (uint32_t)(BW::WS_S + BW::WS_U) * 2u + (uint32_t)r * 32u + (uint32_t)g * 8u;
+                buf_st_quad(bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}, rt, o);
             } else {
                 // publish T' of chunks inside the segment: lane (g, r) stores T'[r][4g .. 4g+3]
                 const Quad tq = ld_quad(&t_pub[r * C::LDK + 4 * g]);
