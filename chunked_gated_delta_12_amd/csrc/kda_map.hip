@@ -504,35 +504,67 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 Zt[t][i] = (t == wave && 4 * g + i == r) ? 1.0f : 0.0f;
                 Nt[t][i] = 0.0f;
             }
-        auto chain_rev = [&](const Slot& sl) {
+        // One chunk of the walk: Z^T <- Diag(Gamma_C) Z^T + (-K+^T) W^T with
+        // W = Z Kend^T T'.  Returns W's operand fragment: lane (g, r) holds
+        // W[16w + r][token 4g + i].  The chunk's LDS operands are read ahead of their
+        // products, so that the reads overlap one another and the products instead
+        // of each waiting in turn.
+        auto chain_rev = [&](const Slot& sl) -> bf16x4 {
+            bf16x8 ka[D / 32];   // Kend rows in mm_la's k-map: block kb, slots 32kb + 4g + (0..3, 16..19)
+#pragma unroll
+            for (int kb = 0; kb < D / 32; ++kb) {
+                const bf16* a = &sl.ke_row[r * C::LDR + 32 * kb + 4 * g];
+                ka[kb] = cat8(ld_b4(a), ld_b4(a + 16));
+            }
+            // T'^T row r and the -K+^T rows as 16-byte reads: slots 4..7 hold the
+            // next four tokens (or the zeroed padding columns), which meet the zero
+            // slots of the padded register operand
+            const PFrag tt = ld_k16(&sl.tt_row[r * C::LDK + 4 * g]);
+            f32x4 gcv[C::KT];
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) gcv[t] = *reinterpret_cast<const f32x4*>(&sl.gc[16 * t + 4 * g]);
             // P = Kend Z^T (tokens x the slab's rows of Z), over all channels
             BFrag zb[C::KT];
 #pragma unroll
             for (int t = 0; t < C::KT; ++t) zb[t] = MM::to_b(Zt[t]);
-            const f32x4 pz = MM::template mm_la<D>(sl.ke_row, C::LDR, zb, f32x4{0, 0, 0, 0}, r, g);
-            // W^T = T'^T P: lane (g, r) holds W[16w + r][token 4g + i], which is its
-            // operand fragment of W (row r, k = 4g + i) in the next product
-            const f32x4 wt = MM::mm16(ld_k16(&sl.tt_row[r * C::LDK + 4 * g]), MM::to_p(pz), f32x4{0, 0, 0, 0});
-            const bf16x4 wb = MM::to_b(wt);
-            // N <- N + W V
+            f32x4 pz = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < C::KT; ++j)
-                Nt[j] = mfma_k16(wb, ld_b4(&sl.v_col[(16 * j + r) * C::LDK + 4 * g]), Nt[j]);
-            // Z^T <- Diag(Gamma_C) Z^T + (-K+^T) W^T
+            for (int kb = 0; kb < D / 32; ++kb) pz = mfma_k32(ka[kb], cat8(zb[2 * kb], zb[2 * kb + 1]), pz);
+            PFrag kn[C::KT];
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t) kn[t] = ld_k16(&sl.kn_col[(16 * t + r) * C::LDK + 4 * g]);
+            // Diag(Gamma_C) Z^T while P is formed
+#pragma unroll
+            for (int t = 0; t < C::KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Zt[t][i] *= gcv[t][i];
+            // W^T = T'^T P
+            const f32x4 wt = MM::mm16(tt, MM::to_p(pz), f32x4{0, 0, 0, 0});
+            const bf16x4 wb = MM::to_b(wt);
             const PFrag wp = MM::pad(wb);
 #pragma unroll
-            for (int t = 0; t < C::KT; ++t) {
-                const f32x4 gcv = *reinterpret_cast<const f32x4*>(&sl.gc[16 * t + 4 * g]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Zt[t][i] *= gcv[i];
-                Zt[t] = MM::mm16(ld_k16(&sl.kn_col[(16 * t + r) * C::LDK + 4 * g]), wp, Zt[t]);
-            }
+            for (int t = 0; t < C::KT; ++t) Zt[t] = MM::mm16(kn[t], wp, Zt[t]);
+            return wb;
         };
+        static_assert(C::NPW % 2 == 0, "the walk's chunks pair up for the N update");
         for (int s = 0; s <= nsteps; ++s) {
             if (s > 0 && !last) {
-                // slot pp holds chunk c1 - 1 - ((s - 1) NPW + pp): descending
+                // slot pp holds chunk c1 - 1 - ((s - 1) NPW + pp): descending.
+                // N <- N + W V over two chunks at a time, as one K = 32 product:
+                // slots 0..3 of a lane group are the first chunk's tokens 4g..4g+3,
+                // slots 4..7 the second's, in both operands.
+                const Slot* sp = &sm.slot[((s - 1) & 1) * C::NPW];
 #pragma unroll
-                for (int pp = 0; pp < C::NPW; ++pp) chain_rev(sm.slot[((s - 1) & 1) * C::NPW + pp]);
+                for (int pp = 0; pp < C::NPW; pp += 2) {
+                    const bf16x4 w0 = chain_rev(sp[pp]);
+                    const bf16x4 w1 = chain_rev(sp[pp + 1]);
+                    const bf16x8 wpair = cat8(w0, w1);
+#pragma unroll
+                    for (int j = 0; j < C::KT; ++j) {
+                        const int o = (16 * j + r) * C::LDK + 4 * g;
+                        Nt[j] = mfma_k32(wpair, cat8(ld_b4(&sp[pp].v_col[o]), ld_b4(&sp[pp + 1].v_col[o])), Nt[j]);
+                    }
+                }
             }
             lds_barrier();
         }
