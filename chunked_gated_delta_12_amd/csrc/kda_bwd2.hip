@@ -64,6 +64,8 @@ struct B2Cfg {
     static constexpr int LDR = D + 4;        // bf16 row stride of [16][D] tiles
     static constexpr int LDK = 20;           // bf16 row stride of [.][16] tiles
     static constexpr int LS = 20;            // fp32 row stride of 16x16 tiles
+    static constexpr int LRB = D + 8;        // bf16 row stride of the staged inputs
+    static constexpr int LRF = D + 4;        // fp32 row stride of the staged theta
     // workspace of one chunk of one sequence (kda_launch.hpp): the start state as
     // row-product operand fragments (checkpoints), U by column tiles, and T^T
     // [16][16]; in the state area of every other chunk the previous chunk's Kend as
@@ -106,17 +108,26 @@ struct B2Smem {
     alignas(16) float gc[D];             // Gamma_C per channel
     float zv[C::NW][16];                 // rowsum(Z * V) over each wavefront's columns
     float kz[C::NW][16];                 // rowsum(K+ * (Z S^T)) over each wavefront's channels
+    // the next chunk's inputs, staged row-major: one 16-byte read per thread and tensor
+    // from memory, then each lane reads its channel of tokens 4g .. 4g+3 (rows padded so
+    // that the four lane groups meet different banks)
+    struct {
+        alignas(16) bf16 k[16 * C::LRB];
+        alignas(16) bf16 q[16 * C::LRB];
+        alignas(16) bf16 o[16 * C::LRB];   // dO
+        alignas(16) bf16 v[16 * C::LRB];
+        alignas(16) float th[16 * C::LRF];
+        float bt[16];
+    } in;
+    // each wavefront's gradient block [token][its 16 channels] on its way to one 16-byte
+    // store per lane (rows of 20: the four lane groups' writes meet different banks)
+    alignas(16) float gst[C::NW][16 * 20];
 };
 
 
 __device__ __forceinline__ bf16x4 bq(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]}; }
 __device__ __forceinline__ bf16x4 bq4(float a, float b, float c, float d) {
     return bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-}
-__device__ __forceinline__ bf16 b16_of(uint32_t raw) { return __builtin_bit_cast(bf16, (unsigned short)raw); }
-// per-lane offset voff plus a wave-uniform offset soff (bytes)
-__device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 // the gradients: written once, not read back by this pass (non-temporal)
 __device__ __forceinline__ void buf_st32(float x, Rsrc r, uint32_t voff, uint32_t soff) {
@@ -201,27 +212,26 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     const int64_t bb = (int64_t)b * T * H + h;                       // beta of token 0
     bf16* wsh = ws + (int64_t)bh * nchunks * C::WSC;
     int ch = 16 * w + li;   // this lane's channel (gate, row products) and value column (column products)
-    // byte offsets of element (token 4g, ch) in a [token][H][D] tensor of 4- and 2-byte
-    // elements; token 4g + i adds i rows, a wave-uniform offset
-    uint32_t vo4 = ((uint32_t)(4 * g) * tstr + (uint32_t)ch) * 4u, vo2 = vo4 >> 1;
-    const uint32_t row4 = tstr * 4u, row2 = tstr * 2u;
     auto relane = [&]() {
         int lv = lane;
         asm volatile("" : "+v"(lv));
         g = lv >> 4;
         li = lv & 15;
         ch = 16 * w + li;
-        vo4 = ((uint32_t)(4 * g) * tstr + (uint32_t)ch) * 4u;
-        vo2 = vo4 >> 1;
     };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // ------------------------------------------------------------ raw inputs of a chunk
-    // lane (g, li) holds tokens 4g .. 4g+3 of element ch; padding tokens read zero
+    // The workgroup reads a chunk's k, q, dO, v and theta as 16-byte pieces, one per
+    // thread and tensor (the first half of the wavefronts k and dO, the second q and v),
+    // and beta by token; stage_raw puts them in LDS, where lane (g, li) reads channel ch
+    // of tokens 4g .. 4g+3.  Padding tokens read zero.
     struct Raw {
-        float th[4], bt[4];
-        uint32_t k[4], q[4], x[4], o[4];   // bf16 bits: k, q, v (x), dO (o)
+        u32x4 a, b, c;   // 16 bytes of k or q, of dO or v, of theta
+        float bt;        // beta of token lane % 16
     };
+    const bool hw = w >= C::NW / 2;                          // wave-uniform
+    const int jb = (w % (C::NW / 2)) * 64 + lane;            // piece of a [16][D] bf16 tile
     // Unconditional: a chunk outside the segment (the one after the last, or before the
     // first) reads zeros through resources of size zero, so no load sits under a branch
     // (which would make the compiler wait for every outstanding access at the join).
@@ -231,30 +241,38 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         const uint32_t nv = __builtin_amdgcn_readfirstlane(inside ? max(0, min(CHUNK, T - tm)) : 0);
         const int64_t base = hb + (int64_t)tm * tstr;
         const uint32_t span = nv * tstr;
+        const uint32_t pb = ((uint32_t)(jb / (D / 8)) * tstr + (uint32_t)(jb % (D / 8)) * 8u) * 2u;
+        const uint32_t pt = ((uint32_t)(tid / (D / 4)) * tstr + (uint32_t)(tid % (D / 4)) * 4u) * 4u;
+        const Rsrc ra = make_rsrc((hw ? q : k) + base, span * 2u);
+        const Rsrc rv = make_rsrc((hw ? v : dout) + base, span * 2u);
         const Rsrc rth = make_rsrc(theta + base, span * 4u);
-        const Rsrc rk = make_rsrc(k + base, span * 2u);
         const Rsrc rb = make_rsrc(beta + bb + (int64_t)tm * H, nv * (uint32_t)H * 4u);
-        const uint32_t vb = (uint32_t)(4 * g) * (uint32_t)H * 4u, hrow = (uint32_t)H * 4u;
+        r.a = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)pb, 0, 0);
+        r.b = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)pb, 0, 0);
+        r.c = __builtin_amdgcn_raw_buffer_load_b128(rth, (int)pt, 0, 0);
+        r.bt = __builtin_bit_cast(float, buf_ld32(rb, (uint32_t)(lane & 15) * (uint32_t)H * 4u, 0u));
+    };
+    // Every thread writes (beta: equal duplicates), so that no branch sits around the
+    // registers of loads in flight.
+    auto stage_raw = [&](const Raw& r) {
+        const int eb = (jb / (D / 8)) * C::LRB + (jb % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&(hw ? sm.in.q : sm.in.k)[eb]) = r.a;
+        *reinterpret_cast<u32x4*>(&(hw ? sm.in.v : sm.in.o)[eb]) = r.b;
+        *reinterpret_cast<u32x4*>(&sm.in.th[(tid / (D / 4)) * C::LRF + (tid % (D / 4)) * 4]) = r.c;
+        sm.in.bt[lane & 15] = r.bt;
+    };
+    // A gradient of the chunk, x[i] of token 4g + i and channel ch, as one 16-byte store
+    // per lane: lane l writes channels 16w + 4(l % 4) .. +3 of token l / 4.
+    auto store_grad = [&](const float (&x)[4], Rsrc r) {
+        float* gw = sm.gst[w];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            r.th[i] = __builtin_bit_cast(float, buf_ld32(rth, vo4, (uint32_t)i * row4));
-            r.k[i] = buf_ld16(rk, vo2, (uint32_t)i * row2);
-            r.bt[i] = __builtin_bit_cast(float, buf_ld32(rb, vb, (uint32_t)i * hrow));
-        }
-        {
-            const Rsrc rq = make_rsrc(q + base, span * 2u);
-            const Rsrc ro = make_rsrc(dout + base, span * 2u);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                r.q[i] = buf_ld16(rq, vo2, (uint32_t)i * row2);
-                r.o[i] = buf_ld16(ro, vo2, (uint32_t)i * row2);
-            }
-        }
-        {   // v: rowsum(Z * V) in dbeta
-            const Rsrc rv = make_rsrc(v + base, span * 2u);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r.x[i] = buf_ld16(rv, vo2, (uint32_t)i * row2);
-        }
+        for (int i = 0; i < 4; ++i) gw[(4 * g + i) * 20 + li] = x[i];
+        wave_lds_sync();
+        const f32x4 y = *reinterpret_cast<const f32x4*>(&gw[(lane >> 2) * 20 + 4 * (lane & 3)]);
+        wave_lds_sync();   // read before the next block's writes
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), r,
+                                               (int)(((uint32_t)(lane >> 2) * tstr + (uint32_t)(16 * w + 4 * (lane & 3))) * 4u),
+                                               0, kCpStream);
     };
 
     // ------------------------------------------------------------ the gate of a chunk
@@ -263,11 +281,12 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     struct Gate {
         float gam[4], igam[4], gC, dsg[4], kf[4], qf[4];
     };
-    auto gate = [&](const Raw& r, int nv, Gate& G, bool want_q) {
+    auto gate = [&](int nv, Gate& G, bool want_q) {
         float g2[4], sgv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * r.th[i]));
+            const float th = sm.in.th[(4 * g + i) * C::LRF + ch];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * th));
             sgv[i] = sg;
             g2[i] = (4 * g + i < nv) ? GMIN2 * sg : 0.0f;   // padding tokens do not decay
         }
@@ -287,8 +306,8 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             G.gam[i] = gm;
             G.igam[i] = __builtin_amdgcn_rcpf(gm);   // <= e^80: the bound keeps it finite
             G.dsg[i] = G_MIN * sgv[i] * (1.0f - sgv[i]);
-            G.kf[i] = (float)b16_of(r.k[i]);
-            G.qf[i] = want_q ? (float)b16_of(r.q[i]) : 0.0f;
+            G.kf[i] = (float)sm.in.k[(4 * g + i) * C::LRB + ch];
+            G.qf[i] = want_q ? (float)sm.in.q[(4 * g + i) * C::LRB + ch] : 0.0f;
         }
     };
 
@@ -362,18 +381,20 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         load_raw(n_hi - 1, raw);
         load_saved(n_hi - 1);
         __builtin_amdgcn_s_waitcnt(0);   // retire the first loads before the loop
+        stage_raw(raw);
+        lds_barrier();
         for (int n = n_hi - 1; n >= n_lo; --n) {
             relane();
             const int tc = n * CHUNK;
             const int nv = min(CHUNK, T - tc);
             Gate G;
-            gate(raw, nv, G, true);
+            gate(nv, G, true);
             float of[4], vf[4], bt[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                of[i] = (float)b16_of(raw.o[i]);
-                vf[i] = (float)b16_of(raw.x[i]);
-                bt[i] = raw.bt[i];
+                of[i] = (float)sm.in.o[(4 * g + i) * C::LRB + ch];
+                vf[i] = (float)sm.in.v[(4 * g + i) * C::LRB + ch];
+                bt[i] = sm.in.bt[4 * g + i];
             }
             // tiles of the chunk (the saved U rows and T^T first: their registers are reloaded next)
             // (no branch around registers of pending loads: every thread writes, the
@@ -477,9 +498,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
                 for (int i = 0; i < 4; ++i) ndy[i] = -bt[i] * z[i];
                 {
                     const Rsrc rdv = make_rsrc(dv + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
+                    const float dvv[4] = {-ndy[0], -ndy[1], -ndy[2], -ndy[3]};
+                    store_grad(dvv, rdv);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        buf_st32(-ndy[i], rdv, vo4, (uint32_t)i * row4);
                         sm.b.Z[(4 * g + i) * LDR + ch] = (bf16)z[i];
                         zvp[i] = z[i] * vf[i];
                     }
@@ -569,20 +591,21 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             // cancel to fp32 accuracy only when both sides use the bf16 values the products
             // used, so those parts are multiplied by the rounded K+, K- and Q+.
             auto rb = [](float x) { return (float)(bf16)x; };
-            float dG[4], kes = 0.0f, kzp[4];
+            float dG[4], kes = 0.0f, kzp[4], dkv[4], dqv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t off = (uint32_t)i * row4;
                 const float aks = -bt[i] * zs[i], akp = bt[i] * dak[i];   // dK+: state part, pair part
                 const float gm = G.gam[i], ig = G.igam[i];
-                buf_st32((aks + akp) * gm + amv[i] * ig + aev[i] * (G.gC * ig), rk, vo4, off);
-                buf_st32((aqv[i] + aqp[i]) * gm, rq, vo4, off);
+                dkv[i] = (aks + akp) * gm + amv[i] * ig + aev[i] * (G.gC * ig);
+                dqv[i] = (aqv[i] + aqp[i]) * gm;
                 const float ked = aev[i] * kev(i);
                 kes += ked;
                 const float kpb = rb(kpv(i));
                 dG[i] = aks * kpv(i) + akp * kpb - amv[i] * rb(kmv(i)) + aqv[i] * qpv(i) + aqp[i] * rb(qpv(i)) - ked;
                 kzp[i] = zs[i] * kpb;   // rowsum(K+ * (Z S^T)) with the K+ the forward's Y used
             }
+            store_grad(dkv, rk);
+            store_grad(dqv, rq);
             kes += __shfl_xor(kes, 16);
             kes += __shfl_xor(kes, 32);
             // the chunk's last token also carries the end decay: d(G_C) = sum_t dKend Kend + dGamma_C Gamma_C
@@ -595,15 +618,18 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             }
             const float s1 = __shfl(suf, 16 + li), s2 = __shfl(suf, 32 + li), s3 = __shfl(suf, 48 + li);
             const float later = (g < 1 ? s1 : 0.0f) + (g < 2 ? s2 : 0.0f) + (g < 3 ? s3 : 0.0f);
+            float dth[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                buf_st32((dG[i] + later) * G.dsg[i], rt_, vo4, (uint32_t)i * row4);
+            for (int i = 0; i < 4; ++i) dth[i] = (dG[i] + later) * G.dsg[i];
+            store_grad(dth, rt_);
             // rowsum(K+ * (Z S^T)) over this wavefront's 16 channels
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float s = rowsum16(kzp[i]);
                 if (li == 0) sm.kz[w][4 * g + i] = s;
             }
+            // the previous chunk's inputs (every read of this chunk's is behind the first barrier)
+            stage_raw(raw);
             lds_barrier();
             if (w < 4) {
                 // dbeta = rowsum(dA * KK) + rowsum(Z * V) - rowsum(K+ * (Z S^T)), on the first
