@@ -611,10 +611,15 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                 // row / 4: the 2-byte writes of lane group g (rows 4g + i) meet banks
                 // 8g .. 8g+7 only, and the 8-byte row reads of 16 lanes meet all 32 banks
                 // once.
-                const Rsrc rs = bws_rsrc(m, m < c1 && (m - c0) % BW::CKPT == 0, (uint32_t)BW::WS_S * 2u);
+                // Only checkpoint chunks store.  The step's chunks are unrolled and NPW is a
+                // multiple of CKPT, so this test is a constant in each unrolled copy and the
+                // other chunks carry no staging or stores at all.
+                static_assert(C::NPW % BW::CKPT == 0, "checkpoints at fixed places of a step");
+                const Rsrc rs = bws_rsrc(m, m < c1, (uint32_t)BW::WS_S * 2u);
                 const int jt = wave;
 #pragma unroll
                 for (int t0 = 0; t0 < C::KT; t0 += 4) {
+                    if ((m - c0) % BW::CKPT != 0) break;
 #pragma unroll
                     for (int t = t0; t < t0 + 4 && t < C::KT; ++t)
 #pragma unroll
