@@ -98,15 +98,11 @@ struct MapScratch<E, D, true> {
     alignas(16) E kn_row[16 * MapCfg<E, D>::LDR];   // -K+ = -K*Gamma   [token][ch]
     alignas(16) E t_row[16 * MapCfg<E, D>::LDK];    // T', for its publication [row][col]
 };
-// SAVE: each consumer stages one 16x16 block of its state tile at a time ([row][20],
-// 8-byte aligned rows), to store it as row-product fragments.
-constexpr int SAVE_STG = 4 * 256;   // four 16x16 blocks
 template <typename E, int D, bool SAVE = false>
 struct MapSmem {
     static constexpr bool REV = MapCfg<E, D, SAVE>::REV;
     MapSlot<E, D, REV> slot[2 * MapCfg<E, D, SAVE>::NPW];
     MapScratch<E, D, REV> scr[MapCfg<E, D, SAVE>::NPW];
-    alignas(16) bf16 stg[SAVE ? MapCfg<E, D, SAVE>::NCW * SAVE_STG : 8];
 };
 
 // N elements as 8-byte stores (4-byte when the run is shorter).
@@ -598,41 +594,34 @@ map_kernel(int T, int H, int BH, int nchunks, int seg_len, int nseg,
                         S[jj][t][i] = (jt >= D / 16 && jt - D / 16 == t && 4 * g + i == r) ? 1.0f : 0.0f;
                 }
         }
-        bf16* stg = &sm.stg[SAVE ? wave * SAVE_STG : 0];   // SAVE: this wavefront's staging block
+        // SAVE: the identity as a padded K = 16 operand (lane (g, r): I[4g + i][r])
+        typename MM::PFrag eye{};
+        if constexpr (SAVE)
+            eye = MM::pad(bf16x4{(bf16)(4 * g == r ? 1.0f : 0.0f), (bf16)(4 * g + 1 == r ? 1.0f : 0.0f),
+                                 (bf16)(4 * g + 2 == r ? 1.0f : 0.0f), (bf16)(4 * g + 3 == r ? 1.0f : 0.0f)});
 
         auto chain = [&](const Slot& sl, int m) {
             if constexpr (SAVE) {
-                // the start state of a checkpoint chunk, as row-product fragments: fragment
+                // The start state of a checkpoint chunk, as row-product fragments: fragment
                 // (channel tile c, block kb, lane (gl, rl)) holds S[16c + rl][32kb + 4gl ..+3]
-                // and S[16c + rl][32kb + 16 + 4gl ..+3]; this tile fills the 8-byte half
-                // (jt & 1) of the fragments of block jt / 2, one 16x16 block at a time
-                // Blocks go through LDS four at a time.  Element (row, col) of a block sits
-                // at 16 p(row) + 4 ((col / 4) ^ (row % 4)) + col % 4, p(row) = 4 (row % 4) +
-                // row / 4: the 2-byte writes of lane group g (rows 4g + i) meet banks
-                // 8g .. 8g+7 only, and the 8-byte row reads of 16 lanes meet all 32 banks
-                // once.
+                // and S[16c + rl][32kb + 16 + 4gl ..+3]; this wavefront's tile (columns
+                // 16jt ..) fills the 8-byte half (jt & 1) of the fragments of block jt / 2.
+                // A state tile in accumulator form (lane (g, r): rows 4g + i, column r), taken
+                // as the padded A operand, is its transpose; times the identity it comes back
+                // as an accumulator that holds S[16t + r][16jt + 4g + i] in lane (g, r), this
+                // lane's half fragment.  The bf16 values pass through exactly.
                 // Only checkpoint chunks store.  The step's chunks are unrolled and NPW is a
-                // multiple of CKPT, so this test is a constant in each unrolled copy and the
-                // other chunks carry no staging or stores at all.
+                // multiple of CKPT, so the test is a constant in each unrolled copy.
                 static_assert(C::NPW % BW::CKPT == 0, "checkpoints at fixed places of a step");
-                const Rsrc rs = bws_rsrc(m, m < c1, (uint32_t)BW::WS_S * 2u);
-                const int jt = wave;
+                if ((m - c0) % BW::CKPT == 0) {
+                    const Rsrc rs = bws_rsrc(m, m < c1, (uint32_t)BW::WS_S * 2u);
+                    const int jt = wave;
 #pragma unroll
-                for (int t0 = 0; t0 < C::KT; t0 += 4) {
-                    if ((m - c0) % BW::CKPT != 0) break;
-#pragma unroll
-                    for (int t = t0; t < t0 + 4 && t < C::KT; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            stg[(t - t0) * 256 + (4 * i + g) * 16 + (((r >> 2) ^ i) << 2) + (r & 3)] = (bf16)S[0][t][i];
-                    wave_lds_sync();
-#pragma unroll
-                    for (int t = t0; t < t0 + 4 && t < C::KT; ++t) {
-                        // S[16t + r][16jt + 4g ..+3]
-                        const bf16x4 piece = ld_b4(&stg[(t - t0) * 256 + (4 * (r & 3) + (r >> 2)) * 16 + ((g ^ (r & 3)) << 2)]);
-                        buf_st_quad(piece, rs, (uint32_t)((((t * (D / 32) + (jt >> 1)) * 64 + g * 16 + r) * 16) + 8 * (jt & 1)));
+                    for (int t = 0; t < C::KT; ++t) {
+                        const f32x4 tr = MM::mm16(MM::pad(MM::to_b(S[0][t])), eye, f32x4{0, 0, 0, 0});
+                        buf_st_quad(MM::to_b(tr), rs,
+                                    (uint32_t)((((t * (D / 32) + (jt >> 1)) * 64 + g * 16 + r) * 16) + 8 * (jt & 1)));
                     }
-                    wave_lds_sync();
                 }
             }
             // Y = V - K+ S   (the M part of the widened state has V = 0)
