@@ -200,6 +200,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Wavefronts w and w + NW/2 share a SIMD, and the older one wins its issue
+    // arbitration: the younger half, left as the critical path of every phase, issues
+    // at a raised priority instead.
+    if (w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);
     // Lane-derived indices.  They are re-derived at the top of every chunk from an
     // opaque copy of the lane id (relane), so that the address arithmetic built on
     // them is recomputed inside the loops instead of being hoisted out of them,
