@@ -129,9 +129,9 @@ __device__ __forceinline__ bf16x4 bq(f32x4 x) { return bf16x4{(bf16)x[0], (bf16)
 __device__ __forceinline__ bf16x4 bq4(float a, float b, float c, float d) {
     return bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
 }
-// the gradients: written once, not read back by this pass (non-temporal)
+// one 4-byte value (dbeta of a token)
 __device__ __forceinline__ void buf_st32(float x, Rsrc r, uint32_t voff, uint32_t soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)voff, (int)soff, kCpStream);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)voff, (int)soff, 0);
 }
 typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
@@ -266,7 +266,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         sm.in.bt[lane & 15] = r.bt;
     };
     // A gradient of the chunk, x[i] of token 4g + i and channel ch, as one 16-byte store
-    // per lane: lane l writes channels 16w + 4(l % 4) .. +3 of token l / 4.
+    // per lane: lane l writes channels 16w + 4(l % 4) .. +3 of token l / 4.  A wavefront
+    // fills half of each 128-byte line it touches; the default cache policy lets the two
+    // halves merge before they are written back (the non-temporal hint wrote them apart:
+    // 0.5 GB more per B = 32 call, for no measurable time).
     auto store_grad = [&](const float (&x)[4], Rsrc r) {
         float* gw = sm.gst[w];
 #pragma unroll
@@ -276,7 +279,7 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         wave_lds_sync();   // read before the next block's writes
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, y), r,
                                                (int)(((uint32_t)(lane >> 2) * tstr + (uint32_t)(16 * w + 4 * (lane & 3))) * 4u),
-                                               0, kCpStream);
+                                               0, 0);
     };
 
     // ------------------------------------------------------------ the gate of a chunk
