@@ -129,7 +129,8 @@ __device__ __forceinline__ void store_run8(E* p, const E* x) {
 __device__ __forceinline__ bf16x8 ld_k16(const bf16* p) { return cat8(ld_b4(p), ld_b4(p + 4)); }
 __device__ __forceinline__ f32x4 ld_k16(const float* p) { return ld_quad(p); }
 
-// Row x[i] -= A[4B+i][4B+J] * xj: the coefficient is lane 4B+J of the lane's own row.
+// x[i] -= A[4g+i][4B+J] * xj for the lane's row group g: the coefficient is lane 4B+J of
+// the lane's own row of 16 lanes.
 template <int B, int J>
 __device__ __forceinline__ void tri_axpy(float (&x)[4], const float (&am)[4], float xj) {
 #pragma unroll
