@@ -224,6 +224,34 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
         ch = 16 * w + li;
     };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // Between the lanes' layout and row-major [16][D] tiles on the matrix cores.  A product
+    // with the identity turns an A operand, lane (g, li) holding row li at k-slots
+    // 4g .. 4g+3, into an accumulator, lane (g, r) holding rows 4g .. 4g+3 of column r.
+    // So a 16x16 block formed in the lanes' layout (tokens 4g .. 4g+3 of column li) comes
+    // back as row pieces (row r, columns 4g .. 4g+3: one 8-byte LDS write per lane), and
+    // 8-byte row pieces read from a staged tile come back in the lanes' layout, in fp32.
+    // Two blocks share one A operand, each product taking one of them through the
+    // identity in its half of the k-slots (the other half of B is zero).  bf16 values
+    // pass through exactly.  The matrix cores are idle most of the chunk, and a block
+    // pair costs two 8-byte LDS accesses per lane instead of eight 2-byte ones.
+    const bf16x4 eyeb = bq4(4 * g == li ? 1.0f : 0.0f, 4 * g + 1 == li ? 1.0f : 0.0f,
+                            4 * g + 2 == li ? 1.0f : 0.0f, 4 * g + 3 == li ? 1.0f : 0.0f);
+    const bf16x4 zb4 = bq4(0.0f, 0.0f, 0.0f, 0.0f);
+    // blocks x0, x1 to columns 16w .. of the row-major tiles t0, t1 (rows of stride LDR)
+    auto tr_rows = [&](bf16x4 x0, bf16* t0, bf16x4 x1, bf16* t1) {
+        const bf16x8 a = cat8(x0, x1);
+        const int o = li * LDR + 16 * w + 4 * g;
+        *reinterpret_cast<bf16x4*>(&t0[o]) = bq(mfma_k32(a, cat8(eyeb, zb4), zero4));
+        *reinterpret_cast<bf16x4*>(&t1[o]) = bq(mfma_k32(a, cat8(zb4, eyeb), zero4));
+    };
+    // the other way: columns 16w .. of the staged input tiles t0, t1 (rows of stride LRB),
+    // lane (g, li) getting tokens 4g .. 4g+3 of channel 16w + li
+    auto from_rows = [&](const bf16* t0, const bf16* t1, f32x4& x0, f32x4& x1) {
+        const int o = li * C::LRB + 16 * w + 4 * g;
+        const bf16x8 a = cat8(ld_b4(&t0[o]), ld_b4(&t1[o]));
+        x0 = mfma_k32(a, cat8(eyeb, zb4), zero4);
+        x1 = mfma_k32(a, cat8(zb4, eyeb), zero4);
+    };
 
     // ------------------------------------------------------------ raw inputs of a chunk
     // The workgroup reads a chunk's k, q, dO, v and theta as 16-byte pieces, one per
@@ -290,6 +318,15 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     };
     auto gate = [&](int nv, Gate& G, bool want_q) {
         float g2[4], sgv[4];
+        {
+            f32x4 kf, qf;
+            from_rows(sm.in.k, sm.in.q, kf, qf);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                G.kf[i] = kf[i];
+                G.qf[i] = want_q ? qf[i] : 0.0f;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float th = sm.in.th[(4 * g + i) * C::LRF + ch];
@@ -313,8 +350,6 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             G.gam[i] = gm;
             G.igam[i] = __builtin_amdgcn_rcpf(gm);   // <= e^80: the bound keeps it finite
             G.dsg[i] = G_MIN * sgv[i] * (1.0f - sgv[i]);
-            G.kf[i] = (float)sm.in.k[(4 * g + i) * C::LRB + ch];
-            G.qf[i] = want_q ? (float)sm.in.q[(4 * g + i) * C::LRB + ch] : 0.0f;
         }
     };
 
@@ -397,18 +432,24 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             Gate G;
             gate(nv, G, true);
             float of[4], vf[4], bt[4];
+            {
+                f32x4 o4, v4;
+                from_rows(sm.in.o, sm.in.v, o4, v4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    of[i] = o4[i];
+                    vf[i] = v4[i];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                of[i] = (float)sm.in.o[(4 * g + i) * C::LRB + ch];
-                vf[i] = (float)sm.in.v[(4 * g + i) * C::LRB + ch];
                 bt[i] = sm.in.bt[4 * g + i];
             }
-            // tiles of the chunk (the saved U rows and T^T first: their registers are reloaded next)
+            // tiles of the chunk (the saved rebuild operands and T^T first: their registers are
+            // reloaded next; U goes with dO below)
             // (no branch around registers of pending loads: every thread writes, the
             // duplicates with equal values)
             {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.U[(4 * g + i) * LDR + ch] = ufn[i];
                 // U^T of the chunks of the rebuild steps (zeros for steps the chunk has not)
 #pragma unroll
                 for (int j = 0; j < C::NRB; ++j)
@@ -421,24 +462,22 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             auto kmv = [&](int i) { return G.kf[i] * G.igam[i]; };
             auto qpv = [&](int i) { return G.qf[i] * G.gam[i]; };
             auto kev = [&](int i) { return G.kf[i] * (G.gC * G.igam[i]); };
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * g + i;
-                sm.kp[t * LDR + ch] = (bf16)kpv(i);
-                sm.km[t * LDR + ch] = (bf16)kmv(i);
-                sm.ke[t * LDR + ch] = (bf16)kev(i);
-                sm.b.qp[t * LDR + ch] = (bf16)qpv(i);
-                sm.b.dO[t * LDR + ch] = (bf16)of[i];
+            {
+                const bf16x4 kpb = bq4(kpv(0), kpv(1), kpv(2), kpv(3));
+                const bf16x4 kmb = bq4(kmv(0), kmv(1), kmv(2), kmv(3));
+                const bf16x4 qpb = bq4(qpv(0), qpv(1), qpv(2), qpv(3));
+                tr_rows(kpb, sm.kp, kmb, sm.km);
+                tr_rows(bq4(kev(0), kev(1), kev(2), kev(3)), sm.ke, qpb, sm.b.qp);
+                tr_rows(bq4(of[0], of[1], of[2], of[3]), sm.b.dO, ufn, sm.U);
+                *reinterpret_cast<bf16x4*>(&sm.kpT[ch * LDK + 4 * g]) = kpb;
+                *reinterpret_cast<bf16x4*>(&sm.kmT[ch * LDK + 4 * g]) = kmb;
+                *reinterpret_cast<bf16x4*>(&sm.b.qpT[ch * LDK + 4 * g]) = qpb;
             }
-            *reinterpret_cast<bf16x4*>(&sm.kpT[ch * LDK + 4 * g]) = bq4(kpv(0), kpv(1), kpv(2), kpv(3));
-            *reinterpret_cast<bf16x4*>(&sm.kmT[ch * LDK + 4 * g]) = bq4(kmv(0), kmv(1), kmv(2), kmv(3));
-            *reinterpret_cast<bf16x4*>(&sm.b.qpT[ch * LDK + 4 * g]) = bq4(qpv(0), qpv(1), qpv(2), qpv(3));
             if (g == 0) sm.gc[ch] = G.gC;
             {   // dS' of the chunk's end, row-major, for the products over its columns
 #pragma unroll
-                for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sm.u.Xs[(16 * rt + 4 * g + i) * LDR + ch] = (bf16)X[rt][0][i];
+                for (int rt = 0; rt < NT; rt += 2)
+                    tr_rows(bq(X[rt][0]), &sm.u.Xs[16 * rt * LDR], bq(X[rt + 1][0]), &sm.u.Xs[16 * (rt + 1) * LDR]);
             }
             lds_barrier();
 
