@@ -103,7 +103,9 @@ struct B2Smem {
     alignas(16) bf16 upT[C::NRB][D * C::LDK];   // U^T of the chunks a start state is rebuilt from [column][token]
     alignas(16) bf16 ttT[16 * C::LDK];   // T^T (BMAP: T'^T)
     alignas(16) float KK[16 * C::LS];    // K+ K-^T [t][s]
-    alignas(16) float dAqk[16 * C::LS];
+    // dA_qk and dA as the bf16 operand fragments of the chain rule's products, [lane][4]:
+    // dA_qk^T, dA_qk, (diag(beta) dA)^T, dA
+    alignas(16) bf16 fq[4][64 * 4];
     alignas(16) float dA[16 * C::LS];
     alignas(16) float gc[D];             // Gamma_C per channel
     float zv[C::NW][16];                 // rowsum(Z * V) over each wavefront's columns
@@ -573,7 +575,10 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 
             // ---- dA_qk = LowerIncl(dO U^T) (wave 0), dA = StrictLower(-Z U^T) (wave 1),
             // KK = K+ K-^T (wave 2, for dbeta); everyone: the row products over the state's
-            // columns, dO S^T, U dS'^T and Z S^T, and dGamma_C = rowsum(dS' * S)
+            // columns, dO S^T, U dS'^T and Z S^T, and dGamma_C = rowsum(dS' * S).  Waves 0
+            // and 1 leave dA_qk and dA as the bf16 fragments every wave's chain-rule products
+            // load (lane (g, li) of the accumulator holds row 4g + i of column li, the
+            // transposed operand; the operand itself comes through the identity product)
             if (w == 2) {
                 const f32x4 kk = small_abt<D>(sm.kp, sm.km, li, g);
 #pragma unroll
@@ -581,13 +586,25 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
             }
             if (w == 0) {
                 const f32x4 x = small_abt<D>(sm.b.dO, sm.U, li, g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.dAqk[(4 * g + i) * LS + li] = (li <= 4 * g + i) ? x[i] : 0.0f;
+                const bf16x4 xb = bq4(li <= 4 * g ? x[0] : 0.0f, li <= 4 * g + 1 ? x[1] : 0.0f,
+                                      li <= 4 * g + 2 ? x[2] : 0.0f, li <= 4 * g + 3 ? x[3] : 0.0f);
+                *reinterpret_cast<bf16x4*>(&sm.fq[0][(16 * g + li) * 4]) = xb;
+                *reinterpret_cast<bf16x4*>(&sm.fq[1][(16 * g + li) * 4]) =
+                    bq(mfma_k32(cat8(xb, xb), cat8(eyeb, zb4), zero4));
             }
             if (w == 1) {
                 const f32x4 x = small_abt<D>(sm.b.Z, sm.U, li, g);
+                float da[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.dA[(4 * g + i) * LS + li] = (li < 4 * g + i) ? -x[i] : 0.0f;
+                for (int i = 0; i < 4; ++i) {
+                    da[i] = (li < 4 * g + i) ? -x[i] : 0.0f;
+                    sm.dA[(4 * g + i) * LS + li] = da[i];
+                }
+                const bf16x4 db = bq4(da[0], da[1], da[2], da[3]);
+                *reinterpret_cast<bf16x4*>(&sm.fq[2][(16 * g + li) * 4]) =
+                    bq4(bt[0] * da[0], bt[1] * da[1], bt[2] * da[2], bt[3] * da[3]);
+                *reinterpret_cast<bf16x4*>(&sm.fq[3][(16 * g + li) * 4]) =
+                    bq(mfma_k32(cat8(db, db), cat8(eyeb, zb4), zero4));
             }
             f32x4 zs = zero4, aqv = zero4, aev = zero4;
             float dgc = 0.0f;
@@ -610,25 +627,12 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
 
             // ---- the rest of the row products and the chain rule; lane (g, li): channel ch, tokens 4g+i
             const bf16x4 kmb = ld_b4(&sm.kmT[ch * LDK + 4 * g]);
-            f32x4 aqp;
-            {
-                const f32x4 daq = *reinterpret_cast<const f32x4*>(&sm.dAqk[li * LS + 4 * g]);
-                aqp = mfma_k16(bq(daq), kmb, zero4);                     // dA_qk K-
-            }
-            f32x4 dak;
-            {
-                const f32x4 da = *reinterpret_cast<const f32x4*>(&sm.dA[li * LS + 4 * g]);
-                dak = mfma_k16(bq(da), kmb, zero4);                      // dA K-
-            }
+            const int fo = (16 * g + li) * 4;
+            const f32x4 aqp = mfma_k16(ld_b4(&sm.fq[1][fo]), kmb, zero4);   // dA_qk K-
+            const f32x4 dak = mfma_k16(ld_b4(&sm.fq[3][fo]), kmb, zero4);   // dA K-
             const bf16x8 qk = cat8(ld_b4(&sm.b.qpT[ch * LDK + 4 * g]), ld_b4(&sm.kpT[ch * LDK + 4 * g]));
-            f32x4 amv;
-            {
-                const bf16x4 a0 = bq4(sm.dAqk[(4 * g + 0) * LS + li], sm.dAqk[(4 * g + 1) * LS + li],
-                                      sm.dAqk[(4 * g + 2) * LS + li], sm.dAqk[(4 * g + 3) * LS + li]);
-                const bf16x4 a1 = bq4(bt[0] * sm.dA[(4 * g + 0) * LS + li], bt[1] * sm.dA[(4 * g + 1) * LS + li],
-                                      bt[2] * sm.dA[(4 * g + 2) * LS + li], bt[3] * sm.dA[(4 * g + 3) * LS + li]);
-                amv = mfma_k32(cat8(a0, a1), qk, zero4);                 // dA_qk^T Q+ + (diag(beta) dA)^T K+
-            }
+            // dA_qk^T Q+ + (diag(beta) dA)^T K+
+            const f32x4 amv = mfma_k32(cat8(ld_b4(&sm.fq[0][fo]), ld_b4(&sm.fq[2][fo])), qk, zero4);
             const Rsrc rq = make_rsrc(dq + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
             const Rsrc rk = make_rsrc(dk + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
             const Rsrc rt_ = make_rsrc(dtheta + hb + (int64_t)tc * tstr, (uint32_t)nv * tstr * 4u);
