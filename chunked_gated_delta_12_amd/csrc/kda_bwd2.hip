@@ -111,8 +111,9 @@ struct B2Smem {
     float zv[C::NW][16];                 // rowsum(Z * V) over each wavefront's columns
     float kz[C::NW][16];                 // rowsum(K+ * (Z S^T)) over each wavefront's channels
     // the next chunk's inputs, staged row-major: one 16-byte read per thread and tensor
-    // from memory, then each lane reads its channel of tokens 4g .. 4g+3 (rows padded so
-    // that the four lane groups meet different banks)
+    // from memory; each lane then takes its channel of tokens 4g .. 4g+3, theta by 4-byte
+    // reads (rows padded so that the four lane groups meet different banks) and the bf16
+    // tensors by 8-byte row reads through the identity product
     struct {
         alignas(16) bf16 k[16 * C::LRB];
         alignas(16) bf16 q[16 * C::LRB];
@@ -258,8 +259,8 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     // ------------------------------------------------------------ raw inputs of a chunk
     // The workgroup reads a chunk's k, q, dO, v and theta as 16-byte pieces, one per
     // thread and tensor (the first half of the wavefronts k and dO, the second q and v),
-    // and beta by token; stage_raw puts them in LDS, where lane (g, li) reads channel ch
-    // of tokens 4g .. 4g+3.  Padding tokens read zero.
+    // and beta by token; stage_raw puts them in LDS, from where lane (g, li) takes channel
+    // ch of tokens 4g .. 4g+3.  Padding tokens read zero.
     struct Raw {
         u32x4 a, b, c;   // 16 bytes of k or q, of dO or v, of theta
         float bt;        // beta of token lane % 16
