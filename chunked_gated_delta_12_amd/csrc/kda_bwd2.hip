@@ -207,24 +207,25 @@ bwd2_kernel(int T, int H, int BH, int nchunks, int seg_len, const bf16* __restri
     // arbitration: the younger half, left as the critical path of every phase, issues
     // at a raised priority instead.
     if (w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);
-    // Lane-derived indices.  They are re-derived at the top of every chunk from an
-    // opaque copy of the lane id (relane), so that the address arithmetic built on
-    // them is recomputed inside the loops instead of being hoisted out of them,
-    // which would keep dozens of loop-invariant address registers alive.
-    int g = lane >> 4, li = lane & 15;
+    // Lane-derived indices.  The lane group g is re-derived at the top of every chunk
+    // from an opaque copy of the lane id (relane), so that the address arithmetic built
+    // on it is recomputed inside the loop instead of being hoisted out of it, which would
+    // keep dozens of loop-invariant address registers alive (with g, li and ch all
+    // hoisted the kernel needs 256 VGPRs and spills).  The addresses that depend on the
+    // column li and channel ch alone stay hoisted: 220 VGPRs, no scratch.
+    int g = lane >> 4;
+    const int li = lane & 15;
     const int bh = blockIdx.x % BH, seg = blockIdx.x / BH, b = bh / H, h = bh % H;
     const int n_lo = seg * seg_len, n_hi = min(nchunks, n_lo + seg_len);
     const uint32_t tstr = (uint32_t)(H * D);                          // elements between tokens
     const int64_t hb = (int64_t)b * T * H * D + (int64_t)h * D;      // token 0 of this head
     const int64_t bb = (int64_t)b * T * H + h;                       // beta of token 0
     bf16* wsh = ws + (int64_t)bh * nchunks * C::WSC;
-    int ch = 16 * w + li;   // this lane's channel (gate, row products) and value column (column products)
+    const int ch = 16 * w + li;   // this lane's channel (gate, row products) and value column (column products)
     auto relane = [&]() {
         int lv = lane;
         asm volatile("" : "+v"(lv));
         g = lv >> 4;
-        li = lv & 15;
-        ch = 16 * w + li;
     };
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     // Between the lanes' layout and row-major [16][D] tiles on the matrix cores.  A product
